@@ -1,0 +1,176 @@
+"""Python binding of libmkd.so, the persistent decode megakernel for MI355X (gfx950).
+
+Argument marshalling only: every step of the decode runs in the HIP kernels behind
+the C-ABI declared in include/mkd.h.  PyTorch is used by callers for device memory
+and streams; tensors are passed as raw device pointers.  There is no fallback: if
+the library is missing or fails to load, importing the engine raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmkd.so")
+
+MKD_OK = 0
+MKD_ERR_ARG = -1
+MKD_ERR_HIP = -2
+MKD_ERR_CAPACITY = -3
+MKD_ERR_DEADLOCK = -4
+MKD_ERR_STATE = -5
+MODE_MEGAKERNEL = 0
+MODE_OP_PER_KERNEL = 1
+DEBUG_HIDDEN = 0
+DEBUG_TOPK_IDS = 1
+DEBUG_TOPK_W = 2
+DEBUG_ROUTER = 3
+DESC_WORDS = 32
+
+# every symbol include/mkd.h declares
+EXPORTS = ("mkd_create", "mkd_destroy", "mkd_load_weights", "mkd_set_mode", "mkd_decode_step",
+           "mkd_sync_status", "mkd_last_error", "mkd_debug_read", "mkd_plan_inspect")
+
+
+class MkdError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mkd error {code}: {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "top_k",
+        "moe_inter", "vocab", "page_size")] + [("rms_eps", ctypes.c_float),
+                                               ("rope_base", ctypes.c_float)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "embed", "norm", "w_qkv", "w_o", "w_router", "w_gate_up", "w_down")]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmkd.so; raises if it is absent (build it with __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_void_p
+        sig = {
+            "mkd_create": ([P(Config), I32, I32, I32, P(VP)], I32),
+            "mkd_destroy": ([VP], None),
+            "mkd_load_weights": ([VP, P(Weights)], I32),
+            "mkd_set_mode": ([VP, I32], I32),
+            "mkd_decode_step": ([VP, VP, I32, VP, VP, VP, VP, VP, VP, I32, VP], I32),
+            "mkd_sync_status": ([VP], I32),
+            "mkd_last_error": ([VP], ctypes.c_char_p),
+            "mkd_debug_read": ([VP, I32, VP, ctypes.c_size_t], I32),
+            "mkd_plan_inspect": ([VP, I32, I32, VP, I32, VP, P(I32)], I32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def config_of(g) -> Config:
+    """mkd_config from any object with the geometry attribute names."""
+    return Config(g.n_layers, g.hidden, g.n_q_heads, g.n_kv_heads, g.head_dim, g.n_experts,
+                  g.top_k, g.moe_inter, g.vocab, g.page_size, g.rms_eps, g.rope_base)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+class Engine:
+    """One mkd_engine.  device=-1 gives a host-only engine for plan inspection."""
+
+    def __init__(self, geom, device: int, max_batch: int, max_pages_per_seq: int):
+        self.geom = geom
+        self.max_batch = max_batch
+        self.max_pages = max_pages_per_seq
+        self._cfg = config_of(geom)
+        h = ctypes.c_void_p()
+        rc = lib().mkd_create(ctypes.byref(self._cfg), device, max_batch, max_pages_per_seq,
+                              ctypes.byref(h))
+        if rc != MKD_OK:
+            raise MkdError(rc, lib().mkd_last_error(None).decode())
+        self._h = h
+        self._weights = None
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().mkd_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, rc):
+        if rc != MKD_OK:
+            raise MkdError(rc, lib().mkd_last_error(self._h).decode())
+        return rc
+
+    def load_weights(self, w: dict):
+        """w: dict of bf16 device tensors (embed, norm, w_qkv, w_o, w_router, w_gate_up,
+        w_down), kept referenced by the engine."""
+        self._weights = dict(w)
+        st = Weights(*[_ptr(w[k]) for k in ("embed", "norm", "w_qkv", "w_o", "w_router",
+                                           "w_gate_up", "w_down")])
+        self._check(lib().mkd_load_weights(self._h, ctypes.byref(st)))
+
+    def set_mode(self, mode: int):
+        self._check(lib().mkd_set_mode(self._h, mode))
+
+    def decode_step(self, tokens, seq_lens, h_seq_lens: np.ndarray, page_table, kv_pool, n_pages,
+                    logits, h_page_table: Optional[np.ndarray] = None, stream=None):
+        """Enqueue one step.  tokens, seq_lens, page_table: int32 device tensors; kv_pool
+        bf16 device tensor; logits fp32 device tensor [batch][vocab]."""
+        h_seq_lens = np.ascontiguousarray(h_seq_lens, dtype=np.int32)
+        hpt = None if h_page_table is None else np.ascontiguousarray(h_page_table, dtype=np.int32)
+        s = None if stream is None else ctypes.c_void_p(stream)
+        self._check(lib().mkd_decode_step(self._h, s, int(h_seq_lens.size), _ptr(tokens),
+                                          _ptr(seq_lens), _ptr(h_seq_lens), _ptr(page_table),
+                                          _ptr(hpt), _ptr(kv_pool), int(n_pages), _ptr(logits)))
+
+    def sync_status(self) -> int:
+        return self._check(lib().mkd_sync_status(self._h))
+
+    def debug_read(self, what: int, batch: int) -> np.ndarray:
+        g = self.geom
+        shapes = {DEBUG_HIDDEN: ((g.n_layers + 1, batch, g.hidden), np.float32),
+                  DEBUG_TOPK_IDS: ((g.n_layers, batch, g.top_k), np.int32),
+                  DEBUG_TOPK_W: ((g.n_layers, batch, g.top_k), np.float32),
+                  DEBUG_ROUTER: ((g.n_layers, batch, g.n_experts), np.float32)}
+        shape, dt = shapes[what]
+        out = np.empty(shape, dtype=dt)
+        self._check(lib().mkd_debug_read(self._h, what, out.ctypes.data, out.nbytes))
+        return out
+
+    def plan(self, batch: int, n_cu: int):
+        """(descriptors [n_tasks][32] int32 grouped by CU, cu_offsets [n_cu+1])."""
+        n = ctypes.c_int32()
+        lib().mkd_plan_inspect(self._h, batch, n_cu, None, 0, None, ctypes.byref(n))
+        desc = np.empty((n.value, DESC_WORDS), dtype=np.int32)
+        offs = np.empty(n_cu + 1, dtype=np.int32)
+        self._check(lib().mkd_plan_inspect(self._h, batch, n_cu, desc.ctypes.data, n.value,
+                                           offs.ctypes.data, ctypes.byref(n)))
+        return desc, offs

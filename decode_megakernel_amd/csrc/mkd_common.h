@@ -1,0 +1,146 @@
+// mkd_common.h - definitions shared by the host scheduler and the device interpreter:
+// the task descriptor, the opcodes, the counter layout and the kernel parameters.
+//
+// Method: "Inside the megakernel serving engine for North Mini Code", sections
+// "Tasks" (sixteen opcodes cover the step; every GEMM opcode shares one body),
+// "The task descriptor" (32 int32 fields, field 0 the opcode, then layer, tile,
+// split, the barrier to wait on, the count to wait for and the barrier to signal)
+// and "Barriers" (counters in global memory, zeroed before each step).
+#pragma once
+#include <stdint.h>
+
+namespace mkd {
+
+// ---------------------------------------------------------------- opcodes
+// Our opcode set.  The pages' sixteen opcodes map onto these as follows:
+//   QKV_PROJ            -> OP_QKV (RoPE and the paged-KV append in the epilogue)
+//   ROUTER_GEMM         -> OP_ROUTER
+//   ROUTER_TOPK, ROUTE_FINALIZE, MOE_GATHER
+//                       -> computed redundantly at the start of OP_MOE_UP and
+//                          OP_MOE_DOWN claimers (no extra counter hop)
+//   ATTN_DRAIN + ATTN_DECODE -> OP_ATTN (claims (seq, kv group, page chunk) items)
+//   ATTN_COMBINE        -> done by the last attention item of a (seq, kv group)
+//   MOE_UPGATE_ACT_DRAIN -> OP_MOE_UP, MOE_DOWN_DRAIN -> OP_MOE_DOWN
+//   MOE_COMBINE         -> weighted sums folded into OP_MOE_DOWN partials
+//   O_PROJ              -> OP_OPROJ (split-K over KV groups)
+//   fused residual add + RMSNorm -> finalisation by the last arriver of a residual
+//                          row tile (O-proj splits + MoE-down splits), consumers
+//                          apply the norm on the fly
+//   LM_HEAD             -> OP_LM_HEAD; OP_EMBED seeds the residual stream.
+enum Opcode : int32_t {
+  OP_NOP = 0,
+  OP_EMBED = 1,
+  OP_QKV = 2,
+  OP_ROUTER = 3,
+  OP_ATTN = 4,
+  OP_MOE_UP = 5,
+  OP_MOE_DOWN = 6,
+  OP_OPROJ = 7,
+  OP_LM_HEAD = 8,
+  OP_COUNT = 9,
+};
+
+// ---------------------------------------------------------------- descriptor
+// 32 int32 per task, 128 bytes, read with scalar loads.
+enum DescField : int32_t {
+  D_OPCODE = 0,
+  D_LAYER = 1,
+  D_ARG0 = 2,   // first row / tile index / claimer index
+  D_ARG1 = 3,   // row count / kv group
+  D_ARG2 = 4,
+  D_ARG3 = 5,
+  D_WAIT = 6,   // counter index to wait on (-1: none)
+  D_TARGET = 7, // count to wait for
+  D_SIGNAL = 8, // counter index to arrive on (-1: none)
+  D_WAVE = 9,   // wave id in the schedule (for the op-per-kernel ablation)
+  D_GIDX = 10,  // position in the global (flattened) order
+  D_WORDS = 32,
+};
+
+// ---------------------------------------------------------------- counters
+// Per-layer block of counters; all zeroed before each step.
+struct CounterLayout {
+  int32_t per_layer;   // counters per layer block
+  int32_t x_ready;     // residual rows finalised for this layer's input (target n_rt)
+  int32_t qkv_done;    // QKV tiles done
+  int32_t router_done; // router tiles done
+  int32_t attn_claim;  // attention queue head
+  int32_t up_claim;    // MoE up queue head
+  int32_t down_claim;  // MoE down queue head
+  int32_t comb;        // [n_kv] combined (seq) count per kv group
+  int32_t attn_items;  // [max_batch][n_kv] items finished per (seq, group)
+  int32_t up_done;     // [n_experts] up tiles finished per expert
+  int32_t rt;          // [n_rt] arrivals per residual row tile
+  int32_t global_base; // start of the step-global block (after n_layers+1 layer blocks)
+  int32_t total;       // total counters
+};
+
+// Step-global status block (not per layer), at counters[global_base + ...].
+enum GlobalCounter : int32_t {
+  G_ABORT = 0,     // nonzero: a wait timed out; every workgroup stops
+  G_ERR_CODE = 1,  // first error code (1 = watchdog, 2 = bad page-table entry)
+  G_ERR_TASK = 2,  // global index of the task that reported it
+  G_ERR_CTR = 3,   // counter index it waited on
+  G_ERR_SEEN = 4,  // value observed
+  G_ERR_WANT = 5,  // target
+  G_DONE_WGS = 6,  // workgroups that finished their list
+  G_COUNT = 8,
+};
+
+// ---------------------------------------------------------------- plan constants
+struct PlanShape {
+  int32_t n_rt;            // residual row tiles (hidden / rt_rows)
+  int32_t rt_rows;         // rows per residual row tile
+  int32_t n_ds;            // MoE-down expert splits per row tile
+  int32_t up_rows;         // activation rows per MoE-up item (gate+up = 2x rows of weights)
+  int32_t n_up_tiles;      // moe_inter / up_rows
+  int32_t pages_per_item;  // attention pages per claimed item
+  int32_t qkv_rows;        // weight rows per QKV tile (RoPE pairs kept together)
+  int32_t router_rows;     // rows per router tile
+  int32_t lm_rows;         // rows per LM-head tile
+};
+
+// ---------------------------------------------------------------- kernel parameters
+struct Params {
+  // geometry
+  int32_t n_layers, hidden, n_q, n_kv, head_dim, n_experts, top_k, inter, vocab, page;
+  float rms_eps;
+  int32_t batch, max_batch, max_pages, n_pages;
+  PlanShape shape;
+  CounterLayout ctr;
+  // weights (bf16)
+  const uint16_t* embed;
+  const uint16_t* norm;
+  const uint16_t* w_qkv;
+  const uint16_t* w_o;
+  const uint16_t* w_router;
+  const uint16_t* w_gate_up;
+  const uint16_t* w_down;
+  // per-step inputs
+  const int32_t* tokens;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  uint16_t* kv_pool;
+  float* logits;
+  // workspace (fp32 unless noted)
+  float* h;           // [L+1][maxB][H]
+  float* ss;          // [L+1][maxB][n_rt] per-row-tile sum of squares
+  float* q;           // [L][maxB][nq*hd] post-RoPE queries
+  float* attn_part;   // [max_items][hpg][hd + 2] unnormalised o, then m, l
+  float* attn_o;      // [L][maxB][nq*hd]
+  float* a_part;      // [L][nkv][maxB][H] O-proj split outputs
+  float* router;      // [L][maxB][E]
+  int32_t* topk_ids;  // [L][maxB][k]
+  float* topk_w;      // [L][maxB][k]
+  float* moe_act;     // [L][maxB*k][I]
+  float* m_part;      // [L][n_ds][maxB][H]
+  const double* inv_freq;  // [hd/2] RoPE frequencies base^(-2i/hd), fp64
+  uint32_t* counters;
+  // task lists
+  const int32_t* tasks;      // [n_tasks][32]
+  const int32_t* cu_offsets; // [n_wg+1]
+  int32_t max_attn_items;    // capacity of attn_part
+  int32_t spin_limit;        // watchdog: polls before a wait gives up
+};
+
+}  // namespace mkd

@@ -1,0 +1,415 @@
+// mkd_engine.cpp - C-ABI of the decode megakernel (declared in include/mkd.h).
+//
+// Host side of one step ("Inside the megakernel serving engine for North Mini Code",
+// section "The serving engine around the kernel": clear per-step state, select the
+// schedule, launch the megakernel): validate the arguments, pick the cached plan for
+// the batch size, zero the step's counters with a fill kernel, and make one
+// cooperative launch of the persistent interpreter (or, in the ablation mode, one
+// launch per wave of tasks).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "../../include/mkd.h"
+#include "mkd_common.h"
+#include "mkd_plan.h"
+
+namespace mkd {
+hipError_t launch_clear(uint32_t* counters, int32_t n, hipStream_t s);
+hipError_t launch_persistent(const Params& p, int n_wg, hipStream_t s);
+hipError_t launch_wave(const Params& p, int32_t first, int32_t count, hipStream_t s);
+}  // namespace mkd
+
+using namespace mkd;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct DevPlan {
+  Plan plan;
+  int32_t* d_per_cu = nullptr;
+  int32_t* d_offsets = nullptr;
+  int32_t* d_global = nullptr;
+};
+
+}  // namespace
+
+struct mkd_engine {
+  mkd_config cfg{};
+  Geometry geom{};
+  int32_t device = -1;
+  int32_t max_batch = 0, max_pages = 0, n_cu = 0;
+  PlanOptions opts;
+  PlanShape shape{};
+  CounterLayout ctr{};
+  bool have_weights = false;
+  mkd_weights w{};
+  int32_t mode = MKD_MODE_MEGAKERNEL;
+  // workspace
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  Params base{};
+  int32_t max_attn_items = 0;
+  std::map<int32_t, DevPlan> plans;
+  std::string err;
+  int32_t last_batch = 0;
+  hipStream_t last_stream = nullptr;
+  ~mkd_engine() {
+    if (device >= 0) {
+      hipSetDevice(device);
+      for (auto& kv : plans) {
+        hipFree(kv.second.d_per_cu);
+        hipFree(kv.second.d_offsets);
+        hipFree(kv.second.d_global);
+      }
+      hipFree(ws);
+    }
+  }
+};
+
+namespace {
+
+int fail(mkd_engine* e, int code, const std::string& msg) {
+  if (e) e->err = msg;
+  return code;
+}
+
+int hip_fail(mkd_engine* e, hipError_t rc, const char* what) {
+  return fail(e, MKD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(rc));
+}
+
+std::string check_config(const mkd_config& c, int32_t max_batch, int32_t max_pages) {
+  if (c.n_layers < 1 || c.hidden < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 ||
+      c.n_experts < 1 || c.top_k < 1 || c.moe_inter < 1 || c.vocab < 1 || c.page_size < 1)
+    return "all dimensions must be positive";
+  if (c.hidden != 256 && c.hidden != 512 && c.hidden != 1024 && c.hidden != 2048)
+    return "hidden must be one of 256, 512, 1024, 2048";
+  if (c.head_dim != 64 && c.head_dim != 128) return "head_dim must be 64 or 128";
+  if (c.n_q_heads % c.n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
+  if (c.n_q_heads / c.n_kv_heads > 16) return "at most 16 query heads per KV group";
+  {
+    const int ko = c.n_q_heads * c.head_dim / c.n_kv_heads;
+    if (ko != 256 && ko != 512 && ko != 1024) return "n_q_heads*head_dim/n_kv_heads must be 256, 512 or 1024";
+  }
+  if (c.moe_inter != 128 && c.moe_inter != 256 && c.moe_inter != 512 && c.moe_inter != 768)
+    return "moe_inter must be one of 128, 256, 512, 768";
+  if (c.n_experts > 512) return "at most 512 experts";
+  if (c.top_k > 16 || c.top_k > c.n_experts) return "top_k must be <= 16 and <= n_experts";
+  if (c.page_size != 16) return "page_size must be 16";
+  if (!(c.rms_eps >= 0.0f) || !(c.rope_base > 0.0f)) return "rms_eps >= 0 and rope_base > 0 required";
+  if (max_batch < 1 || max_batch > 16) return "max_batch must be in [1, 16]";
+  if (max_pages < 1) return "max_pages_per_seq must be positive";
+  return "";
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int32_t max_pages_per_seq,
+               mkd_engine** out) {
+  if (!out) return MKD_ERR_ARG;
+  *out = nullptr;
+  if (!cfg) {
+    g_create_error = "cfg is NULL";
+    return MKD_ERR_ARG;
+  }
+  const std::string bad = check_config(*cfg, max_batch, max_pages_per_seq);
+  if (!bad.empty()) {
+    g_create_error = bad;
+    return MKD_ERR_ARG;
+  }
+  std::unique_ptr<mkd_engine> e(new mkd_engine());
+  e->cfg = *cfg;
+  e->geom = Geometry{cfg->n_layers, cfg->hidden, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim,
+                     cfg->n_experts, cfg->top_k, cfg->moe_inter, cfg->vocab, cfg->page_size};
+  e->max_batch = max_batch;
+  e->max_pages = max_pages_per_seq;
+  if (cfg->hidden <= 256) e->opts.rt_rows = 32;
+  if (cfg->moe_inter <= 256) e->opts.up_rows = 16;
+  if (cfg->head_dim / 2 < e->opts.qkv_pair_rows) e->opts.qkv_pair_rows = cfg->head_dim / 2;
+  e->shape = make_shape(e->geom, e->opts);
+  e->ctr = make_counters(e->geom, e->shape, max_batch);
+  e->max_attn_items = max_batch * cfg->n_kv_heads *
+                      ((max_pages_per_seq + e->opts.pages_per_item - 1) / e->opts.pages_per_item);
+  if (hip_device < 0) {  // host-only engine: plan inspection
+    e->n_cu = 0;
+    *out = e.release();
+    return MKD_OK;
+  }
+  hipError_t rc = hipSetDevice(hip_device);
+  if (rc != hipSuccess) {
+    g_create_error = std::string("hipSetDevice: ") + hipGetErrorString(rc);
+    return MKD_ERR_HIP;
+  }
+  e->device = hip_device;
+  hipDeviceProp_t prop;
+  rc = hipGetDeviceProperties(&prop, hip_device);
+  if (rc != hipSuccess) {
+    g_create_error = std::string("hipGetDeviceProperties: ") + hipGetErrorString(rc);
+    return MKD_ERR_HIP;
+  }
+  if (!prop.cooperativeLaunch) {
+    g_create_error = "device does not support cooperative launches";
+    return MKD_ERR_HIP;
+  }
+  e->n_cu = prop.multiProcessorCount;
+  // workspace layout
+  const int64_t L = cfg->n_layers, B = max_batch, H = cfg->hidden, E = cfg->n_experts, K = cfg->top_k;
+  const int64_t QD = (int64_t)cfg->n_q_heads * cfg->head_dim, hpg = cfg->n_q_heads / cfg->n_kv_heads;
+  Params& p = e->base;
+  std::vector<std::pair<size_t, void**>> slots = {
+      {sizeof(float) * (L + 1) * B * H, (void**)&p.h},
+      {sizeof(float) * (L + 1) * B * e->shape.n_rt, (void**)&p.ss},
+      {sizeof(float) * L * B * QD, (void**)&p.q},
+      {sizeof(float) * (size_t)e->max_attn_items * hpg * (cfg->head_dim + 2), (void**)&p.attn_part},
+      {sizeof(float) * L * B * QD, (void**)&p.attn_o},
+      {sizeof(float) * L * cfg->n_kv_heads * B * H, (void**)&p.a_part},
+      {sizeof(float) * L * B * E, (void**)&p.router},
+      {sizeof(int32_t) * L * B * K, (void**)&p.topk_ids},
+      {sizeof(float) * L * B * K, (void**)&p.topk_w},
+      {sizeof(float) * L * B * K * cfg->moe_inter, (void**)&p.moe_act},
+      {sizeof(float) * L * e->shape.n_ds * B * H, (void**)&p.m_part},
+      {sizeof(double) * cfg->head_dim / 2, (void**)&p.inv_freq},
+      {sizeof(uint32_t) * (size_t)e->ctr.total, (void**)&p.counters},
+  };
+  size_t total = 0;
+  for (auto& s : slots) total += align256(s.first);
+  rc = hipMalloc(&e->ws, total);
+  if (rc != hipSuccess) {
+    g_create_error = std::string("hipMalloc workspace: ") + hipGetErrorString(rc);
+    return MKD_ERR_HIP;
+  }
+  e->ws_bytes = total;
+  size_t at = 0;
+  for (auto& s : slots) {
+    *s.second = (char*)e->ws + at;
+    at += align256(s.first);
+  }
+  rc = hipMemset(e->ws, 0, total);
+  if (rc == hipSuccess) {
+    std::vector<double> inv(cfg->head_dim / 2);
+    for (int i = 0; i < cfg->head_dim / 2; ++i)
+      inv[i] = std::pow((double)cfg->rope_base, -2.0 * (double)i / (double)cfg->head_dim);
+    rc = hipMemcpy((void*)p.inv_freq, inv.data(), sizeof(double) * inv.size(), hipMemcpyHostToDevice);
+  }
+  if (rc != hipSuccess) {
+    g_create_error = std::string("workspace init: ") + hipGetErrorString(rc);
+    return MKD_ERR_HIP;
+  }
+  p.n_layers = cfg->n_layers;
+  p.hidden = cfg->hidden;
+  p.n_q = cfg->n_q_heads;
+  p.n_kv = cfg->n_kv_heads;
+  p.head_dim = cfg->head_dim;
+  p.n_experts = cfg->n_experts;
+  p.top_k = cfg->top_k;
+  p.inter = cfg->moe_inter;
+  p.vocab = cfg->vocab;
+  p.page = cfg->page_size;
+  p.rms_eps = cfg->rms_eps;
+  p.max_batch = max_batch;
+  p.max_pages = max_pages_per_seq;
+  p.shape = e->shape;
+  p.ctr = e->ctr;
+  p.max_attn_items = e->max_attn_items;
+  p.spin_limit = 4000000;
+  *out = e.release();
+  return MKD_OK;
+}
+
+void mkd_destroy(mkd_engine* eng) { delete eng; }
+
+int mkd_load_weights(mkd_engine* e, const mkd_weights* w) {
+  if (!e) return MKD_ERR_ARG;
+  if (!w || !w->embed || !w->norm || !w->w_qkv || !w->w_o || !w->w_router || !w->w_gate_up || !w->w_down)
+    return fail(e, MKD_ERR_ARG, "every weight pointer must be non-NULL");
+  e->w = *w;
+  e->base.embed = (const uint16_t*)w->embed;
+  e->base.norm = (const uint16_t*)w->norm;
+  e->base.w_qkv = (const uint16_t*)w->w_qkv;
+  e->base.w_o = (const uint16_t*)w->w_o;
+  e->base.w_router = (const uint16_t*)w->w_router;
+  e->base.w_gate_up = (const uint16_t*)w->w_gate_up;
+  e->base.w_down = (const uint16_t*)w->w_down;
+  e->have_weights = true;
+  return MKD_OK;
+}
+
+int mkd_set_mode(mkd_engine* e, int32_t mode) {
+  if (!e) return MKD_ERR_ARG;
+  if (mode != MKD_MODE_MEGAKERNEL && mode != MKD_MODE_OP_PER_KERNEL) return fail(e, MKD_ERR_ARG, "unknown mode");
+  e->mode = mode;
+  return MKD_OK;
+}
+
+static int get_plan(mkd_engine* e, int32_t batch, DevPlan** out) {
+  auto it = e->plans.find(batch);
+  if (it != e->plans.end()) {
+    *out = &it->second;
+    return MKD_OK;
+  }
+  DevPlan dp;
+  const std::string bad = build_plan(e->geom, e->opts, e->max_batch, batch, e->n_cu, &dp.plan);
+  if (!bad.empty()) return fail(e, MKD_ERR_ARG, "plan: " + bad);
+  hipError_t rc = hipMalloc(&dp.d_per_cu, sizeof(int32_t) * dp.plan.per_cu.size());
+  if (rc == hipSuccess) rc = hipMalloc(&dp.d_global, sizeof(int32_t) * dp.plan.global.size());
+  if (rc == hipSuccess) rc = hipMalloc(&dp.d_offsets, sizeof(int32_t) * dp.plan.cu_offsets.size());
+  if (rc == hipSuccess)
+    rc = hipMemcpy(dp.d_per_cu, dp.plan.per_cu.data(), sizeof(int32_t) * dp.plan.per_cu.size(),
+                   hipMemcpyHostToDevice);
+  if (rc == hipSuccess)
+    rc = hipMemcpy(dp.d_global, dp.plan.global.data(), sizeof(int32_t) * dp.plan.global.size(),
+                   hipMemcpyHostToDevice);
+  if (rc == hipSuccess)
+    rc = hipMemcpy(dp.d_offsets, dp.plan.cu_offsets.data(), sizeof(int32_t) * dp.plan.cu_offsets.size(),
+                   hipMemcpyHostToDevice);
+  if (rc != hipSuccess) {
+    hipFree(dp.d_per_cu);
+    hipFree(dp.d_global);
+    hipFree(dp.d_offsets);
+    return hip_fail(e, rc, "plan upload");
+  }
+  auto ins = e->plans.emplace(batch, dp);
+  *out = &ins.first->second;
+  return MKD_OK;
+}
+
+int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d_tokens,
+                    const int32_t* d_seq_lens, const int32_t* h_seq_lens, const int32_t* d_page_table,
+                    const int32_t* h_page_table, void* kv_pool, int32_t n_pages, float* d_logits) {
+  if (!e) return MKD_ERR_ARG;
+  if (e->device < 0) return fail(e, MKD_ERR_STATE, "host-only engine cannot decode");
+  if (!e->have_weights) return fail(e, MKD_ERR_STATE, "weights not loaded");
+  if (batch < 1 || batch > e->max_batch)
+    return fail(e, MKD_ERR_CAPACITY, "batch must be in [1, max_batch]");
+  if (!d_tokens || !d_seq_lens || !h_seq_lens || !d_page_table || !kv_pool || !d_logits)
+    return fail(e, MKD_ERR_ARG, "NULL pointer argument");
+  if (n_pages < 1) return fail(e, MKD_ERR_ARG, "n_pages must be positive");
+  const int P = e->cfg.page_size;
+  int64_t items = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int32_t s = h_seq_lens[b];
+    if (s < 0) return fail(e, MKD_ERR_ARG, "negative sequence length");
+    if (s / P >= e->max_pages)
+      return fail(e, MKD_ERR_CAPACITY, "sequence " + std::to_string(b) + " needs more pages than max_pages_per_seq");
+    if (h_page_table) {
+      for (int lp = 0; lp <= s / P; ++lp) {
+        const int32_t pg = h_page_table[(int64_t)b * e->max_pages + lp];
+        if (pg < 0 || pg >= n_pages)
+          return fail(e, MKD_ERR_ARG, "page table entry (" + std::to_string(b) + ", " + std::to_string(lp) +
+                                          ") = " + std::to_string(pg) + " is outside [0, n_pages)");
+      }
+    }
+    items += (int64_t)e->cfg.n_kv_heads * ((s / P + 1 + e->opts.pages_per_item - 1) / e->opts.pages_per_item);
+  }
+  if (items > e->max_attn_items) return fail(e, MKD_ERR_CAPACITY, "attention work exceeds the workspace");
+  hipError_t rc = hipSetDevice(e->device);
+  if (rc != hipSuccess) return hip_fail(e, rc, "hipSetDevice");
+  DevPlan* dp = nullptr;
+  int r = get_plan(e, batch, &dp);
+  if (r != MKD_OK) return r;
+  Params p = e->base;
+  p.batch = batch;
+  p.n_pages = n_pages;
+  p.tokens = d_tokens;
+  p.seq_lens = d_seq_lens;
+  p.page_table = d_page_table;
+  p.kv_pool = (uint16_t*)kv_pool;
+  p.logits = d_logits;
+  p.cu_offsets = dp->d_offsets;
+  hipStream_t s = (hipStream_t)stream;
+  rc = launch_clear(p.counters, e->ctr.total, s);
+  if (rc != hipSuccess) return hip_fail(e, rc, "counter clear");
+  if (e->mode == MKD_MODE_MEGAKERNEL) {
+    p.tasks = dp->d_per_cu;
+    rc = launch_persistent(p, e->n_cu, s);
+    if (rc != hipSuccess) return hip_fail(e, rc, "megakernel launch");
+  } else {
+    p.tasks = dp->d_global;
+    for (const Wave& w : dp->plan.waves) {
+      if (w.count == 0) continue;
+      rc = launch_wave(p, w.first, w.count, s);
+      if (rc != hipSuccess) return hip_fail(e, rc, "wave launch");
+    }
+  }
+  e->last_batch = batch;
+  e->last_stream = s;
+  e->err.clear();
+  return MKD_OK;
+}
+
+int mkd_sync_status(mkd_engine* e) {
+  if (!e) return MKD_ERR_ARG;
+  if (e->device < 0) return MKD_OK;
+  hipError_t rc = hipSetDevice(e->device);
+  if (rc == hipSuccess) rc = hipStreamSynchronize(e->last_stream);
+  if (rc != hipSuccess) return hip_fail(e, rc, "stream synchronize");
+  uint32_t st[G_COUNT];
+  rc = hipMemcpy(st, e->base.counters + e->ctr.global_base, sizeof(st), hipMemcpyDeviceToHost);
+  if (rc != hipSuccess) return hip_fail(e, rc, "status read");
+  if (st[G_ERR_CODE] == 0) return MKD_OK;
+  char buf[256];
+  if (st[G_ERR_CODE] == 1) {
+    snprintf(buf, sizeof(buf), "watchdog: task %u waited on counter %u (saw %u, wanted %u)", st[G_ERR_TASK],
+             st[G_ERR_CTR], st[G_ERR_SEEN], st[G_ERR_WANT]);
+    fail(e, MKD_ERR_DEADLOCK, buf);
+  } else {
+    snprintf(buf, sizeof(buf), "invalid input on device: task %u saw %d (limit %u)", st[G_ERR_TASK],
+             (int)st[G_ERR_SEEN], st[G_ERR_WANT]);
+    fail(e, MKD_ERR_ARG, buf);
+  }
+  const int code = st[G_ERR_CODE] == 1 ? MKD_ERR_DEADLOCK : MKD_ERR_ARG;
+  hipMemset(e->base.counters + e->ctr.global_base, 0, sizeof(st));
+  return code;
+}
+
+const char* mkd_last_error(const mkd_engine* e) { return e ? e->err.c_str() : g_create_error.c_str(); }
+
+int mkd_debug_read(mkd_engine* e, int32_t what, void* dst, size_t bytes) {
+  if (!e || !dst) return MKD_ERR_ARG;
+  if (e->device < 0) return fail(e, MKD_ERR_STATE, "host-only engine");
+  const int64_t B = e->last_batch, L = e->cfg.n_layers, mb = e->max_batch;
+  if (B < 1) return fail(e, MKD_ERR_STATE, "no step has run");
+  int64_t inner = 0, outer = 0;
+  const char* src = nullptr;
+  switch (what) {
+    case MKD_DEBUG_HIDDEN: inner = e->cfg.hidden * 4; outer = L + 1; src = (const char*)e->base.h; break;
+    case MKD_DEBUG_TOPK_IDS: inner = e->cfg.top_k * 4; outer = L; src = (const char*)e->base.topk_ids; break;
+    case MKD_DEBUG_TOPK_W: inner = e->cfg.top_k * 4; outer = L; src = (const char*)e->base.topk_w; break;
+    case MKD_DEBUG_ROUTER: inner = e->cfg.n_experts * 4; outer = L; src = (const char*)e->base.router; break;
+    default: return fail(e, MKD_ERR_ARG, "unknown debug buffer");
+  }
+  if (bytes < (size_t)(outer * B * inner)) return fail(e, MKD_ERR_ARG, "debug buffer too small");
+  hipError_t rc = hipSetDevice(e->device);
+  if (rc == hipSuccess) rc = hipStreamSynchronize(e->last_stream);
+  if (rc == hipSuccess)
+    rc = hipMemcpy2D(dst, (size_t)(B * inner), src, (size_t)(mb * inner), (size_t)(B * inner), (size_t)outer,
+                     hipMemcpyDeviceToHost);
+  if (rc != hipSuccess) return hip_fail(e, rc, "debug read");
+  return MKD_OK;
+}
+
+int mkd_plan_inspect(mkd_engine* e, int32_t batch, int32_t n_cu, int32_t* desc, int32_t max_tasks,
+                     int32_t* cu_offsets, int32_t* n_tasks) {
+  if (!e || !n_tasks) return MKD_ERR_ARG;
+  Plan plan;
+  const std::string bad = build_plan(e->geom, e->opts, e->max_batch, batch, n_cu, &plan);
+  if (!bad.empty()) return fail(e, MKD_ERR_ARG, "plan: " + bad);
+  *n_tasks = plan.n_tasks();
+  if (plan.n_tasks() > max_tasks) return fail(e, MKD_ERR_CAPACITY, "max_tasks too small");
+  if (desc) std::memcpy(desc, plan.per_cu.data(), sizeof(int32_t) * plan.per_cu.size());
+  if (cu_offsets) std::memcpy(cu_offsets, plan.cu_offsets.data(), sizeof(int32_t) * plan.cu_offsets.size());
+  return MKD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+// mkd_plan.cpp - host task scheduler (see mkd_plan.h).
+#include "mkd_plan.h"
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+
+namespace mkd {
+
+PlanShape make_shape(const Geometry& g, const PlanOptions& o) {
+  PlanShape s{};
+  s.rt_rows = o.rt_rows;
+  s.n_rt = g.hidden / o.rt_rows;
+  s.n_ds = o.n_ds;
+  s.up_rows = o.up_rows;
+  s.n_up_tiles = g.inter / o.up_rows;
+  s.pages_per_item = o.pages_per_item;
+  s.qkv_rows = 2 * o.qkv_pair_rows;
+  s.router_rows = o.router_rows;
+  s.lm_rows = o.lm_rows;
+  return s;
+}
+
+CounterLayout make_counters(const Geometry& g, const PlanShape& s, int32_t max_batch) {
+  CounterLayout c{};
+  int32_t at = 0;
+  c.x_ready = at++;
+  c.qkv_done = at++;
+  c.router_done = at++;
+  c.attn_claim = at++;
+  c.up_claim = at++;
+  c.down_claim = at++;
+  c.comb = at;
+  at += g.n_kv;
+  c.attn_items = at;
+  at += max_batch * g.n_kv;
+  c.up_done = at;
+  at += g.n_experts;
+  c.rt = at;
+  at += s.n_rt;
+  c.per_layer = (at + 15) / 16 * 16;
+  c.global_base = c.per_layer * (g.n_layers + 1);
+  c.total = c.global_base + G_COUNT;
+  return c;
+}
+
+namespace {
+
+struct Emitter {
+  std::vector<int32_t>* v;
+  int32_t wave_id = 0;
+  int32_t emit(int32_t op, int32_t layer, int32_t a0, int32_t a1, int32_t a2, int32_t a3, int32_t wait,
+               int32_t target, int32_t signal) {
+    const size_t at = v->size();
+    v->resize(at + D_WORDS, 0);
+    int32_t* d = v->data() + at;
+    d[D_OPCODE] = op;
+    d[D_LAYER] = layer;
+    d[D_ARG0] = a0;
+    d[D_ARG1] = a1;
+    d[D_ARG2] = a2;
+    d[D_ARG3] = a3;
+    d[D_WAIT] = wait;
+    d[D_TARGET] = target;
+    d[D_SIGNAL] = signal;
+    d[D_WAVE] = wave_id;
+    d[D_GIDX] = (int32_t)(at / D_WORDS);
+    return d[D_GIDX];
+  }
+};
+
+}  // namespace
+
+std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batch, int32_t batch,
+                       int32_t n_cu, Plan* out) {
+  if (batch < 1 || batch > max_batch) return "batch out of range";
+  if (n_cu < 1) return "n_cu must be positive";
+  if (g.hidden % o.rt_rows) return "hidden must be a multiple of rt_rows";
+  if (g.inter % o.up_rows) return "moe_inter must be a multiple of up_rows";
+  if ((g.head_dim / 2) % o.qkv_pair_rows) return "head_dim/2 must be a multiple of qkv_pair_rows";
+  if (o.pages_per_item < 1 || o.pages_per_item > 16) return "pages_per_item must be in [1, 16]";
+  if (o.n_ds < 1) return "n_ds must be positive";
+  Plan& P = *out;
+  P = Plan();
+  P.batch = batch;
+  P.n_cu = n_cu;
+  P.shape = make_shape(g, o);
+  P.ctr = make_counters(g, P.shape, max_batch);
+  const PlanShape& s = P.shape;
+  const CounterLayout& c = P.ctr;
+  auto L = [&](int l, int off) { return l * c.per_layer + off; };
+  Emitter em{&P.global};
+  auto begin_wave = [&](int32_t kind, int32_t layer) {
+    P.waves.push_back(Wave{kind, layer, P.n_tasks(), 0});
+    em.wave_id = (int32_t)P.waves.size() - 1;
+  };
+  auto end_wave = [&]() { P.waves.back().count = P.n_tasks() - P.waves.back().first; };
+
+  const int n_qkv_heads = g.n_q + 2 * g.n_kv;
+  const int n_qkv_tiles = n_qkv_heads * (g.head_dim / 2 / o.qkv_pair_rows);
+  const int n_router_tiles = (g.n_experts + o.router_rows - 1) / o.router_rows;
+  const int n_attn = o.n_attn_claimers > 0 ? o.n_attn_claimers : std::max(1, n_cu / 2);
+  const int n_up = o.n_up_claimers > 0 ? o.n_up_claimers : n_cu;
+  const int n_down = o.n_down_claimers > 0 ? o.n_down_claimers : n_cu;
+
+  begin_wave(-1, 0);
+  for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_EMBED, 0, rt, 0, 0, 0, -1, 0, L(0, c.x_ready));
+  end_wave();
+  for (int l = 0; l < g.n_layers; ++l) {
+    for (int wi = 0; wi < W_KINDS; ++wi) {
+      const int kind = o.order[wi];
+      begin_wave(kind, l);
+      switch (kind) {
+        case W_QKV:
+          for (int hh = 0; hh < n_qkv_heads; ++hh)
+            for (int j0 = 0; j0 < g.head_dim / 2; j0 += o.qkv_pair_rows)
+              em.emit(OP_QKV, l, hh, j0, o.qkv_pair_rows, 0, L(l, c.x_ready), s.n_rt, L(l, c.qkv_done));
+          break;
+        case W_ROUTER:
+          for (int r0 = 0; r0 < g.n_experts; r0 += o.router_rows)
+            em.emit(OP_ROUTER, l, r0, std::min(o.router_rows, g.n_experts - r0), 0, 0, L(l, c.x_ready), s.n_rt,
+                    L(l, c.router_done));
+          break;
+        case W_ATTN:
+          for (int i = 0; i < n_attn; ++i)
+            em.emit(OP_ATTN, l, i, 0, 0, 0, L(l, c.qkv_done), n_qkv_tiles, -1);
+          break;
+        case W_MOE_UP:
+          for (int i = 0; i < n_up; ++i)
+            em.emit(OP_MOE_UP, l, i, 0, 0, 0, L(l, c.router_done), n_router_tiles, -1);
+          break;
+        case W_MOE_DOWN:
+          for (int i = 0; i < n_down; ++i)
+            em.emit(OP_MOE_DOWN, l, i, 0, 0, 0, L(l, c.router_done), n_router_tiles, -1);
+          break;
+        case W_OPROJ:
+          for (int rt = 0; rt < s.n_rt; ++rt)
+            for (int gg = 0; gg < g.n_kv; ++gg)
+              em.emit(OP_OPROJ, l, rt, gg, 0, 0, L(l, c.comb + gg), batch, -1);
+          break;
+        default:
+          return "bad wave order";
+      }
+      end_wave();
+    }
+  }
+  begin_wave(-2, g.n_layers);
+  for (int r0 = 0; r0 < g.vocab; r0 += o.lm_rows)
+    em.emit(OP_LM_HEAD, g.n_layers, r0, std::min(o.lm_rows, g.vocab - r0), 0, 0, L(g.n_layers, c.x_ready), s.n_rt,
+            -1);
+  end_wave();
+
+  // deal task k to CU k mod n_cu, keeping global order within each CU
+  const int n = P.n_tasks();
+  std::vector<std::vector<int32_t>> lists(n_cu);
+  for (int k = 0; k < n; ++k) lists[k % n_cu].push_back(k);
+  P.cu_offsets.assign(n_cu + 1, 0);
+  P.per_cu.reserve(P.global.size());
+  for (int cu = 0; cu < n_cu; ++cu) {
+    P.cu_offsets[cu] = (int32_t)(P.per_cu.size() / D_WORDS);
+    for (int32_t k : lists[cu])
+      P.per_cu.insert(P.per_cu.end(), P.global.begin() + (size_t)k * D_WORDS,
+                      P.global.begin() + (size_t)(k + 1) * D_WORDS);
+  }
+  P.cu_offsets[n_cu] = (int32_t)(P.per_cu.size() / D_WORDS);
+  return validate_plan(g, P);
+}
+
+std::string validate_plan(const Geometry& g, const Plan& P) {
+  const int n = P.n_tasks();
+  const CounterLayout& c = P.ctr;
+  // static arrivals per counter, by global index
+  std::map<int32_t, std::vector<int32_t>> arrivals;
+  for (int k = 0; k < n; ++k) {
+    const int32_t* d = P.global.data() + (size_t)k * D_WORDS;
+    if (d[D_GIDX] != k) return "task " + std::to_string(k) + ": global index mismatch";
+    if (d[D_SIGNAL] >= 0) arrivals[d[D_SIGNAL]].push_back(k);
+  }
+  // dynamic producers: residual row tiles are finalised by the last of their
+  // O-proj / MoE-down producers (x_ready of the next layer), attention combines
+  // arrive on comb; both come from waves of the same layer.
+  for (int k = 0; k < n; ++k) {
+    const int32_t* d = P.global.data() + (size_t)k * D_WORDS;
+    const int op = d[D_OPCODE];
+    if (op < OP_NOP || op >= OP_COUNT) return "task " + std::to_string(k) + ": bad opcode";
+    if (d[D_WAIT] < 0) continue;
+    if (d[D_WAIT] >= c.global_base) return "task " + std::to_string(k) + ": wait on a status counter";
+    const int layer = d[D_WAIT] / c.per_layer, off = d[D_WAIT] % c.per_layer;
+    int64_t avail = 0;
+    if (off == c.x_ready && layer > 0) {
+      // finalised by layer-1's O-proj / MoE-down waves: they must all precede k
+      bool oproj = false, down = false;
+      for (const Wave& w : P.waves)
+        if (w.layer == layer - 1 && w.first + w.count <= k) {
+          oproj |= w.kind == W_OPROJ;
+          down |= w.kind == W_MOE_DOWN && w.count > 0;
+        }
+      avail = (oproj && down) ? P.shape.n_rt : 0;
+    } else if (off >= c.comb && off < c.comb + g.n_kv) {
+      bool attn = false;
+      for (const Wave& w : P.waves)
+        if (w.layer == layer && w.kind == W_ATTN && w.count > 0 && w.first + w.count <= k) attn = true;
+      avail = attn ? P.batch : 0;
+    } else {
+      auto it = arrivals.find(d[D_WAIT]);
+      if (it != arrivals.end())
+        for (int32_t a : it->second) avail += a < k ? 1 : 0;
+    }
+    if (avail < d[D_TARGET])
+      return "task " + std::to_string(k) + " (op " + std::to_string(op) + ", layer " + std::to_string(d[D_LAYER]) +
+             ") waits for " + std::to_string(d[D_TARGET]) + " arrivals on counter " + std::to_string(d[D_WAIT]) +
+             " but only " + std::to_string(avail) + " producers precede it";
+  }
+  // MoE-down claimers wait on up counters filled by MoE-up claimers: up before down.
+  for (int l = 0; l < g.n_layers; ++l) {
+    int up_end = -1, down_first = -1;
+    for (const Wave& w : P.waves)
+      if (w.layer == l) {
+        if (w.kind == W_MOE_UP) up_end = w.first + w.count;
+        if (w.kind == W_MOE_DOWN) down_first = w.first;
+      }
+    if (up_end < 0 || down_first < 0 || down_first < up_end)
+      return "layer " + std::to_string(l) + ": MoE-down claimers must follow the MoE-up wave";
+  }
+  // per-CU lists in increasing global order
+  for (int cu = 0; cu + 1 < (int)P.cu_offsets.size(); ++cu) {
+    int32_t prev = -1;
+    for (int t = P.cu_offsets[cu]; t < P.cu_offsets[cu + 1]; ++t) {
+      const int32_t gi = P.per_cu[(size_t)t * D_WORDS + D_GIDX];
+      if (gi <= prev) return "cu " + std::to_string(cu) + ": list not in global order";
+      prev = gi;
+    }
+  }
+  return "";
+}
+
+}  // namespace mkd

@@ -1,0 +1,77 @@
+// mkd_plan.h - host task scheduler for the decode megakernel.
+//
+// "Inside the megakernel serving engine for North Mini Code", section "The task
+// scheduler: mapping tasks to SMs": the host builds named waves for each layer,
+// chooses an order, flattens them into one task list and deals task k to compute
+// unit k mod n_cu; attention and the MoE stages reserve a fixed number of claimer
+// tasks that drain shared queues.  Any order without circular waits is correct; the
+// order only changes throughput.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "mkd_common.h"
+
+namespace mkd {
+
+struct Geometry {
+  int32_t n_layers, hidden, n_q, n_kv, head_dim, n_experts, top_k, inter, vocab, page;
+};
+
+// Wave kinds of one layer, in the order they can be arranged.
+enum WaveKind : int32_t { W_QKV = 0, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_OPROJ, W_KINDS };
+
+struct PlanOptions {
+  int32_t rt_rows = 32;        // residual rows per O-proj / MoE-down tile
+  int32_t n_ds = 8;            // MoE-down expert splits per row tile
+  int32_t up_rows = 16;        // activation rows per MoE-up item
+  int32_t pages_per_item = 16; // attention pages per claimed item (<= 16)
+  int32_t qkv_pair_rows = 16;  // RoPE pairs per QKV tile (tile = 2x rows)
+  int32_t router_rows = 16;
+  int32_t lm_rows = 32;
+  int32_t n_attn_claimers = 0; // 0: automatic
+  int32_t n_up_claimers = 0;
+  int32_t n_down_claimers = 0;
+  // Order of the waves inside a layer.  Default follows the pages' default order
+  // (qkv -> router -> attention -> MoE up/down -> O-proj).
+  int32_t order[W_KINDS] = {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_OPROJ};
+};
+
+struct Wave {
+  int32_t kind;   // WaveKind, or -1 for embed, -2 for LM head
+  int32_t layer;
+  int32_t first;  // index into the global-order task array
+  int32_t count;
+};
+
+struct Plan {
+  int32_t batch = 0;
+  int32_t n_cu = 0;
+  PlanShape shape{};
+  CounterLayout ctr{};
+  std::vector<int32_t> global;      // [n][32] tasks in global (flattened) order
+  std::vector<Wave> waves;          // ranges of `global`
+  std::vector<int32_t> per_cu;      // [n][32] tasks grouped by CU, each in global order
+  std::vector<int32_t> cu_offsets;  // [n_cu + 1]
+  int32_t n_tasks() const { return (int32_t)(global.size() / D_WORDS); }
+};
+
+// Shape constants and counter layout (independent of the batch size except
+// attn_items, sized by max_batch).
+PlanShape make_shape(const Geometry& g, const PlanOptions& o);
+CounterLayout make_counters(const Geometry& g, const PlanShape& s, int32_t max_batch);
+
+// Build the plan for `batch` sequences on `n_cu` compute units.  Returns "" on
+// success, else a description of the violated constraint.
+std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batch, int32_t batch,
+                       int32_t n_cu, Plan* out);
+
+// Static checks of a plan: every counter a task waits on receives at least the
+// awaited number of arrivals from tasks earlier in the global order (static
+// producers), claimers wait only on earlier waves, and every compute unit's list is
+// in increasing global order (so no circular wait exists).  Returns "" if valid.
+std::string validate_plan(const Geometry& g, const Plan& p);
+
+}  // namespace mkd

@@ -1,0 +1,81 @@
+"""The C-ABI library: loads without a GPU, exports every declared symbol, validates
+its arguments, and builds schedules that pass the static checks.  CPU only."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_megakernel_amd as mkd
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OP_EMBED, OP_QKV, OP_ROUTER, OP_ATTN, OP_MOE_UP, OP_MOE_DOWN, OP_OPROJ, OP_LM_HEAD = range(1, 9)
+
+
+def test_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "mkd.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|void|const char\*)\s+(mkd_\w+)\s*\(", header, re.M))
+    assert declared == set(mkd.EXPORTS)
+    L = mkd.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_create_rejects_bad_geometry():
+    bad = [dict(hidden=300), dict(head_dim=96), dict(page_size=8), dict(top_k=20),
+           dict(n_q_heads=5)]
+    for change in bad:
+        g = synth.Geometry(**{**synth.TINY.__dict__, **change})
+        with pytest.raises(mkd.MkdError) as ei:
+            mkd.Engine(g, -1, 1, 8)
+        assert ei.value.code == mkd.MKD_ERR_ARG
+    with pytest.raises(mkd.MkdError):
+        mkd.Engine(synth.TINY, -1, 17, 8)       # max_batch above 16
+
+
+def test_host_engine_refuses_to_decode():
+    e = mkd.Engine(synth.TINY, -1, 1, 8)
+    rc = mkd.lib().mkd_decode_step(e._h, None, 1, None, None, None, None, None, None, 1, None)
+    assert rc == mkd.MKD_ERR_STATE
+    assert mkd.lib().mkd_sync_status(None) == mkd.MKD_ERR_ARG
+
+
+def _waves(desc):
+    return desc[:, 0], desc[:, 1]
+
+
+@pytest.mark.parametrize("geom,batch,n_cu", [(synth.TINY, 1, 256), (synth.TINY, 3, 7),
+                                             (synth.FULL, 1, 256), (synth.FULL, 16, 256)])
+def test_plan_structure(geom, batch, n_cu):
+    e = mkd.Engine(geom, -1, 16, 64)
+    desc, offs = e.plan(batch, n_cu)
+    assert offs[0] == 0 and offs[-1] == desc.shape[0] and (np.diff(offs) >= 0).all()
+    # round robin: CU c holds global indices c, c + n_cu, ...
+    for cu in range(n_cu):
+        gidx = desc[offs[cu]:offs[cu + 1], 10]
+        assert (gidx % n_cu == cu).all() and (np.diff(gidx) > 0).all()
+    ops = desc[:, 0]
+    gq = geom.n_q_heads + 2 * geom.n_kv_heads
+    n_rt = geom.hidden // 32
+    assert (ops == OP_EMBED).sum() == n_rt
+    assert (ops == OP_OPROJ).sum() == geom.n_layers * n_rt * geom.n_kv_heads
+    assert (ops == OP_LM_HEAD).sum() == -(-geom.vocab // 32)
+    qkv = desc[ops == OP_QKV]
+    # QKV tiles cover every (head, rope pair) exactly once per layer
+    for layer in range(geom.n_layers):
+        t = qkv[qkv[:, 1] == layer]
+        covered = sorted((h, j0 + i) for h, j0, pb in t[:, 2:5] for i in range(pb))
+        assert covered == [(h, i) for h in range(gq) for i in range(geom.head_dim // 2)]
+    # barrier accounting: every QKV tile signals the counter the attention claimers
+    # wait on, with the target equal to the number of tiles
+    attn = desc[ops == OP_ATTN]
+    for layer in range(geom.n_layers):
+        a = attn[attn[:, 1] == layer]
+        t = qkv[qkv[:, 1] == layer]
+        assert (a[:, 6] == t[0, 8]).all() and (a[:, 7] == len(t)).all()
+    # O-proj waits for the batch's combined attention of its KV group
+    op = desc[ops == OP_OPROJ]
+    assert (op[:, 7] == batch).all()
