@@ -1,0 +1,278 @@
+"""Decode benchmark of the persistent megakernel on one MI355X.
+
+Workload (default): the synthetic 30B-total / ~3B-active parallel-transformer MoE
+(48 layers, hidden 2048, 32 q / 4 kv heads of 128, 128 experts top-8 with SwiGLU
+inter 768, tied 151552 x 2048 embedding), bf16 random weights, batch 1 with 8192
+cached tokens (random K/V) in shuffled 16-token pages, greedy decoding: each step
+feeds the argmax of the previous step's logits at the next position.
+
+One JSON line is printed.  `value` is decode tokens/s over the timed steps; the
+roofline block prices the step kernel against MI355X's 8 TB/s HBM with the
+algorithmic bytes of each step (active weights actually selected + KV read), and
+cpu_baseline times the CPU reference on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "decode tok/s + achieved HBM TB/s (% of SoL), 30B-A3B MoE bs1 @8K ctx"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_megakernel_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(geom, seq_lens, n_distinct_experts):
+    """Bytes a decode step must move at least once: every weight it uses (dense
+    projections, the distinct experts selected in each layer, the LM head, one
+    embedding row per token, the norm vectors) and every cached K/V it attends to.
+    n_distinct_experts: [n_layers] distinct experts selected by the batch."""
+    H, hd, nq, nkv = geom.hidden, geom.head_dim, geom.n_q_heads, geom.n_kv_heads
+    bf = 2
+    dense = (geom.qkv_rows * H + H * nq * hd + geom.n_experts * H + H) * bf
+    expert = (2 * geom.moe_inter * H + H * geom.moe_inter) * bf
+    kv_per_layer = sum((s + 1) for s in seq_lens) * nkv * hd * 2 * bf
+    total = 0
+    for layer in range(geom.n_layers):
+        total += dense + n_distinct_experts[layer] * expert + kv_per_layer
+    total += geom.vocab * H * bf + H * bf + len(seq_lens) * H * bf
+    return total
+
+
+def cpu_baseline(wl, n_layers_sample=2, reps=2):
+    """The CPU reference as it stands, timed on this host on a bounded sample: the
+    layer function on layers 0..n-1 of the workload (weights and that layer's KV
+    materialised on the host beforehand, untimed) and the final norm + LM head.
+    Scaled to one full step: t = n_layers * mean(t_layer) + t_lm_head."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    g = wl.geom
+    H = g.hidden
+    pt = synth.page_tables(wl)
+    toks = synth.host_tokens(wl)
+    numel = g.tensor_numel()
+    per_layer = {k: numel[k] // g.n_layers for k in ("w_qkv", "w_o", "w_router", "w_gate_up", "w_down")}
+    t_layers = []
+    h = oracle.bf16_to_f32(synth.host_weight(wl, "embed", int(toks[0]) * H, H)).reshape(1, H).copy()
+    for layer in range(n_layers_sample):
+        Wl = {k: synth.host_weight(wl, k, layer * n, n) for k, n in per_layer.items()}
+        gamma = synth.host_weight(wl, "norm", layer * H, H)
+        kv0 = synth.host_kv_layer(wl, layer)
+        for _ in range(reps):
+            kv = kv0.copy()
+            hh = h.copy()
+            t0 = time.perf_counter()
+            oracle.layer(g, wl.seq_lens, pt, kv, wl.n_pages, gamma, Wl["w_qkv"], Wl["w_o"], Wl["w_router"],
+                         Wl["w_gate_up"], Wl["w_down"], hh)
+            t_layers.append(time.perf_counter() - t0)
+        h = hh
+        del Wl, kv0
+    embed = synth.host_weight(wl, "embed")
+    gamma = synth.host_weight(wl, "norm", g.n_layers * H, H)
+    t_lm = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.lm_head(g, h, gamma, embed)
+        t_lm.append(time.perf_counter() - t0)
+    t_step = g.n_layers * float(np.mean(t_layers)) + float(np.mean(t_lm))
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": wl.batch / t_step,
+        "unit": "tok/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"layer function on {n_layers_sample} of {g.n_layers} layers x {reps} reps "
+                  f"({float(np.mean(t_layers)) * 1e3:.1f} ms/layer) + final norm and LM head "
+                  f"({float(np.mean(t_lm)) * 1e3:.1f} ms), scaled to one {g.n_layers}-layer step "
+                  f"of batch {wl.batch} at context {wl.seq_lens[0]}",
+        "ms_per_step": t_step * 1e3,
+    }
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import decode_megakernel_amd as mkd
+    import synth
+    from synth import device as sdev
+
+    torch.cuda.set_device(0)
+    ctx, batch = args.ctx, args.batch
+    total_steps = args.warmup + args.steps
+    wl = synth.full_workload(ctx=ctx, batch=batch, steps=min(total_steps, args.max_positions))
+    if args.layers:
+        import dataclasses
+        wl = dataclasses.replace(wl, geom=dataclasses.replace(wl.geom, n_layers=args.layers))
+    g = wl.geom
+    t_setup = time.perf_counter()
+    W = sdev.device_weights(wl)
+    pool = sdev.device_kv_pool(wl)
+    inp = sdev.device_step_inputs(wl)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    eng = mkd.Engine(g, 0, max_batch=batch, max_pages_per_seq=wl.max_pages)
+    eng.load_weights(W)
+    eng.set_mode(mkd.MODE_OP_PER_KERNEL if args.mode == "ablation" else mkd.MODE_MEGAKERNEL)
+    stream = torch.cuda.current_stream()
+    logits = torch.empty((batch, g.vocab), dtype=torch.float32, device="cuda")
+    tokens = inp["tokens"].clone()
+    base_lens = inp["h_seq_lens"].copy()
+    seq_lens = inp["seq_lens"].clone()
+    h_pt = inp["h_page_table"]
+
+    def step(s, ev=None):
+        # positions advance one per step and wrap after max_positions tokens
+        off = s % args.max_positions
+        h_lens = base_lens + off
+        seq_lens.copy_(torch.from_numpy(h_lens), non_blocking=False) if off == 0 else seq_lens.add_(1)
+        if ev is not None:
+            ev[0].record(stream)
+        eng.decode_step(tokens, seq_lens, h_lens, inp["page_table"], pool, wl.n_pages, logits,
+                        stream=stream.cuda_stream)
+        if ev is not None:
+            ev[1].record(stream)
+        torch.argmax(logits, dim=-1, out=tokens_i64)
+        tokens.copy_(tokens_i64)
+
+    tokens_i64 = torch.empty(batch, dtype=torch.int64, device="cuda")
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    eng.sync_status()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    eng.sync_status()
+    launch_ms = np.array([a.elapsed_time(b) for a, b in events])
+    elapsed = t1 - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    value = batch * args.steps / elapsed
+    # algorithmic bytes of each timed step (batch 1: top-k picks k distinct experts)
+    ids = eng.debug_read(mkd.DEBUG_TOPK_IDS, batch)
+    distinct = [len(np.unique(ids[l])) for l in range(g.n_layers)]
+    step_bytes = []
+    for i in range(args.steps):
+        off = (args.warmup + i) % args.max_positions
+        step_bytes.append(algorithmic_bytes(g, [s + off for s in wl.seq_lens], distinct))
+    mean_bytes = float(np.mean(step_bytes))
+    achieved = mean_bytes / (float(np.mean(launch_ms)) * 1e-3) / 1e9
+    sol_ms = mean_bytes / (PEAK_HBM_GBS * 1e9) * 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"synthetic 30B-total/~3B-active parallel-transformer MoE, {g.n_layers} layers, "
+                        f"batch {batch}, {ctx} cached tokens, greedy decode",
+            "batch": batch, "context": ctx, "layers": g.n_layers, "experts": g.n_experts, "top_k": g.top_k,
+            "mode": "megakernel" if args.mode != "ablation" else "op-per-kernel",
+        },
+        "achieved_TBps": round(mean_bytes / (ms_per_step * 1e-3) / 1e12, 4),
+        "sol_fraction": round(sol_ms / ms_per_step, 4),
+        "sol_tok_s": round(batch / (sol_ms * 1e-3), 1),
+        "bytes_per_step": int(mean_bytes),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "mk_persistent" if args.mode != "ablation" else "all step kernels",
+            "launch_ms_mean": round(float(np.mean(launch_ms)), 4),
+            "launch_ms_p10": round(float(np.percentile(launch_ms, 10)), 4),
+            "launch_ms_p90": round(float(np.percentile(launch_ms, 90)), 4),
+        },
+        "setup_s": round(setup_s, 2),
+        "kernel_source": kernel_source_hash(),
+    }
+    pmc = os.path.join(ROOT, "profiles", "mk_persistent_full_b1_ctx8k_traffic.json")
+    if os.path.exists(pmc) and args.mode != "ablation" and batch == 1 and ctx == 8192 and not args.layers:
+        with open(pmc) as f:
+            rec = json.load(f)
+        if rec.get("kernel_source") == out["kernel_source"]:
+            out["roofline"]["traffic"] = rec.get("traffic_bytes_per_launch")
+    if args.trace:
+        # one more step with the per-task trace on (not part of the timed region)
+        from decode_megakernel_amd import trace as mtrace
+        desc, _ = eng.plan(batch, torch.cuda.get_device_properties(0).multi_processor_count)
+        buf = torch.zeros((desc.shape[0], 4), dtype=torch.int64, device="cuda")
+        eng.set_trace(buf)
+        step(args.warmup + args.steps)
+        torch.cuda.synchronize()
+        eng.sync_status()
+        eng.set_trace(None)
+        rec = mtrace.decode(desc, buf.cpu().numpy())
+        summ = mtrace.summarize(rec)
+        mtrace.chrome_trace(rec, args.trace + ".chrome.json")
+        with open(args.trace, "w") as f:
+            json.dump(summ, f, indent=1)
+        out["trace_summary"] = {k: summ[k] for k in ("span_us", "layer_span_us_median",
+                                                      "workgroup_busy_fraction_mean")}
+    del W, pool
+    torch.cuda.empty_cache()
+    return out, wl
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--ctx", type=int, default=8192)
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (diagnostics)")
+    ap.add_argument("--mode", choices=["megakernel", "ablation"], default="megakernel")
+    ap.add_argument("--max-positions", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace", default="", help="write a per-task trace summary (JSON) here")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design "
+                                   "note, not an implemented path", "n_gpus": args.gpus}))
+        sys.exit(2)
+    libs = [os.path.join(ROOT, "decode_megakernel_amd", "libmkd.so"), os.path.join(ROOT, "synth", "libsynth_gpu.so"),
+            os.path.join(ROOT, "synth", "libsynth_host.so"), os.path.join(ROOT, "oracle", "liboracle.so")]
+    if not all(os.path.exists(p) for p in libs):
+        import __graft_entry__
+        __graft_entry__.build()
+    out, wl = run(args)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

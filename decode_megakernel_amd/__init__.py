@@ -32,7 +32,8 @@ DESC_WORDS = 32
 
 # every symbol include/mkd.h declares
 EXPORTS = ("mkd_create", "mkd_destroy", "mkd_load_weights", "mkd_set_mode", "mkd_decode_step",
-           "mkd_sync_status", "mkd_last_error", "mkd_debug_read", "mkd_plan_inspect")
+           "mkd_sync_status", "mkd_last_error", "mkd_debug_read", "mkd_plan_inspect",
+           "mkd_set_trace")
 
 
 class MkdError(RuntimeError):
@@ -74,6 +75,7 @@ def lib():
             "mkd_last_error": ([VP], ctypes.c_char_p),
             "mkd_debug_read": ([VP, I32, VP, ctypes.c_size_t], I32),
             "mkd_plan_inspect": ([VP, I32, I32, VP, I32, VP, P(I32)], I32),
+            "mkd_set_trace": ([VP, VP, ctypes.c_size_t], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -164,6 +166,14 @@ class Engine:
         out = np.empty(shape, dtype=dt)
         self._check(lib().mkd_debug_read(self._h, what, out.ctypes.data, out.nbytes))
         return out
+
+    def set_trace(self, buf):
+        """buf: uint64/int64 device tensor of n_tasks * 4 entries, or None to disable."""
+        if buf is None:
+            self._check(lib().mkd_set_trace(self._h, None, 0))
+        else:
+            self._check(lib().mkd_set_trace(self._h, _ptr(buf), buf.numel() * buf.element_size()))
+        self._trace = buf
 
     def plan(self, batch: int, n_cu: int):
         """(descriptors [n_tasks][32] int32 grouped by CU, cu_offsets [n_cu+1])."""

@@ -141,6 +141,10 @@ struct Params {
   const int32_t* cu_offsets; // [n_wg+1]
   int32_t max_attn_items;    // capacity of attn_part
   int32_t spin_limit;        // watchdog: polls before a wait gives up
+  // optional per-task trace: trace[gidx][4] = {start, inputs ready, end, meta}
+  // (100 MHz wall clock; meta = opcode | workgroup << 16 | claimed items << 32)
+  uint64_t* trace;
+  int32_t trace_cap;         // tasks the trace buffer holds
 };
 
 }  // namespace mkd

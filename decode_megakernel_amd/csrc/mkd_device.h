@@ -17,6 +17,14 @@
 
 namespace mkd {
 
+// Address spaces: global memory (1) and LDS (3).  Every pointer the kernels use
+// carries its address space so that the compiler emits global_* and ds_*
+// instructions: a generic (flat) access would count against both the vector-memory
+// and the LDS wait counters, making every LDS access and barrier wait for all weight
+// loads in flight.
+#define GAS __attribute__((address_space(1)))
+#define LAS __attribute__((address_space(3)))
+
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kWreg = 16;  // 16-byte weight chunks held in registers per lane
@@ -30,11 +38,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // ------------------------------------------------------------------ loads
 // Streaming (non-temporal) 16-byte load for weights and cached K/V: read once per
 // step, so they should not displace activations from the caches.
-__device__ __forceinline__ u32x4 ld_stream16(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+__device__ __forceinline__ u32x4 ld_stream16(const GAS void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const GAS u32x4*>(p));
 }
-__device__ __forceinline__ u32x2 ld_stream8(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+__device__ __forceinline__ u32x2 ld_stream8(const GAS void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const GAS u32x2*>(p));
 }
 
 // ------------------------------------------------------------------ bf16
@@ -54,7 +62,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // sum_k w[k] * x[k] over 8 bf16 weights and 8 fp32 activations.
-__device__ __forceinline__ float dot8(const u32x4 w, const float4 a, const float4 b) {
+__device__ __forceinline__ float dot8(const u32x4 w, const f32x4 a, const f32x4 b) {
   float s = bf_lo(w.x) * a.x;
   s = fmaf(bf_hi(w.x), a.y, s);
   s = fmaf(bf_lo(w.y), a.z, s);
@@ -80,11 +88,16 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ------------------------------------------------------------------ counters
-__device__ __forceinline__ uint32_t ctr_load(const uint32_t* c) {
+__device__ __forceinline__ uint32_t ctr_load(const GAS uint32_t* c) {
   return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t ctr_add(uint32_t* c, uint32_t v) {
+__device__ __forceinline__ uint32_t ctr_add(GAS uint32_t* c, uint32_t v) {
   return __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ctr_cas(GAS uint32_t* c, uint32_t expect, uint32_t v) {
+  __hip_atomic_compare_exchange_strong(c, &expect, v, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return expect;
 }
 __device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
@@ -92,15 +105,92 @@ __device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(_
 // particular) have completed.
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ uint32_t* gctr(const Params& p, int which) {
+// Device view of the kernel parameters: the same fields, with address-space
+// qualified pointers.
+struct DParams {
+  int32_t n_layers, hidden, n_q, n_kv, head_dim, n_experts, top_k, inter, vocab, page;
+  float rms_eps;
+  int32_t batch, max_batch, max_pages, n_pages;
+  PlanShape shape;
+  CounterLayout ctr;
+  const GAS uint16_t* embed;
+  const GAS uint16_t* norm;
+  const GAS uint16_t* w_qkv;
+  const GAS uint16_t* w_o;
+  const GAS uint16_t* w_router;
+  const GAS uint16_t* w_gate_up;
+  const GAS uint16_t* w_down;
+  const GAS int32_t* tokens;
+  const GAS int32_t* seq_lens;
+  const GAS int32_t* page_table;
+  GAS uint16_t* kv_pool;
+  GAS float* logits;
+  GAS float* h;
+  GAS float* ss;
+  GAS float* q;
+  GAS float* attn_part;
+  GAS float* attn_o;
+  GAS float* a_part;
+  GAS float* router;
+  GAS int32_t* topk_ids;
+  GAS float* topk_w;
+  GAS float* moe_act;
+  GAS float* m_part;
+  const GAS double* inv_freq;
+  GAS uint32_t* counters;
+  const GAS int32_t* tasks;
+  const GAS int32_t* cu_offsets;
+  int32_t max_attn_items;
+  int32_t spin_limit;
+  GAS uint64_t* trace;
+  int32_t trace_cap;
+};
+
+template <typename T>
+__device__ __forceinline__ GAS T* gas(T* p) {
+  return (GAS T*)p;
+}
+
+// Kernel arguments read through the constant address space (scalar loads).
+typedef const __attribute__((address_space(4))) Params KParams;
+
+__device__ __forceinline__ DParams device_view(KParams& p) {
+  DParams d;
+  d.n_layers = p.n_layers; d.hidden = p.hidden; d.n_q = p.n_q; d.n_kv = p.n_kv; d.head_dim = p.head_dim;
+  d.n_experts = p.n_experts; d.top_k = p.top_k; d.inter = p.inter; d.vocab = p.vocab; d.page = p.page;
+  d.rms_eps = p.rms_eps;
+  d.batch = p.batch; d.max_batch = p.max_batch; d.max_pages = p.max_pages; d.n_pages = p.n_pages;
+  d.shape.n_rt = p.shape.n_rt; d.shape.rt_rows = p.shape.rt_rows; d.shape.n_ds = p.shape.n_ds;
+  d.shape.up_rows = p.shape.up_rows; d.shape.n_up_tiles = p.shape.n_up_tiles;
+  d.shape.pages_per_item = p.shape.pages_per_item; d.shape.qkv_rows = p.shape.qkv_rows;
+  d.shape.router_rows = p.shape.router_rows; d.shape.lm_rows = p.shape.lm_rows;
+  d.ctr.per_layer = p.ctr.per_layer; d.ctr.x_ready = p.ctr.x_ready; d.ctr.qkv_done = p.ctr.qkv_done;
+  d.ctr.router_done = p.ctr.router_done; d.ctr.attn_claim = p.ctr.attn_claim; d.ctr.up_claim = p.ctr.up_claim;
+  d.ctr.down_claim = p.ctr.down_claim; d.ctr.comb = p.ctr.comb; d.ctr.attn_items = p.ctr.attn_items;
+  d.ctr.up_done = p.ctr.up_done; d.ctr.rt = p.ctr.rt; d.ctr.global_base = p.ctr.global_base;
+  d.ctr.total = p.ctr.total;
+  d.embed = gas(p.embed); d.norm = gas(p.norm); d.w_qkv = gas(p.w_qkv); d.w_o = gas(p.w_o);
+  d.w_router = gas(p.w_router); d.w_gate_up = gas(p.w_gate_up); d.w_down = gas(p.w_down);
+  d.tokens = gas(p.tokens); d.seq_lens = gas(p.seq_lens); d.page_table = gas(p.page_table);
+  d.kv_pool = gas(p.kv_pool); d.logits = gas(p.logits);
+  d.h = gas(p.h); d.ss = gas(p.ss); d.q = gas(p.q); d.attn_part = gas(p.attn_part); d.attn_o = gas(p.attn_o);
+  d.a_part = gas(p.a_part); d.router = gas(p.router); d.topk_ids = gas(p.topk_ids); d.topk_w = gas(p.topk_w);
+  d.moe_act = gas(p.moe_act); d.m_part = gas(p.m_part); d.inv_freq = gas(p.inv_freq);
+  d.counters = gas(p.counters); d.tasks = gas(p.tasks); d.cu_offsets = gas(p.cu_offsets);
+  d.max_attn_items = p.max_attn_items; d.spin_limit = p.spin_limit;
+  d.trace = gas(p.trace); d.trace_cap = p.trace_cap;
+  return d;
+}
+
+__device__ __forceinline__ GAS uint32_t* gctr(const DParams& p, int which) {
   return p.counters + p.ctr.global_base + which;
 }
-__device__ __forceinline__ bool aborted(const Params& p) { return ctr_load(gctr(p, G_ABORT)) != 0; }
+__device__ __forceinline__ bool aborted(const DParams& p) { return ctr_load(gctr(p, G_ABORT)) != 0; }
 
 // Record the first device-side error and stop every workgroup.
-__device__ inline void report_error(const Params& p, uint32_t code, int32_t task, int32_t ctr,
+__device__ inline void report_error(const DParams& p, uint32_t code, int32_t task, int32_t ctr,
                                     uint32_t seen, uint32_t want) {
-  if (atomicCAS(gctr(p, G_ERR_CODE), 0u, code) == 0u) {
+  if (ctr_cas(gctr(p, G_ERR_CODE), 0u, code) == 0u) {
     *gctr(p, G_ERR_TASK) = (uint32_t)task;
     *gctr(p, G_ERR_CTR) = (uint32_t)ctr;
     *gctr(p, G_ERR_SEEN) = seen;

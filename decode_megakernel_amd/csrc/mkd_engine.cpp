@@ -8,6 +8,7 @@
 // launch per wave of tasks).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -61,6 +62,8 @@ struct mkd_engine {
   std::string err;
   int32_t last_batch = 0;
   hipStream_t last_stream = nullptr;
+  uint64_t* trace = nullptr;
+  int32_t trace_cap = 0;
   ~mkd_engine() {
     if (device >= 0) {
       hipSetDevice(device);
@@ -89,23 +92,23 @@ std::string check_config(const mkd_config& c, int32_t max_batch, int32_t max_pag
   if (c.n_layers < 1 || c.hidden < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 ||
       c.n_experts < 1 || c.top_k < 1 || c.moe_inter < 1 || c.vocab < 1 || c.page_size < 1)
     return "all dimensions must be positive";
-  if (c.hidden != 256 && c.hidden != 512 && c.hidden != 1024 && c.hidden != 2048)
-    return "hidden must be one of 256, 512, 1024, 2048";
+  if (c.hidden != 256 && c.hidden != 2048) return "hidden must be 256 or 2048";
   if (c.head_dim != 64 && c.head_dim != 128) return "head_dim must be 64 or 128";
   if (c.n_q_heads % c.n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
   if (c.n_q_heads / c.n_kv_heads > 16) return "at most 16 query heads per KV group";
   {
     const int ko = c.n_q_heads * c.head_dim / c.n_kv_heads;
-    if (ko != 256 && ko != 512 && ko != 1024) return "n_q_heads*head_dim/n_kv_heads must be 256, 512 or 1024";
+    if (ko != 256 && ko != 1024) return "n_q_heads*head_dim/n_kv_heads must be 256 or 1024";
   }
-  if (c.moe_inter != 128 && c.moe_inter != 256 && c.moe_inter != 512 && c.moe_inter != 768)
-    return "moe_inter must be one of 128, 256, 512, 768";
+  if (c.moe_inter != 128 && c.moe_inter != 768) return "moe_inter must be 128 or 768";
   if (c.n_experts > 512) return "at most 512 experts";
   if (c.top_k > 16 || c.top_k > c.n_experts) return "top_k must be <= 16 and <= n_experts";
   if (c.page_size != 16) return "page_size must be 16";
+  if (c.n_kv_heads > 16) return "at most 16 KV groups";
   if (!(c.rms_eps >= 0.0f) || !(c.rope_base > 0.0f)) return "rms_eps >= 0 and rope_base > 0 required";
   if (max_batch < 1 || max_batch > 16) return "max_batch must be in [1, 16]";
   if (max_pages < 1) return "max_pages_per_seq must be positive";
+  if (max_pages > 24576) return "max_pages_per_seq must be <= 24576 (393216 tokens)";
   return "";
 }
 
@@ -327,6 +330,8 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
   p.kv_pool = (uint16_t*)kv_pool;
   p.logits = d_logits;
   p.cu_offsets = dp->d_offsets;
+  p.trace = e->trace;
+  p.trace_cap = e->trace_cap;
   hipStream_t s = (hipStream_t)stream;
   rc = launch_clear(p.counters, e->ctr.total, s);
   if (rc != hipSuccess) return hip_fail(e, rc, "counter clear");
@@ -371,6 +376,14 @@ int mkd_sync_status(mkd_engine* e) {
   const int code = st[G_ERR_CODE] == 1 ? MKD_ERR_DEADLOCK : MKD_ERR_ARG;
   hipMemset(e->base.counters + e->ctr.global_base, 0, sizeof(st));
   return code;
+}
+
+int mkd_set_trace(mkd_engine* e, void* dev_buf, size_t bytes) {
+  if (!e) return MKD_ERR_ARG;
+  if (dev_buf && bytes < 32) return fail(e, MKD_ERR_ARG, "trace buffer smaller than one record");
+  e->trace = (uint64_t*)dev_buf;
+  e->trace_cap = dev_buf ? (int32_t)std::min<size_t>(bytes / 32, 0x7FFFFFFF) : 0;
+  return MKD_OK;
 }
 
 const char* mkd_last_error(const mkd_engine* e) { return e ? e->err.c_str() : g_create_error.c_str(); }

@@ -1,0 +1,89 @@
+"""Decode the per-task trace of a megakernel step (see mkd_set_trace in include/mkd.h).
+
+Each task record holds the 100 MHz wall-clock time it started, the time its input
+counter was satisfied, the time it ended, and its opcode / workgroup / number of
+claimed items.  `summarize` reports, per opcode, the time spent waiting for inputs
+and working, per layer the span between its first start and last end, and per
+workgroup the idle time; `chrome_trace` writes the timeline in the Chrome /
+Perfetto trace-event format.
+"""
+from __future__ import annotations
+
+import json
+
+import numpy as np
+
+OPNAMES = {0: "nop", 1: "embed", 2: "qkv", 3: "router", 4: "attn", 5: "moe_up", 6: "moe_down",
+           7: "oproj", 8: "lm_head"}
+TICK_US = 0.01  # 100 MHz
+
+
+def decode(desc: np.ndarray, trace: np.ndarray) -> dict:
+    """desc: [n][32] descriptors (any order, field 10 = global index); trace: [>=n][4] uint64."""
+    gidx = desc[:, 10]
+    order = np.argsort(gidx)
+    d = desc[order]
+    t = trace[: len(d)].astype(np.int64)
+    valid = t[:, 2] > 0
+    t0 = t[valid, 0].min()
+    return {
+        "op": d[:, 0],
+        "layer": d[:, 1],
+        "gidx": d[:, 10],
+        "start": (t[:, 0] - t0) * TICK_US,
+        "ready": (t[:, 1] - t0) * TICK_US,
+        "end": (t[:, 2] - t0) * TICK_US,
+        "wg": ((t[:, 3] >> 16) & 0xFFFF).astype(np.int64),
+        "items": (t[:, 3] >> 32).astype(np.int64),
+        "valid": valid,
+    }
+
+
+def summarize(rec: dict) -> dict:
+    v = rec["valid"]
+    span = float(rec["end"][v].max() - rec["start"][v].min())
+    per_op = {}
+    for op in np.unique(rec["op"][v]):
+        m = v & (rec["op"] == op)
+        wait = rec["ready"][m] - rec["start"][m]
+        work = rec["end"][m] - rec["ready"][m]
+        per_op[OPNAMES.get(int(op), str(op))] = {
+            "tasks": int(m.sum()),
+            "wait_us_total": round(float(wait.sum()), 1),
+            "work_us_total": round(float(work.sum()), 1),
+            "work_us_mean": round(float(work.mean()), 2),
+            "items": int(rec["items"][m].sum()),
+        }
+    layers = {}
+    for layer in np.unique(rec["layer"][v]):
+        m = v & (rec["layer"] == layer)
+        layers[int(layer)] = round(float(rec["end"][m].max() - rec["start"][m].min()), 2)
+    n_wg = int(rec["wg"][v].max()) + 1
+    busy = np.zeros(n_wg)
+    for w in range(n_wg):
+        m = v & (rec["wg"] == w)
+        busy[w] = float((rec["end"][m] - rec["ready"][m]).sum())
+    lay = np.array(list(layers.values()))
+    return {
+        "span_us": round(span, 1),
+        "per_op": per_op,
+        "layer_span_us_median": round(float(np.median(lay)), 2) if len(lay) else 0.0,
+        "workgroup_busy_fraction_mean": round(float(busy.mean() / span), 4) if span > 0 else 0.0,
+        "layers": layers,
+    }
+
+
+def chrome_trace(rec: dict, path: str) -> None:
+    ev = []
+    v = rec["valid"]
+    for i in np.nonzero(v)[0]:
+        name = f"{OPNAMES.get(int(rec['op'][i]), '?')} L{int(rec['layer'][i])}"
+        wg = int(rec["wg"][i])
+        if rec["ready"][i] > rec["start"][i]:
+            ev.append({"name": "wait", "ph": "X", "pid": 0, "tid": wg, "ts": float(rec["start"][i]),
+                       "dur": float(rec["ready"][i] - rec["start"][i]), "cat": "wait"})
+        ev.append({"name": name, "ph": "X", "pid": 0, "tid": wg, "ts": float(rec["ready"][i]),
+                   "dur": float(max(rec["end"][i] - rec["ready"][i], 0.0)), "cat": "work",
+                   "args": {"gidx": int(rec["gidx"][i]), "items": int(rec["items"][i])}})
+    with open(path, "w") as f:
+        json.dump({"traceEvents": ev, "displayTimeUnit": "ns"}, f)

@@ -151,6 +151,14 @@ const char* mkd_last_error(const mkd_engine* eng);
 #define MKD_DEBUG_ROUTER 3
 int mkd_debug_read(mkd_engine* eng, int32_t what, void* dst, size_t bytes);
 
+/* Optional per-task trace of later steps (the tracing subsystem): dev_buf is a device
+   buffer of `bytes` bytes receiving, for the task at global index i of the step's
+   schedule, four uint64 at offset 32*i: wall-clock (100 MHz) start, time its input
+   counter was satisfied, end, and meta = opcode | workgroup << 16 | claimed items
+   << 32.  Tasks beyond the buffer are not recorded.  dev_buf = NULL disables it.
+   The caller owns the buffer. */
+int mkd_set_trace(mkd_engine* eng, void* dev_buf, size_t bytes);
+
 /* Plan inspection (host only; works on an engine created with hip_device = -1):
    writes the task descriptors the scheduler builds for `batch` sequences onto
    `n_cu` compute units.  desc receives n_tasks * 32 int32 in execution order per
