@@ -135,6 +135,8 @@ struct Params {
   float* moe_act;     // [L][maxB*k][I]
   float* m_part;      // [L][n_ds][maxB][H]
   const double* inv_freq;  // [hd/2] RoPE frequencies base^(-2i/hd), fp64
+  float* rope;             // [maxB][hd/2][2] cos, sin of this step's positions
+  const void* dummy;       // 1 KB of zeros: target of the GEMV ring's idle slots
   uint32_t* counters;
   // task lists
   const int32_t* tasks;      // [n_tasks][32]
@@ -142,7 +144,8 @@ struct Params {
   int32_t max_attn_items;    // capacity of attn_part
   int32_t spin_limit;        // watchdog: polls before a wait gives up
   // optional per-task trace: trace[gidx][4] = {start, inputs ready, end, meta}
-  // (100 MHz wall clock; meta = opcode | workgroup << 16 | claimed items << 32)
+  // (100 MHz wall clock; meta = opcode | workgroup << 8 | claimed items << 20 |
+  //  (inputs staged - start) << 32 | (workers done - start) << 48, both in clock ticks)
   uint64_t* trace;
   int32_t trace_cap;         // tasks the trace buffer holds
 };

@@ -24,10 +24,14 @@ namespace mkd {
 // loads in flight.
 #define GAS __attribute__((address_space(1)))
 #define LAS __attribute__((address_space(3)))
+// Read-only inputs (task lists, token ids, lengths, page tables) are read through the
+// constant address space, so wave-uniform reads become scalar loads.
+#define CAS __attribute__((address_space(4)))
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kWreg = 16;  // 16-byte weight chunks held in registers per lane
+constexpr int kWorkers = kWaves - 1;  // wave 0 is the controller
+constexpr int kWreg = 20;  // 16-byte weight chunks held in registers per worker lane
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -120,9 +124,9 @@ struct DParams {
   const GAS uint16_t* w_router;
   const GAS uint16_t* w_gate_up;
   const GAS uint16_t* w_down;
-  const GAS int32_t* tokens;
-  const GAS int32_t* seq_lens;
-  const GAS int32_t* page_table;
+  const CAS int32_t* tokens;
+  const CAS int32_t* seq_lens;
+  const CAS int32_t* page_table;
   GAS uint16_t* kv_pool;
   GAS float* logits;
   GAS float* h;
@@ -136,10 +140,11 @@ struct DParams {
   GAS float* topk_w;
   GAS float* moe_act;
   GAS float* m_part;
-  const GAS double* inv_freq;
+  const CAS double* inv_freq;
+  GAS float* rope;
   GAS uint32_t* counters;
-  const GAS int32_t* tasks;
-  const GAS int32_t* cu_offsets;
+  const CAS int32_t* tasks;
+  const CAS int32_t* cu_offsets;
   int32_t max_attn_items;
   int32_t spin_limit;
   GAS uint64_t* trace;
@@ -149,6 +154,10 @@ struct DParams {
 template <typename T>
 __device__ __forceinline__ GAS T* gas(T* p) {
   return (GAS T*)p;
+}
+template <typename T>
+__device__ __forceinline__ const CAS T* cas(const T* p) {
+  return (const CAS T*)p;
 }
 
 // Kernel arguments read through the constant address space (scalar loads).
@@ -171,12 +180,13 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.ctr.total = p.ctr.total;
   d.embed = gas(p.embed); d.norm = gas(p.norm); d.w_qkv = gas(p.w_qkv); d.w_o = gas(p.w_o);
   d.w_router = gas(p.w_router); d.w_gate_up = gas(p.w_gate_up); d.w_down = gas(p.w_down);
-  d.tokens = gas(p.tokens); d.seq_lens = gas(p.seq_lens); d.page_table = gas(p.page_table);
+  d.tokens = cas(p.tokens); d.seq_lens = cas(p.seq_lens); d.page_table = cas(p.page_table);
   d.kv_pool = gas(p.kv_pool); d.logits = gas(p.logits);
   d.h = gas(p.h); d.ss = gas(p.ss); d.q = gas(p.q); d.attn_part = gas(p.attn_part); d.attn_o = gas(p.attn_o);
   d.a_part = gas(p.a_part); d.router = gas(p.router); d.topk_ids = gas(p.topk_ids); d.topk_w = gas(p.topk_w);
-  d.moe_act = gas(p.moe_act); d.m_part = gas(p.m_part); d.inv_freq = gas(p.inv_freq);
-  d.counters = gas(p.counters); d.tasks = gas(p.tasks); d.cu_offsets = gas(p.cu_offsets);
+  d.moe_act = gas(p.moe_act); d.m_part = gas(p.m_part); d.inv_freq = cas(p.inv_freq);
+  d.rope = gas(p.rope);
+  d.counters = gas(p.counters); d.tasks = cas(p.tasks); d.cu_offsets = cas(p.cu_offsets);
   d.max_attn_items = p.max_attn_items; d.spin_limit = p.spin_limit;
   d.trace = gas(p.trace); d.trace_cap = p.trace_cap;
   return d;

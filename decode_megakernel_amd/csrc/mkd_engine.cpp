@@ -138,7 +138,6 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
   e->max_batch = max_batch;
   e->max_pages = max_pages_per_seq;
   if (cfg->hidden <= 256) e->opts.rt_rows = 32;
-  if (cfg->moe_inter <= 256) e->opts.up_rows = 16;
   if (cfg->head_dim / 2 < e->opts.qkv_pair_rows) e->opts.qkv_pair_rows = cfg->head_dim / 2;
   e->shape = make_shape(e->geom, e->opts);
   e->ctr = make_counters(e->geom, e->shape, max_batch);
@@ -183,6 +182,8 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
       {sizeof(float) * L * B * K * cfg->moe_inter, (void**)&p.moe_act},
       {sizeof(float) * L * e->shape.n_ds * B * H, (void**)&p.m_part},
       {sizeof(double) * cfg->head_dim / 2, (void**)&p.inv_freq},
+      {sizeof(float) * B * cfg->head_dim, (void**)&p.rope},
+      {1024, (void**)&p.dummy},
       {sizeof(uint32_t) * (size_t)e->ctr.total, (void**)&p.counters},
   };
   size_t total = 0;

@@ -78,8 +78,11 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   if (g.hidden % o.rt_rows) return "hidden must be a multiple of rt_rows";
   if (g.inter % o.up_rows) return "moe_inter must be a multiple of up_rows";
   if ((g.head_dim / 2) % o.qkv_pair_rows) return "head_dim/2 must be a multiple of qkv_pair_rows";
-  if (o.pages_per_item < 1 || o.pages_per_item > 16) return "pages_per_item must be in [1, 16]";
-  if (o.n_ds < 1) return "n_ds must be positive";
+  if (o.pages_per_item < 1 || o.pages_per_item > 14) return "pages_per_item must be in [1, 14]";
+  if (o.n_ds < 1 || o.n_ds > 16) return "n_ds must be in [1, 16]";
+  // a GEMV tile holds at most 5 row steps per worker wave (7 workers, >= 1 row per step)
+  if (o.rt_rows > 35 || 2 * o.up_rows > 35 || 2 * o.qkv_pair_rows > 35 || o.router_rows > 35 || o.lm_rows > 35)
+    return "GEMV tiles are limited to 35 rows";
   Plan& P = *out;
   P = Plan();
   P.batch = batch;

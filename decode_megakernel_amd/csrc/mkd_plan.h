@@ -26,9 +26,9 @@ enum WaveKind : int32_t { W_QKV = 0, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_O
 struct PlanOptions {
   int32_t rt_rows = 32;        // residual rows per O-proj / MoE-down tile
   int32_t n_ds = 8;            // MoE-down expert splits per row tile
-  int32_t up_rows = 16;        // activation rows per MoE-up item
-  int32_t pages_per_item = 16; // attention pages per claimed item (<= 16)
-  int32_t qkv_pair_rows = 16;  // RoPE pairs per QKV tile (tile = 2x rows)
+  int32_t up_rows = 8;         // activation rows per MoE-up item (weights: 2x rows)
+  int32_t pages_per_item = 14; // attention pages per claimed item (<= 14: 7 workers x 2 pages)
+  int32_t qkv_pair_rows = 8;   // RoPE pairs per QKV tile (tile = 2x rows)
   int32_t router_rows = 16;
   int32_t lm_rows = 32;
   int32_t n_attn_claimers = 0; // 0: automatic

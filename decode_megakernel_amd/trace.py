@@ -33,8 +33,10 @@ def decode(desc: np.ndarray, trace: np.ndarray) -> dict:
         "start": (t[:, 0] - t0) * TICK_US,
         "ready": (t[:, 1] - t0) * TICK_US,
         "end": (t[:, 2] - t0) * TICK_US,
-        "wg": ((t[:, 3] >> 16) & 0xFFFF).astype(np.int64),
-        "items": (t[:, 3] >> 32).astype(np.int64),
+        "wg": ((t[:, 3] >> 8) & 0xFFF).astype(np.int64),
+        "items": ((t[:, 3] >> 20) & 0xFFF).astype(np.int64),
+        "staged": (t[:, 0] - t0 + ((t[:, 3] >> 32) & 0xFFFF)) * TICK_US,
+        "done": (t[:, 0] - t0 + ((t[:, 3] >> 48) & 0xFFFF)) * TICK_US,
         "valid": valid,
     }
 
@@ -47,12 +49,17 @@ def summarize(rec: dict) -> dict:
         m = v & (rec["op"] == op)
         wait = rec["ready"][m] - rec["start"][m]
         work = rec["end"][m] - rec["ready"][m]
+        has = m & (rec["staged"] > rec["start"]) & (rec["done"] > rec["start"])
         per_op[OPNAMES.get(int(op), str(op))] = {
             "tasks": int(m.sum()),
             "wait_us_total": round(float(wait.sum()), 1),
             "work_us_total": round(float(work.sum()), 1),
             "work_us_mean": round(float(work.mean()), 2),
             "items": int(rec["items"][m].sum()),
+            # for single-tile tasks: ready -> inputs staged, staged -> compute done, done -> end
+            "stage_us_median": round(float(np.median(rec["staged"][has] - rec["ready"][has])), 2) if has.any() else None,
+            "compute_us_median": round(float(np.median(rec["done"][has] - rec["staged"][has])), 2) if has.any() else None,
+            "epilogue_us_median": round(float(np.median(rec["end"][has] - rec["done"][has])), 2) if has.any() else None,
         }
     layers = {}
     for layer in np.unique(rec["layer"][v]):

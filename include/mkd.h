@@ -154,8 +154,10 @@ int mkd_debug_read(mkd_engine* eng, int32_t what, void* dst, size_t bytes);
 /* Optional per-task trace of later steps (the tracing subsystem): dev_buf is a device
    buffer of `bytes` bytes receiving, for the task at global index i of the step's
    schedule, four uint64 at offset 32*i: wall-clock (100 MHz) start, time its input
-   counter was satisfied, end, and meta = opcode | workgroup << 16 | claimed items
-   << 32.  Tasks beyond the buffer are not recorded.  dev_buf = NULL disables it.
+   counter was satisfied, end, and meta = opcode (8 bits) | workgroup << 8 (12 bits) |
+   claimed items << 20 (12 bits) | ticks from start until the inputs were staged << 32
+   (16 bits) | ticks from start until the compute finished << 48 (16 bits).  Tasks
+   beyond the buffer are not recorded.  dev_buf = NULL disables it.
    The caller owns the buffer. */
 int mkd_set_trace(mkd_engine* eng, void* dev_buf, size_t bytes);
 
