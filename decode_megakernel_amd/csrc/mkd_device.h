@@ -109,6 +109,26 @@ __device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(_
 // particular) have completed.
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Stores of data that other workgroups read during the same step.  An agent-scope
+// atomic store is written through the XCD's L2 to the device-coherent level (it must be
+// visible to agent-scope loads on every XCD without any fence after it), so a producer
+// publishes such data by waiting for its own stores to complete and then adding to the
+// counter: no agent-scope release fence, whose L2 write-back of every dirty line costs
+// microseconds.  Consumers still acquire (invalidate) before reading with plain loads.
+__device__ __forceinline__ void st_pub(GAS float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_pub(GAS uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_pub4(GAS float* p, f32x4 v) {
+  GAS uint64_t* q = reinterpret_cast<GAS uint64_t*>(p);
+  __hip_atomic_store(q, (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (uint64_t)__float_as_uint(v.z) | ((uint64_t)__float_as_uint(v.w) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Device view of the kernel parameters: the same fields, with address-space
 // qualified pointers.
 struct DParams {

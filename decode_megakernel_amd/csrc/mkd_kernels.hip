@@ -141,12 +141,12 @@ __device__ __forceinline__ bool ctl_wait(Ctx& c, GAS uint32_t* ctr, uint32_t tar
   return __shfl(ok, 0, 64) != 0;
 }
 
-// Publish the controller's stores (the agent-scope release fence writes back the L2
-// and waits for this wave's stores) and add one to the counter; returns the old value.
+// Publish the controller's stores (written through with st_pub: waiting for their
+// completion suffices) and add one to the counter; returns the old value.
 __device__ __forceinline__ uint32_t ctl_arrive(Ctx& c, GAS uint32_t* ctr) {
   uint32_t old = 0;
   if (c.lane == 0) {
-    fence_release_agent();
+    wait_vm_all();
     old = ctr_add(ctr, 1u);
   }
   return (uint32_t)__shfl((int)old, 0, 64);
@@ -155,7 +155,7 @@ __device__ __forceinline__ uint32_t ctl_arrive(Ctx& c, GAS uint32_t* ctr) {
 // Same, when the old value is not needed (the atomic does not wait for a reply).
 __device__ __forceinline__ void ctl_signal(Ctx& c, GAS uint32_t* ctr) {
   if (c.lane == 0) {
-    fence_release_agent();
+    wait_vm_all();
     ctr_add(ctr, 1u);
   }
 }
@@ -385,14 +385,14 @@ __device__ __forceinline__ void ctl_finalize_rows(Ctx& c, int l, int rt) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) v += t[j];
     }
-    p.h[(int64_t)(l + 1) * hstride + hb] = v;
+    st_pub(p.h + (int64_t)(l + 1) * hstride + hb, v);
     red[i] = v * v;
   }
   for (int b = 0; b < B; ++b) {
     float t = 0.0f;
     for (int r = c.lane; r < R; r += 64) t += red[b * R + r];
     t = group_sum<64>(t);
-    if (c.lane == 0) p.ss[((int64_t)(l + 1) * p.max_batch + b) * p.shape.n_rt + rt] = t;
+    if (c.lane == 0) st_pub(p.ss + ((int64_t)(l + 1) * p.max_batch + b) * p.shape.n_rt + rt, t);
   }
   ctl_signal(c, layer_ctr(p, l + 1, p.ctr.x_ready));
 }
@@ -422,22 +422,22 @@ __device__ __forceinline__ bool op_embed(Ctx& c) {
       tok = 0;
     }
     const float v = bf16_to_f32(p.embed[(int64_t)tok * H + r]);
-    p.h[(int64_t)b * H + r] = v;
+    st_pub(p.h + (int64_t)b * H + r, v);
     red[i] = v * v;
   }
   for (int b = 0; b < B; ++b) {
     float t = 0.0f;
     for (int r = c.lane; r < R; r += 64) t += red[b * R + r];
     t = group_sum<64>(t);
-    if (c.lane == 0) p.ss[(int64_t)b * p.shape.n_rt + rt] = t;
+    if (c.lane == 0) st_pub(p.ss + (int64_t)b * p.shape.n_rt + rt, t);
   }
   if (rt == 0) {
     const int half = p.head_dim / 2;
     for (int i = c.lane; i < B * half; i += 64) {
       const int b = i / half, k = i % half;
       const double ang = (double)p.seq_lens[b] * p.inv_freq[k];
-      p.rope[2 * i] = (float)cos(ang);
-      p.rope[2 * i + 1] = (float)sin(ang);
+      st_pub(p.rope + 2 * i, (float)cos(ang));
+      st_pub(p.rope + 2 * i + 1, (float)sin(ang));
     }
   }
   ctl_signal(c, layer_ctr(p, 0, p.ctr.x_ready));
@@ -474,8 +474,8 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
       }
       if (hh < p.n_q) {
         GAS float* q = p.q + ((int64_t)l * p.max_batch + b) * p.n_q * hd + (int64_t)hh * hd;
-        q[dim] = o1;
-        q[dim + half] = o2;
+        st_pub(q + dim, o1);
+        st_pub(q + dim + half, o2);
       } else {
         const int lp = pos / p.page, t = pos % p.page;
         const int phys = (lp < p.max_pages) ? p.page_table[(int64_t)b * p.max_pages + lp] : -1;
@@ -488,11 +488,11 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
         const int64_t pg = (((int64_t)l * 2 + (is_k ? 0 : 1)) * p.n_pages + phys) * p.n_kv + g;
         GAS uint16_t* base = p.kv_pool + pg * (int64_t)p.page * hd;
         if (is_k) {
-          base[(int64_t)t * hd + dim] = f32_to_bf16(o1);
-          base[(int64_t)t * hd + dim + half] = f32_to_bf16(o2);
+          st_pub(base + (int64_t)t * hd + dim, f32_to_bf16(o1));
+          st_pub(base + (int64_t)t * hd + dim + half, f32_to_bf16(o2));
         } else {
-          base[(int64_t)dim * p.page + t] = f32_to_bf16(o1);
-          base[(int64_t)(dim + half) * p.page + t] = f32_to_bf16(o2);
+          st_pub(base + (int64_t)dim * p.page + t, f32_to_bf16(o1));
+          st_pub(base + (int64_t)(dim + half) * p.page + t, f32_to_bf16(o2));
         }
       }
     }
@@ -520,7 +520,7 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
     for (int i = c.lane; i < R * B; i += 64) {
       const int r = i / B, b = i % B;
       if (lm_head) p.logits[(int64_t)b * p.vocab + r0 + r] = c.s.rowsum[i];
-      else p.router[((int64_t)l * p.max_batch + b) * p.n_experts + r0 + r] = c.s.rowsum[i];
+      else st_pub(p.router + ((int64_t)l * p.max_batch + b) * p.n_experts + r0 + r, c.s.rowsum[i]);
     }
     if (c.d[D_SIGNAL] >= 0) ctl_signal(c, p.counters + c.d[D_SIGNAL]);
   }
@@ -545,7 +545,7 @@ __device__ __forceinline__ bool op_oproj(Ctx& c) {
     if (!ctl_gemv_barriers(c, ok)) return false;
     for (int i = c.lane; i < R * B; i += 64) {
       const int r = i / B, b = i % B;
-      p.a_part[(((int64_t)l * p.n_kv + g) * p.max_batch + b) * H + rt * R + r] = c.s.rowsum[i];
+      st_pub(p.a_part + (((int64_t)l * p.n_kv + g) * p.max_batch + b) * H + rt * R + r, c.s.rowsum[i]);
     }
     ctl_arrive_rt(c, l, rt);
   }
@@ -705,7 +705,7 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
         const float gt = c.s.rowsum[r * n_e + jj], u = c.s.rowsum[(UR + r) * n_e + jj];
         const float act = gt / (1.0f + expf(-gt)) * u;
         const int slot = rt[RT_FLAT + o0 + jj];  // b * k + j
-        p.moe_act[((int64_t)l * p.max_batch * k + slot) * I + (int64_t)tile * UR + r] = act;
+        st_pub(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * I + (int64_t)tile * UR + r, act);
       }
       ctl_signal(c, layer_ctr(p, l, p.ctr.up_done + e));
       if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
@@ -782,7 +782,7 @@ __device__ __forceinline__ bool op_moe_down(Ctx& c) {
     if (c.ctl) {
       for (int i = c.lane; i < R * B; i += 64) {
         const int r = i / B, b = i % B;
-        p.m_part[(((int64_t)l * NDS + ds) * p.max_batch + b) * H + (int64_t)rtile * R + r] = macc[i];
+        st_pub(p.m_part + (((int64_t)l * NDS + ds) * p.max_batch + b) * H + (int64_t)rtile * R + r, macc[i]);
       }
       ctl_arrive_rt(c, l, rtile);
     }
@@ -1003,7 +1003,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     bar();
     if (c.ctl) {
       GAS float* dst = p.attn_part + (int64_t)idx * hpg * (HD + 2);
-      for (int i = c.lane; i < hpg * (HD + 2); i += 64) dst[i] = part[i];
+      for (int i = c.lane; i < hpg * (HD + 2); i += 64) st_pub(dst + i, part[i]);
       const uint32_t old = ctl_arrive(c, layer_ctr(p, l, p.ctr.attn_items + b * nkv + g));
       if (c.lane == 0) c.s.mi[MI_OLD] = (int32_t)old;
     }
@@ -1047,7 +1047,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
           }
         }
         GAS float* dst = p.attn_o + ((int64_t)l * p.max_batch + b) * p.n_q * HD + (int64_t)(g * hpg + h) * HD + d4;
-        *reinterpret_cast<GAS f32x4*>(dst) = acc * mrow[h];
+        st_pub4(dst, acc * mrow[h]);
       }
       wait_vm_all();
       bar();
