@@ -225,7 +225,7 @@ def run(args):
     if args.trace:
         # one more step with the per-task trace on (not part of the timed region)
         from decode_megakernel_amd import trace as mtrace
-        desc, _ = eng.plan(batch, torch.cuda.get_device_properties(0).multi_processor_count)
+        desc, _, _ = eng.plan(batch, torch.cuda.get_device_properties(0).multi_processor_count)
         buf = torch.zeros((desc.shape[0], 4), dtype=torch.int64, device="cuda")
         eng.set_trace(buf)
         step(args.warmup + args.steps)
@@ -234,7 +234,8 @@ def run(args):
         eng.set_trace(None)
         rec = mtrace.decode(desc, buf.cpu().numpy())
         summ = mtrace.summarize(rec)
-        mtrace.chrome_trace(rec, args.trace + ".chrome.json")
+        if args.chrome:
+            mtrace.chrome_trace(rec, args.trace + ".chrome.json")
         with open(args.trace, "w") as f:
             json.dump(summ, f, indent=1)
         out["trace_summary"] = {k: summ[k] for k in ("span_us", "layer_span_us_median",
@@ -256,6 +257,7 @@ def main():
     ap.add_argument("--max-positions", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace", default="", help="write a per-task trace summary (JSON) here")
+    ap.add_argument("--chrome", action="store_true", help="with --trace: also write the Chrome trace")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design "

@@ -61,9 +61,11 @@ def lib():
     """Load libmkd.so; raises if it is absent (build it with __graft_entry__.build())."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
-        L = ctypes.CDLL(LIB_PATH)
+        # MKD_LIBRARY names another build of the same library (e.g. other tuning constants)
+        path = os.environ.get("MKD_LIBRARY", LIB_PATH)
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(path)
         P, I32, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_void_p
         sig = {
             "mkd_create": ([P(Config), I32, I32, I32, P(VP)], I32),
@@ -74,7 +76,7 @@ def lib():
             "mkd_sync_status": ([VP], I32),
             "mkd_last_error": ([VP], ctypes.c_char_p),
             "mkd_debug_read": ([VP, I32, VP, ctypes.c_size_t], I32),
-            "mkd_plan_inspect": ([VP, I32, I32, VP, I32, VP, P(I32)], I32),
+            "mkd_plan_inspect": ([VP, I32, I32, VP, I32, VP, P(I32), P(I32)], I32),
             "mkd_set_trace": ([VP, VP, ctypes.c_size_t], I32),
         }
         for name, (args, res) in sig.items():
@@ -176,11 +178,15 @@ class Engine:
         self._trace = buf
 
     def plan(self, batch: int, n_cu: int):
-        """(descriptors [n_tasks][32] int32 grouped by CU, cu_offsets [n_cu+1])."""
+        """(descriptors [n_tasks][32] int32 grouped by task list, list offsets
+        [n_cu * n_teams + 1], n_teams); list cu * n_teams + t is team t of CU cu."""
         n = ctypes.c_int32()
-        lib().mkd_plan_inspect(self._h, batch, n_cu, None, 0, None, ctypes.byref(n))
+        teams = ctypes.c_int32()
+        rc = lib().mkd_plan_inspect(self._h, batch, n_cu, None, 0, None, ctypes.byref(n), ctypes.byref(teams))
+        if rc not in (MKD_OK, MKD_ERR_CAPACITY):
+            self._check(rc)
         desc = np.empty((n.value, DESC_WORDS), dtype=np.int32)
-        offs = np.empty(n_cu + 1, dtype=np.int32)
+        offs = np.empty(2 * n_cu + 1, dtype=np.int32)
         self._check(lib().mkd_plan_inspect(self._h, batch, n_cu, desc.ctypes.data, n.value,
-                                           offs.ctypes.data, ctypes.byref(n)))
-        return desc, offs
+                                           offs.ctypes.data, ctypes.byref(n), ctypes.byref(teams)))
+        return desc, offs[: n_cu * teams.value + 1].copy(), teams.value

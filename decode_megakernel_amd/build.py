@@ -16,10 +16,13 @@ HIP_FLAGS = [
 SOURCES = ["mkd_kernels.hip", "mkd_plan.cpp", "mkd_engine.cpp"]
 
 
-def build(verbose=False, extra=()):
+def build(verbose=False, extra=(), out=SO):
+    """Compile every source and link `out`; `extra` holds additional hipcc flags (e.g.
+    -DMKD_RING=8 to change a tuning constant)."""
     objs = []
+    tag = str(abs(hash((tuple(extra), out))))
     for src in SOURCES:
-        obj = os.path.join(CSRC, src.rsplit(".", 1)[0] + ".o")
+        obj = os.path.join(CSRC, src.rsplit(".", 1)[0] + "." + tag + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = ["hipcc", *HIP_FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
@@ -29,14 +32,14 @@ def build(verbose=False, extra=()):
             sys.stderr.write(r.stderr)
             raise RuntimeError(f"hipcc failed on {src}")
         objs.append(obj)
-    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", SO]
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stderr)
         raise RuntimeError("link of libmkd.so failed")
     for o in objs:
         os.remove(o)
-    return SO
+    return out
 
 
 if __name__ == "__main__":

@@ -106,6 +106,7 @@ struct Params {
   int32_t n_layers, hidden, n_q, n_kv, head_dim, n_experts, top_k, inter, vocab, page;
   float rms_eps;
   int32_t batch, max_batch, max_pages, n_pages;
+  int32_t n_teams;  // teams per workgroup (1: 8 waves, 2: 4 waves each)
   PlanShape shape;
   CounterLayout ctr;
   // weights (bf16)
@@ -140,7 +141,7 @@ struct Params {
   uint32_t* counters;
   // task lists
   const int32_t* tasks;      // [n_tasks][32]
-  const int32_t* cu_offsets; // [n_wg+1]
+  const int32_t* cu_offsets; // [n_wg * n_teams + 1]: task list of team t of workgroup i is list i * n_teams + t
   int32_t max_attn_items;    // capacity of attn_part
   int32_t spin_limit;        // watchdog: polls before a wait gives up
   // optional per-task trace: trace[gidx][4] = {start, inputs ready, end, meta}

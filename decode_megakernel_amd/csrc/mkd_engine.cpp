@@ -25,6 +25,7 @@ namespace mkd {
 hipError_t launch_clear(uint32_t* counters, int32_t n, hipStream_t s);
 hipError_t launch_persistent(const Params& p, int n_wg, hipStream_t s);
 hipError_t launch_wave(const Params& p, int32_t first, int32_t count, hipStream_t s);
+int geometry_index(int hidden, int ko, int inter, int hd);
 }  // namespace mkd
 
 using namespace mkd;
@@ -92,16 +93,12 @@ std::string check_config(const mkd_config& c, int32_t max_batch, int32_t max_pag
   if (c.n_layers < 1 || c.hidden < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 ||
       c.n_experts < 1 || c.top_k < 1 || c.moe_inter < 1 || c.vocab < 1 || c.page_size < 1)
     return "all dimensions must be positive";
-  if (c.hidden != 256 && c.hidden != 2048) return "hidden must be 256 or 2048";
-  if (c.head_dim != 64 && c.head_dim != 128) return "head_dim must be 64 or 128";
   if (c.n_q_heads % c.n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
   if (c.n_q_heads / c.n_kv_heads > 16) return "at most 16 query heads per KV group";
-  {
-    const int ko = c.n_q_heads * c.head_dim / c.n_kv_heads;
-    if (ko != 256 && ko != 1024) return "n_q_heads*head_dim/n_kv_heads must be 256 or 1024";
-  }
-  if (c.moe_inter != 128 && c.moe_inter != 768) return "moe_inter must be 128 or 768";
-  if (c.n_experts > 512) return "at most 512 experts";
+  if (geometry_index(c.hidden, c.n_q_heads * c.head_dim / c.n_kv_heads, c.moe_inter, c.head_dim) < 0)
+    return "(hidden, n_q_heads*head_dim/n_kv_heads, moe_inter, head_dim) must be (2048, 1024, 768, 128) or "
+           "(256, 256, 128, 64): the kernel is compiled for these geometries";
+  if (c.n_experts > 256) return "at most 256 experts";
   if (c.top_k > 16 || c.top_k > c.n_experts) return "top_k must be <= 16 and <= n_experts";
   if (c.page_size != 16) return "page_size must be 16";
   if (c.n_kv_heads > 16) return "at most 16 KV groups";
@@ -138,11 +135,12 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
   e->max_batch = max_batch;
   e->max_pages = max_pages_per_seq;
   if (cfg->hidden <= 256) e->opts.rt_rows = 32;
-  if (cfg->head_dim / 2 < e->opts.qkv_pair_rows) e->opts.qkv_pair_rows = cfg->head_dim / 2;
-  e->shape = make_shape(e->geom, e->opts);
+  e->shape = make_shape(e->geom, e->opts, 1);
   e->ctr = make_counters(e->geom, e->shape, max_batch);
-  e->max_attn_items = max_batch * cfg->n_kv_heads *
-                      ((max_pages_per_seq + e->opts.pages_per_item - 1) / e->opts.pages_per_item);
+  {
+    const int ppi = std::min(e->opts.pages_per_item, e->opts.pages_per_item_2);
+    e->max_attn_items = max_batch * cfg->n_kv_heads * ((max_pages_per_seq + ppi - 1) / ppi);
+  }
   if (hip_device < 0) {  // host-only engine: plan inspection
     e->n_cu = 0;
     *out = e.release();
@@ -300,6 +298,12 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
     return fail(e, MKD_ERR_ARG, "NULL pointer argument");
   if (n_pages < 1) return fail(e, MKD_ERR_ARG, "n_pages must be positive");
   const int P = e->cfg.page_size;
+  hipError_t rc = hipSetDevice(e->device);
+  if (rc != hipSuccess) return hip_fail(e, rc, "hipSetDevice");
+  DevPlan* dp = nullptr;
+  int r = get_plan(e, batch, &dp);
+  if (r != MKD_OK) return r;
+  const int ppi = dp->plan.shape.pages_per_item;
   int64_t items = 0;
   for (int b = 0; b < batch; ++b) {
     const int32_t s = h_seq_lens[b];
@@ -314,15 +318,12 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
                                           ") = " + std::to_string(pg) + " is outside [0, n_pages)");
       }
     }
-    items += (int64_t)e->cfg.n_kv_heads * ((s / P + 1 + e->opts.pages_per_item - 1) / e->opts.pages_per_item);
+    items += (int64_t)e->cfg.n_kv_heads * ((s / P + 1 + ppi - 1) / ppi);
   }
   if (items > e->max_attn_items) return fail(e, MKD_ERR_CAPACITY, "attention work exceeds the workspace");
-  hipError_t rc = hipSetDevice(e->device);
-  if (rc != hipSuccess) return hip_fail(e, rc, "hipSetDevice");
-  DevPlan* dp = nullptr;
-  int r = get_plan(e, batch, &dp);
-  if (r != MKD_OK) return r;
   Params p = e->base;
+  p.n_teams = dp->plan.n_teams;
+  p.shape = dp->plan.shape;
   p.batch = batch;
   p.n_pages = n_pages;
   p.tokens = d_tokens;
@@ -414,12 +415,13 @@ int mkd_debug_read(mkd_engine* e, int32_t what, void* dst, size_t bytes) {
 }
 
 int mkd_plan_inspect(mkd_engine* e, int32_t batch, int32_t n_cu, int32_t* desc, int32_t max_tasks,
-                     int32_t* cu_offsets, int32_t* n_tasks) {
+                     int32_t* cu_offsets, int32_t* n_tasks, int32_t* n_teams) {
   if (!e || !n_tasks) return MKD_ERR_ARG;
   Plan plan;
   const std::string bad = build_plan(e->geom, e->opts, e->max_batch, batch, n_cu, &plan);
   if (!bad.empty()) return fail(e, MKD_ERR_ARG, "plan: " + bad);
   *n_tasks = plan.n_tasks();
+  if (n_teams) *n_teams = plan.n_teams;
   if (plan.n_tasks() > max_tasks) return fail(e, MKD_ERR_CAPACITY, "max_tasks too small");
   if (desc) std::memcpy(desc, plan.per_cu.data(), sizeof(int32_t) * plan.per_cu.size());
   if (cu_offsets) std::memcpy(cu_offsets, plan.cu_offsets.data(), sizeof(int32_t) * plan.cu_offsets.size());

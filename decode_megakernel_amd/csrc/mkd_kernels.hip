@@ -6,15 +6,20 @@
 //    step, walking a host-built task list in global memory; dependencies are counters
 //    that producers increment and consumers spin on.
 //  - "The threadblock shape": every opcode runs under one fixed shape with fixed
-//    roles.  Here: 8 wave64s; wave 0 is the controller (counter polls, queue claims,
-//    activation staging into LDS, epilogue stores, fences and arrives) and waves 1..7
-//    are workers that only stream weights / K-V from HBM and compute.  On gfx9 the
+//    roles.  Here: 8 wave64s forming one team of 8 waves or two teams of 4 (small
+//    batches).  A team walks its own task list; its first wave is the controller
+//    (counter polls, queue claims, activation staging into LDS, epilogue stores and
+//    arrives) and the others are workers that only stream weights / K-V from HBM and
+//    compute.  With two teams the attention branch (QKV, attention, O-proj) and the
+//    MoE branch (router, expert up, expert down) of a parallel layer run side by side
+//    on every CU, so one team streams while the other resolves a dependency.  On gfx9 the
 //    vector-memory counter is in order and shared by loads, stores and atomics, so a
 //    wave with weight loads in flight cannot get a quick answer from a poll, a small
 //    load or a store; keeping every latency-critical access on a wave that never
 //    streams weights is what lets the workers keep HBM busy while the controller
 //    resolves dependencies.  Barriers only order LDS, so worker loads stay in flight
-//    across them.
+//    across them; a two-team workgroup synchronises each team with an LDS counter
+//    instead of the workgroup-wide s_barrier.
 //  - "Tasks": the GEMM opcodes share one body (a bf16 GEMV tile held in worker
 //    registers, fp32 accumulation, wave reductions); QKV applies RoPE in the
 //    epilogue; attention is split over KV slices and combined; routing scores the
@@ -37,17 +42,27 @@
 namespace mkd {
 
 // ------------------------------------------------------------------ LDS layout
-// One workgroup per CU is forced by the LDS footprint (> half of the 160 KB).
-constexpr int kLdsXs = 0;            // 128 KB: activation staging, attention merge / combine
-constexpr int kLdsXsBytes = 131072;
-constexpr int kLdsRowsum = 131072;   // 8 KB: per-row results of a tile
-constexpr int kLdsRoute = 139264;    // 8 KB: routing tables
-constexpr int kLdsMisc = 147456;     // 1 KB: broadcasts, controller state, inverse RMS
-constexpr int kLdsBytes = 148480;
-constexpr int kAttnMaxChunks = 1536;  // attention chunks per (sequence, KV group) combined in LDS
-constexpr int kMaxPagesPerWave = 2;   // attention pages each worker holds in registers
+// One workgroup per CU is forced by the LDS footprint (> half of the 160 KB).  Each team
+// owns a region: activation staging / attention merge (xs), per-row results of a tile
+// (rowsum), routing tables (route) and controller state (misc).  One team of 8 waves has
+// 128 KB of xs (16 tokens x 2048 fp32); each of two teams of 4 waves has 44 KB (4 tokens).
+constexpr int kLdsRowsumBytes = 8192;
+constexpr int kLdsRouteBytes = 6144;
+constexpr int kLdsMiscBytes = 1024;
+constexpr int kXsBytes1 = 131072;
+constexpr int kXsBytes2 = 45056;
+constexpr int kTeamBytes1 = kXsBytes1 + kLdsRowsumBytes + kLdsRouteBytes + kLdsMiscBytes;
+constexpr int kTeamBytes2 = kXsBytes2 + kLdsRowsumBytes + kLdsRouteBytes + kLdsMiscBytes;
+constexpr int kLdsBar = kTeamBytes1;   // [2] team barrier counters
+constexpr int kLdsBytes = kLdsBar + 64;
+static_assert(2 * kTeamBytes2 <= kLdsBar, "two team regions must fit");
+#ifndef MKD_MAXP
+#define MKD_MAXP 1
+#endif
+constexpr int kMaxPagesPerWave = MKD_MAXP;  // attention pages each worker holds in registers
+constexpr int kMaccOffset = 640;      // MoE-down accumulator, floats after rowsum
 #ifndef MKD_RING
-#define MKD_RING 5
+#define MKD_RING 6
 #endif
 constexpr int kRing = MKD_RING;       // 16-byte weight chunks in flight per worker lane
 constexpr int kMaxSteps = 5;          // row steps per worker in one GEMV tile
@@ -59,12 +74,15 @@ struct Smem {
   LAS int32_t* route;
   LAS int32_t* mi;  // misc ints
   LAS float* mf;    // misc floats (inverse RMS per token)
-  __device__ explicit Smem(LAS char* base)
-      : xs(reinterpret_cast<LAS float*>(base + kLdsXs)),
-        rowsum(reinterpret_cast<LAS float*>(base + kLdsRowsum)),
-        route(reinterpret_cast<LAS int32_t*>(base + kLdsRoute)),
-        mi(reinterpret_cast<LAS int32_t*>(base + kLdsMisc)),
-        mf(reinterpret_cast<LAS float*>(base + kLdsMisc + 768)) {}
+  __device__ Smem(LAS char* lds, int team, int n_teams) {
+    const int xb = n_teams == 1 ? kXsBytes1 : kXsBytes2;
+    LAS char* base = lds + team * (n_teams == 1 ? kTeamBytes1 : kTeamBytes2);
+    xs = reinterpret_cast<LAS float*>(base);
+    rowsum = reinterpret_cast<LAS float*>(base + xb);
+    route = reinterpret_cast<LAS int32_t*>(base + xb + kLdsRowsumBytes);
+    mi = reinterpret_cast<LAS int32_t*>(base + xb + kLdsRowsumBytes + kLdsRouteBytes);
+    mf = reinterpret_cast<LAS float*>(base + xb + kLdsRowsumBytes + kLdsRouteBytes + 768);
+  }
 };
 // misc int slots
 constexpr int MI_OK = 1;         // controller -> workers: inputs ready (0: abort)
@@ -74,6 +92,7 @@ constexpr int MI_ITEMS = 4;      // trace: items claimed by the current task
 constexpr int MI_READY_LO = 6;   // trace: when the current task's first wait completed
 constexpr int MI_READY_HI = 7;
 constexpr int MI_XS_LAYER = 8;   // layer whose normed input xs holds (-1: none)
+constexpr int MI_ROUTE_LAYER = 9;  // layer whose routing tables the route area holds (-1: none)
 constexpr int MI_NEXT = 10;      // [2] claimed item indices (ping-pong)
 constexpr int MI_OLD = 12;       // previous counter value of the last arrive
 constexpr int MI_T_STAGED = 14;  // trace: low 32 bits of the clock when inputs were staged
@@ -96,14 +115,34 @@ struct Ctx {
   Smem s;
   const CAS int32_t* d;     // descriptor
   int32_t task;             // global task index
-  int32_t wave, lane, wi;   // wave (uniform), lane, worker index (wave - 1)
-  bool ctl;                 // wave 0: the controller
+  int32_t tw, lane, wi;     // wave within the team (uniform), lane, worker index (tw - 1)
+  int32_t nw;               // worker waves in the team (7 or 3)
+  int32_t tid, tthreads;    // thread index within the team, threads in the team
+  LAS uint32_t* barc;       // the team's barrier counter
+  bool ctl;                 // the team's first wave: the controller
 };
 
 __device__ __forceinline__ GAS uint32_t* layer_ctr(const DParams& p, int l, int off) {
   return p.counters + (int64_t)l * p.ctr.per_layer + off;
 }
-__device__ __forceinline__ void bar() { __syncthreads(); }
+// Team barrier.  A whole-workgroup team uses s_barrier; a 4-wave team counts arrivals in
+// its LDS counter (the counter only grows; an arrival's old value names the barrier
+// instance, whose last arrival brings the count to the next multiple of the team size).
+__device__ __forceinline__ void bar(const Ctx& c) {
+  if (c.nw == kWaves - 1) {
+    __syncthreads();
+    return;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  uint32_t old = 0;
+  if (c.lane == 0) old = __hip_atomic_fetch_add(c.barc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
+  const uint32_t waves = (uint32_t)(c.nw + 1);
+  const uint32_t target = (old / waves + 1u) * waves;
+  while (__hip_atomic_load(c.barc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+    __builtin_amdgcn_s_sleep(1);
+  asm volatile("" ::: "memory");
+}
 
 // ------------------------------------------------------------------ controller primitives
 // Spin until counter >= target (lane 0 polls, then acquire).  A wait this workgroup
@@ -170,6 +209,21 @@ __device__ __forceinline__ int32_t ctl_claim(Ctx& c, GAS uint32_t* head) {
   return __shfl(v, 0, 64);
 }
 
+// Issue a claim without waiting for the reply: the returned value (lane 0) is only
+// consumed by ctl_claim_put, placed where the reply has had time to arrive (the
+// wait-counter pass waits for it there).
+__device__ __forceinline__ uint32_t ctl_claim_issue(Ctx& c, GAS uint32_t* head) {
+  uint32_t v = 0;
+  if (c.lane == 0) {
+    v = ctr_add(head, 1u);
+    c.s.mi[MI_ITEMS] += 1;
+  }
+  return v;
+}
+__device__ __forceinline__ void ctl_claim_put(Ctx& c, int slot, uint32_t v) {
+  if (c.lane == 0) c.s.mi[slot] = (int32_t)v;
+}
+
 __device__ __forceinline__ void ctl_set_ok(Ctx& c, bool ok) {
   if (c.lane == 0) c.s.mi[MI_OK] = ok ? 1 : 0;
 }
@@ -180,14 +234,18 @@ __device__ __forceinline__ bool read_ok(Ctx& c) { return read_mi(c, MI_OK) != 0;
 // Weight rows of a tile come from up to two row segments (gate|up, or the two
 // halves of a RoPE head) with a common leading dimension.
 struct RowSrc {
-  const GAS uint16_t* base1;
-  const GAS uint16_t* base2;
-  int64_t ld;
-  int32_t n1;
-  __device__ const GAS uint16_t* row(int i) const {
-    return i < n1 ? base1 + (int64_t)i * ld : base2 + (int64_t)(i - n1) * ld;
+  const GAS uint16_t* base;  // first row of the first segment (wave-uniform)
+  uint32_t seg2;             // element offset of the second segment's first row
+  uint32_t ld;               // leading dimension (elements)
+  int32_t n1;                // rows in the first segment
+  // element offset of row i from base (32 bits: a tile spans a few MB at most)
+  __device__ uint32_t row_off(int i) const {
+    return i < n1 ? (uint32_t)i * ld : seg2 + (uint32_t)(i - n1) * ld;
   }
 };
+__device__ __forceinline__ RowSrc row_src(const GAS uint16_t* b1, const GAS uint16_t* b2, int64_t ld, int n1) {
+  return RowSrc{b1, (uint32_t)(b2 - b1), (uint32_t)ld, n1};
+}
 
 // Lane mapping of a K-long bf16 row onto a worker wave: LPR lanes per row, CPL
 // 16-byte chunks per lane per row, RPS rows per step; worker w takes steps w, w+7, ...
@@ -203,63 +261,67 @@ struct Gemv {
   static constexpr int CPL = CH / LPR;
   static constexpr int MAXS = kMaxSteps;
   static constexpr int NF = MAXS * CPL;
-  static constexpr int MAX_ROWS = MAXS * RPS * kWorkers;
   static_assert(K % 64 == 0, "row length must be a multiple of 64");
 };
 
 // Address of chunk f of this worker's share: row step f / CPL, 16-byte chunk f % CPL.
 template <int K>
-__device__ __forceinline__ const GAS void* gemv_chunk_addr(const Ctx& c, const RowSrc& src, int f) {
+__device__ __forceinline__ uint32_t gemv_chunk_off(const Ctx& c, const RowSrc& src, int f) {
   using G = Gemv<K>;
   const int si = f / G::CPL, cc = f % G::CPL;
-  const int row = (c.wi + kWorkers * si) * G::RPS + c.lane / G::LPR;
+  const int row = (c.wi + c.nw * si) * G::RPS + c.lane / G::LPR;
   const int kc = c.lane % G::LPR + G::LPR * cc;
-  return src.row(row) + kc * 8;
+  return src.row_off(row) + (uint32_t)kc * 8u;
 }
 
 // Worker side of a GEMV tile (includes the task's two barriers).  The worker's F chunks
 // (its row steps w, w+7, ... times CPL) stream through a ring of kRing loads: the first
 // kRing are issued before the first barrier (weight prefetch while the controller waits
 // for the inputs), the rest as chunks are consumed.  Every ring slot issues exactly one
-// load per round (slots past F load a small cached dummy line), so the loop body is
+// load per round (slots past F reload the worker's first chunk, a cache hit), so the
+// addresses are a wave-uniform base plus a 32-bit lane offset and the loop body is
 // straight-line and the wait-counter pass keeps kRing loads in flight.
 // rowsum[row * nb + j] = W[row] . x_j, x_j = xs + tok[j] * K, rows < R.  NB bounds nb.
 template <int K, int NB>
 __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R, const LAS float* xs,
-                                          const LAS int32_t* tok, int nb, LAS float* rowsum,
-                                          const GAS u32x4* dummy) {
+                                          const LAS int32_t* tok, int nb, LAS float* rowsum) {
   using G = Gemv<K>;
   const int S = (R + G::RPS - 1) / G::RPS;
-  const int ns = c.wi < S ? (S - c.wi + kWorkers - 1) / kWorkers : 0;
+  const int ns = c.wi < S ? (S - c.wi + c.nw - 1) / c.nw : 0;
   const int F = ns * G::CPL;
-  const GAS void* dum = dummy + c.lane;
+  const uint32_t off0 = gemv_chunk_off<K>(c, src, 0);
   u32x4 ring[kRing];
 #pragma unroll
-  for (int r = 0; r < kRing; ++r) ring[r] = ld_stream16(r < F ? gemv_chunk_addr<K>(c, src, r) : dum);
-  bar();
+  for (int r = 0; r < kRing; ++r) ring[r] = ld_stream16(src.base + (r < F ? gemv_chunk_off<K>(c, src, r) : off0));
+  bar(c);
   if (!read_ok(const_cast<Ctx&>(c))) return false;
   float acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = 0.0f;
+  int toff[NB];  // token row offsets into xs (wave-uniform)
+#pragma unroll
+  for (int j = 0; j < NB; ++j) toff[j] = (NB == 1 || j < nb) ? __builtin_amdgcn_readfirstlane(tok[j]) * K : 0;
   for (int base = 0; base < F; base += kRing) {
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
       const int f = base + r;
       const u32x4 w = ring[r];
       const int fn = f + kRing;
-      ring[r] = ld_stream16(fn < F ? gemv_chunk_addr<K>(c, src, fn) : dum);
+      ring[r] = ld_stream16(src.base + (fn < F ? gemv_chunk_off<K>(c, src, fn) : off0));
       if (f < F) {
         const int cc = f % G::CPL;
         const int kc = c.lane % G::LPR + G::LPR * cc;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           if (NB == 1 || j < nb) {
-            const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(xs + tok[j] * K + kc * 8);
+            const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(xs + toff[j] + kc * 8);
             acc[j] += dot8(w, xp[0], xp[1]);
           }
+          // bound the activations in flight to 4 tokens (32 registers)
+          if (NB > 1 && (j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
         if (cc == G::CPL - 1) {
-          const int row = (c.wi + kWorkers * (f / G::CPL)) * G::RPS + c.lane / G::LPR;
+          const int row = (c.wi + c.nw * (f / G::CPL)) * G::RPS + c.lane / G::LPR;
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
             if (NB == 1 || j < nb) {
@@ -272,53 +334,45 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
       }
     }
   }
-  bar();
+  bar(c);
   return true;
 }
 
 template <int K>
 __device__ __forceinline__ bool worker_gemv(const Ctx& c, const RowSrc& src, int R, const LAS float* xs,
                                             const LAS int32_t* tok, int nb, LAS float* rowsum) {
-  const GAS u32x4* dummy = (const GAS u32x4*)c.kp->dummy;
-  if (nb == 1) return gemv_tile<K, 1>(c, src, R, xs, tok, nb, rowsum, dummy);
-  return gemv_tile<K, kMaxBatch>(c, src, R, xs, tok, nb, rowsum, dummy);
+  if (nb == 1) return gemv_tile<K, 1>(c, src, R, xs, tok, nb, rowsum);
+  return gemv_tile<K, kMaxBatch>(c, src, R, xs, tok, nb, rowsum);
 }
 
-// Controller side of the same two barriers.
-__device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok) {
+// Controller side of the same two barriers.  A pending claim reply (next_slot >= 0) is
+// stored to its LDS slot while the workers compute.
+__device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_slot = -1, uint32_t claim = 0) {
   ctl_set_ok(c, ok);
   if (c.lane == 0 && c.s.mi[MI_T_STAGED] == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
-  bar();
+  bar(c);
   if (!ok) return false;
-  bar();
+  if (next_slot >= 0) ctl_claim_put(c, next_slot, claim);
+  bar(c);
   if (c.lane == 0 && c.s.mi[MI_T_DONE] == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
   return true;
 }
 
 // ------------------------------------------------------------------ activation staging (controller)
-// xs[b][k] = h_l[b][k] * inv_rms_b * gamma_l[k] for every token of the batch: the RMSNorm
-// that every consumer of layer l's input applies on the fly.  inv_rms_b comes from the
-// per-row-tile sums of squares written when the residual rows were finalised.  The
-// staged vector is kept while the next tasks on this CU read the same layer's input.
+// xs[b][k] = h_l[b][k] * gamma_l[k] and mf[b] = inv_rms_b for every token of the batch:
+// the RMSNorm that every consumer of layer l's input applies, with the per-token scale
+// moved to the consumer's epilogue (row sums times mf[token]) so that staging is one
+// round trip: the per-row-tile sums of squares (written when the residual rows were
+// finalised) are loaded together with h and gamma.  The staged vector is kept while the
+// next tasks on this CU read the same layer's input.
 __device__ __forceinline__ void ctl_stage_x_normed(Ctx& c, int l) {
   if (read_mi(c, MI_XS_LAYER) == l) return;
   const DParams p = device_view(*c.kp);
-  const int B = p.batch, H = p.hidden, NRT = p.shape.n_rt;
+  const int B = p.batch, H = p.hidden, NRT = p.shape.n_rt;  // NRT <= 64
   float part[16];
 #pragma unroll
-  for (int b = 0; b < 16; ++b) {
-    float t = 0.0f;
-    if (b < B)
-      for (int r = c.lane; r < NRT; r += 64) t += p.ss[((int64_t)l * p.max_batch + b) * NRT + r];
-    part[b] = t;
-  }
-#pragma unroll
-  for (int b = 0; b < 16; ++b) {
-    if (b < B) {
-      const float t = group_sum<64>(part[b]);
-      if (c.lane == 0) c.s.mf[b] = 1.0f / sqrtf(t / (float)H + p.rms_eps);
-    }
-  }
+  for (int b = 0; b < 16; ++b)
+    part[b] = (b < B && c.lane < NRT) ? p.ss[((int64_t)l * p.max_batch + b) * NRT + c.lane] : 0.0f;
   const GAS uint16_t* gamma = p.norm + (int64_t)l * H;
   const int n8 = B * (H / 8);
 #pragma unroll 4
@@ -328,15 +382,21 @@ __device__ __forceinline__ void ctl_stage_x_normed(Ctx& c, int l) {
     const f32x4 h0 = *reinterpret_cast<const GAS f32x4*>(hp);
     const f32x4 h1 = *reinterpret_cast<const GAS f32x4*>(hp + 4);
     const u32x4 gw = *reinterpret_cast<const GAS u32x4*>(gamma + k8);
-    const float r = c.s.mf[b];
     f32x4 o0, o1;
-    o0.x = h0.x * r * bf_lo(gw.x); o0.y = h0.y * r * bf_hi(gw.x);
-    o0.z = h0.z * r * bf_lo(gw.y); o0.w = h0.w * r * bf_hi(gw.y);
-    o1.x = h1.x * r * bf_lo(gw.z); o1.y = h1.y * r * bf_hi(gw.z);
-    o1.z = h1.z * r * bf_lo(gw.w); o1.w = h1.w * r * bf_hi(gw.w);
+    o0.x = h0.x * bf_lo(gw.x); o0.y = h0.y * bf_hi(gw.x);
+    o0.z = h0.z * bf_lo(gw.y); o0.w = h0.w * bf_hi(gw.y);
+    o1.x = h1.x * bf_lo(gw.z); o1.y = h1.y * bf_hi(gw.z);
+    o1.z = h1.z * bf_lo(gw.w); o1.w = h1.w * bf_hi(gw.w);
     LAS float* xo = c.s.xs + b * H + k8;
     *reinterpret_cast<LAS f32x4*>(xo) = o0;
     *reinterpret_cast<LAS f32x4*>(xo + 4) = o1;
+  }
+#pragma unroll
+  for (int b = 0; b < 16; ++b) {
+    if (b < B) {
+      const float t = group_sum<64>(part[b]);
+      if (c.lane == 0) c.s.mf[b] = 1.0f / sqrtf(t / (float)H + p.rms_eps);
+    }
   }
   if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
   if (c.lane == 0) c.s.mi[MI_XS_LAYER] = l;
@@ -455,20 +515,26 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
   const int l = c.d[D_LAYER], hh = c.d[D_ARG0], j0 = c.d[D_ARG1], PB = c.d[D_ARG2];
   const int hd = p.head_dim, half = hd / 2, H = p.hidden, B = p.batch;
   const GAS uint16_t* wl = p.w_qkv + (int64_t)l * (p.n_q + 2 * p.n_kv) * hd * H;
-  const RowSrc src{wl + ((int64_t)hh * hd + j0) * H, wl + ((int64_t)hh * hd + half + j0) * H, H, PB};
+  const RowSrc src = row_src(wl + ((int64_t)hh * hd + j0) * H, wl + ((int64_t)hh * hd + half + j0) * H, H, PB);
   if (!c.ctl) {
     return worker_gemv<K>(c, src, 2 * PB, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum);
   } else {
     const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
     if (ok) ctl_stage_x_normed(c, l);
+    // the epilogue's first (cos, sin) pair per lane is loaded while the workers compute
+    const bool rope_head = hh < p.n_q + p.n_kv;
+    f32x2 cs0 = f32x2{1.0f, 0.0f};
+    if (ok && rope_head && c.lane < PB * B)
+      cs0 = *reinterpret_cast<const GAS f32x2*>(p.rope + ((int64_t)(c.lane % B) * half + j0 + c.lane / B) * 2);
     if (!ctl_gemv_barriers(c, ok)) return false;
     for (int i = c.lane; i < PB * B; i += 64) {
       const int r = i / B, b = i % B, dim = j0 + r;
-      const float a = c.s.rowsum[r * B + b], bb = c.s.rowsum[(PB + r) * B + b];
+      const float a = c.s.rowsum[r * B + b] * c.s.mf[b], bb = c.s.rowsum[(PB + r) * B + b] * c.s.mf[b];
       const int pos = p.seq_lens[b];
       float o1 = a, o2 = bb;
-      if (hh < p.n_q + p.n_kv) {
-        const float cs = p.rope[((int64_t)b * half + dim) * 2], sn = p.rope[((int64_t)b * half + dim) * 2 + 1];
+      if (rope_head) {
+        const f32x2 csn = i == c.lane ? cs0 : *reinterpret_cast<const GAS f32x2*>(p.rope + ((int64_t)b * half + dim) * 2);
+        const float cs = csn.x, sn = csn.y;
         o1 = a * cs - bb * sn;
         o2 = bb * cs + a * sn;
       }
@@ -510,7 +576,7 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
   const int l = c.d[D_LAYER], r0 = c.d[D_ARG0], R = c.d[D_ARG1];
   const int H = p.hidden, B = p.batch;
   const GAS uint16_t* base = lm_head ? p.embed + (int64_t)r0 * H : p.w_router + ((int64_t)l * p.n_experts + r0) * H;
-  const RowSrc src{base, base, H, R};
+  const RowSrc src = row_src(base, base, H, R);
   if (!c.ctl) {
     return worker_gemv<K>(c, src, R, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum);
   } else {
@@ -519,8 +585,9 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
     if (!ctl_gemv_barriers(c, ok)) return false;
     for (int i = c.lane; i < R * B; i += 64) {
       const int r = i / B, b = i % B;
-      if (lm_head) p.logits[(int64_t)b * p.vocab + r0 + r] = c.s.rowsum[i];
-      else st_pub(p.router + ((int64_t)l * p.max_batch + b) * p.n_experts + r0 + r, c.s.rowsum[i]);
+      const float v = c.s.rowsum[i] * c.s.mf[b];
+      if (lm_head) p.logits[(int64_t)b * p.vocab + r0 + r] = v;
+      else st_pub(p.router + ((int64_t)l * p.max_batch + b) * p.n_experts + r0 + r, v);
     }
     if (c.d[D_SIGNAL] >= 0) ctl_signal(c, p.counters + c.d[D_SIGNAL]);
   }
@@ -536,7 +603,7 @@ __device__ __forceinline__ bool op_oproj(Ctx& c) {
   const int l = c.d[D_LAYER], rt = c.d[D_ARG0], g = c.d[D_ARG1];
   const int R = p.shape.rt_rows, H = p.hidden, KO = p.n_q * p.head_dim, B = p.batch;
   const GAS uint16_t* base = p.w_o + ((int64_t)l * H + (int64_t)rt * R) * KO + (int64_t)g * K;
-  const RowSrc src{base, base, KO, R};
+  const RowSrc src = row_src(base, base, KO, R);
   if (!c.ctl) {
     return worker_gemv<K>(c, src, R, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum);
   } else {
@@ -553,9 +620,9 @@ __device__ __forceinline__ bool op_oproj(Ctx& c) {
 }
 
 // ------------------------------------------------------------------ routing (all waves)
-// Exclusive prefix sum of one int per thread over the workgroup; total receives the sum.
-__device__ __forceinline__ int block_exscan(int v, LAS int32_t* tmp, int& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Exclusive prefix sum of one int per thread over the team; total receives the sum.
+__device__ __forceinline__ int team_exscan(const Ctx& c, int v, LAS int32_t* tmp, int& total) {
+  const int lane = c.lane, w = c.tw;
   int x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -563,15 +630,15 @@ __device__ __forceinline__ int block_exscan(int v, LAS int32_t* tmp, int& total)
     if (lane >= off) x += y;
   }
   if (lane == 63) tmp[w] = x;
-  bar();
+  bar(c);
   int pre = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
-    const int t = tmp[i];
+    const int t = i <= c.nw ? tmp[i] : 0;
     pre += i < w ? t : 0;
     tot += t;
   }
-  bar();
+  bar(c);
   total = tot;
   return pre + x - v;
 }
@@ -579,15 +646,18 @@ __device__ __forceinline__ int block_exscan(int v, LAS int32_t* tmp, int& total)
 // ROUTER_TOPK + ROUTE_FINALIZE + MOE_GATHER in LDS: top-k of each token's router logits
 // (descending, ties to the lower expert index), softmax over the selected logits, then
 // the active experts in ascending order and, per expert, its (token, slot) entries in
-// ascending token order.  Called by every wave after the controller's acquire of the
-// router counter; no wave has weight loads in flight here.
+// ascending token order.  Called by every wave of the team after the controller's
+// acquire of the router counter; no wave has weight loads in flight here.  The tables
+// stay valid for the rest of the layer (the MoE-down claimer after the MoE-up claimer
+// on the same CU reuses them).
 __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
+  if (!write_debug && read_mi(c, MI_ROUTE_LAYER) == l) return;
   const DParams p = device_view(*c.kp);
-  const int B = p.batch, E = p.n_experts, k = p.top_k;
+  const int B = p.batch, E = p.n_experts, k = p.top_k;  // E <= 256
   LAS int32_t* rt = c.s.route;
   LAS float* rw = reinterpret_cast<LAS float*>(rt + RT_W);
   const int lane = c.lane;
-  for (int b = c.wave; b < B; b += kWaves) {
+  for (int b = c.tw; b < B; b += c.nw + 1) {
     const GAS float* r = p.router + ((int64_t)l * p.max_batch + b) * E;
     float v[8];
 #pragma unroll
@@ -595,7 +665,6 @@ __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
       const int e = lane + 64 * i;
       v[i] = e < E ? r[e] : -INFINITY;
     }
-    float sel_v0 = 0.0f;
     for (int j = 0; j < k; ++j) {
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
@@ -613,13 +682,13 @@ __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (lane + 64 * i == bi) v[i] = -INFINITY;
-      if (j == 0) sel_v0 = bv;
       if (lane == 0) {
         rt[RT_IDS + b * 16 + j] = bi;
         rw[b * 16 + j] = bv;  // logit for now
       }
     }
     if (lane == 0) {
+      const float sel_v0 = rw[b * 16];
       float sum = 0.0f;
       for (int j = 0; j < k; ++j) {
         const float ex = expf(rw[b * 16 + j] - sel_v0);
@@ -629,17 +698,17 @@ __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
       for (int j = 0; j < k; ++j) rw[b * 16 + j] /= sum;
     }
   }
-  bar();
+  bar(c);
   // per-expert entry counts, one thread per expert, then block-wide exclusive scans give
   // each active expert its rank and its offset in the flat (token, slot) list.
-  const int e = threadIdx.x;
+  const int e = c.tid;  // E <= threads of a team
   int m_e = 0;
   if (e < E)
     for (int b = 0; b < B; ++b)
       for (int j = 0; j < k; ++j) m_e += rt[RT_IDS + b * 16 + j] == e;
   int n_entries = 0, n_act = 0;
-  const int off = block_exscan(m_e, c.s.mi + MI_SCAN, n_entries);
-  const int rank = block_exscan(m_e > 0 ? 1 : 0, c.s.mi + MI_SCAN, n_act);
+  const int off = team_exscan(c, m_e, c.s.mi + MI_SCAN, n_entries);
+  const int rank = team_exscan(c, m_e > 0 ? 1 : 0, c.s.mi + MI_SCAN, n_act);
   if (m_e > 0) {
     rt[RT_ACT + rank] = e;
     rt[RT_OFF + rank] = off;
@@ -648,16 +717,17 @@ __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
       for (int j = 0; j < k; ++j)
         if (rt[RT_IDS + b * 16 + j] == e) rt[RT_FLAT + at++] = b * k + j;
   }
-  if (threadIdx.x == 0) {
+  if (c.tid == 0) {
     rt[RT_OFF + n_act] = n_entries;
     rt[RT_NACT] = n_act;
   }
-  if (write_debug && threadIdx.x < B * k) {
-    const int b = threadIdx.x / k, j = threadIdx.x % k;
+  if (write_debug && c.tid < B * k) {
+    const int b = c.tid / k, j = c.tid % k;
     p.topk_ids[((int64_t)l * p.max_batch + b) * k + j] = rt[RT_IDS + b * 16 + j];
     p.topk_w[((int64_t)l * p.max_batch + b) * k + j] = rw[b * 16 + j];
   }
-  bar();
+  bar(c);
+  if (c.tid == 0) c.s.mi[MI_ROUTE_LAYER] = l;
 }
 
 // ------------------------------------------------------------------ OP_MOE_UP (claimer)
@@ -671,15 +741,14 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   const int UR = p.shape.up_rows, NT = p.shape.n_up_tiles, H = p.hidden, I = p.inter, k = p.top_k;
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.up_claim);
   if (c.ctl) {
+    // the claim does not depend on the routing (the index is interpreted after it)
+    const uint32_t first = ctl_claim_issue(c, head);
     const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
-    if (ok) {
-      ctl_stage_x_normed(c, l);
-      const int32_t first = ctl_claim(c, head);
-      if (c.lane == 0) c.s.mi[MI_NEXT] = first;
-    }
+    if (ok) ctl_stage_x_normed(c, l);
+    ctl_claim_put(c, MI_NEXT, first);
     ctl_set_ok(c, ok);
   }
-  bar();
+  bar(c);
   if (!read_ok(c)) return false;
   route_layer(c, l, c.d[D_ARG0] == 0);
   const LAS int32_t* rt = c.s.route;
@@ -692,19 +761,19 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
     const int o0 = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a]);
     const int n_e = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a + 1]) - o0;
     const GAS uint16_t* base = p.w_gate_up + (((int64_t)l * p.n_experts + e) * 2 * I + (int64_t)tile * UR) * H;
-    const RowSrc src{base, base + (int64_t)I * H, H, UR};
+    const RowSrc src = row_src(base, base + (int64_t)I * H, H, UR);
     if (!c.ctl) {
       if (!worker_gemv<K>(c, src, 2 * UR, c.s.xs, c.s.mi + MI_TOK, n_e, c.s.rowsum)) return false;
     } else {
       if (c.lane < n_e) c.s.mi[MI_TOK + c.lane] = rt[RT_FLAT + o0 + c.lane] / k;
-      const int32_t nxt = ctl_claim(c, head);
-      if (c.lane == 0) c.s.mi[MI_NEXT + ((j + 1) & 1)] = nxt;
-      if (!ctl_gemv_barriers(c, true)) return false;
+      const uint32_t nxt = ctl_claim_issue(c, head);
+      if (!ctl_gemv_barriers(c, true, MI_NEXT + ((j + 1) & 1), nxt)) return false;
       for (int i = c.lane; i < UR * n_e; i += 64) {
         const int r = i / n_e, jj = i % n_e;
-        const float gt = c.s.rowsum[r * n_e + jj], u = c.s.rowsum[(UR + r) * n_e + jj];
-        const float act = gt / (1.0f + expf(-gt)) * u;
         const int slot = rt[RT_FLAT + o0 + jj];  // b * k + j
+        const float sc = c.s.mf[slot / k];
+        const float gt = c.s.rowsum[r * n_e + jj] * sc, u = c.s.rowsum[(UR + r) * n_e + jj] * sc;
+        const float act = gt / (1.0f + expf(-gt)) * u;
         st_pub(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * I + (int64_t)tile * UR + r, act);
       }
       ctl_signal(c, layer_ctr(p, l, p.ctr.up_done + e));
@@ -727,36 +796,34 @@ __device__ __forceinline__ bool op_moe_down(Ctx& c) {
   const int R = p.shape.rt_rows, NDS = p.shape.n_ds, H = p.hidden, I = p.inter, B = p.batch, k = p.top_k;
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.down_claim);
   if (c.ctl) {
+    const uint32_t first = ctl_claim_issue(c, head);
     const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
-    if (ok) {
-      const int32_t first = ctl_claim(c, head);
-      if (c.lane == 0) c.s.mi[MI_NEXT] = first;
-      if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
-    }
+    ctl_claim_put(c, MI_NEXT, first);
+    if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
     ctl_set_ok(c, ok);
   }
-  bar();
+  bar(c);
   if (!read_ok(c)) return false;
   route_layer(c, l, false);
   const LAS int32_t* rt = c.s.route;
   const LAS float* rw = reinterpret_cast<const LAS float*>(rt + RT_W);
   const int n_act = __builtin_amdgcn_readfirstlane(rt[RT_NACT]);
-  LAS float* macc = c.s.rowsum + 1024;  // [R][B], controller only
+  LAS float* macc = c.s.rowsum + kMaccOffset;  // [R][B], controller only
   for (int j = 0;; ++j) {
     const int idx = read_mi(c, MI_NEXT + (j & 1));
     if (idx >= p.shape.n_rt * NDS) break;
     const int rtile = idx / NDS, ds = idx % NDS;
+    uint32_t nxt = 0;
     if (c.ctl) {
       for (int i = c.lane; i < R * B; i += 64) macc[i] = 0.0f;
-      const int32_t nxt = ctl_claim(c, head);
-      if (c.lane == 0) c.s.mi[MI_NEXT + ((j + 1) & 1)] = nxt;
+      nxt = ctl_claim_issue(c, head);  // reply stored at the end of the item
     }
     for (int a = ds; a < n_act; a += NDS) {
       const int e = __builtin_amdgcn_readfirstlane(rt[RT_ACT + a]);
       const int o0 = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a]);
       const int n_e = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a + 1]) - o0;
       const GAS uint16_t* base = p.w_down + (((int64_t)l * p.n_experts + e) * H + (int64_t)rtile * R) * I;
-      const RowSrc src{base, base, I, R};
+      const RowSrc src = row_src(base, base, I, R);
       if (!c.ctl) {
         if (!worker_gemv<K>(c, src, R, c.s.xs, c.s.mi + MI_TOK, n_e, c.s.rowsum)) return false;
       } else {
@@ -784,9 +851,10 @@ __device__ __forceinline__ bool op_moe_down(Ctx& c) {
         const int r = i / B, b = i % B;
         st_pub(p.m_part + (((int64_t)l * NDS + ds) * p.max_batch + b) * H + (int64_t)rtile * R + r, macc[i]);
       }
+      ctl_claim_put(c, MI_NEXT + ((j + 1) & 1), nxt);
       ctl_arrive_rt(c, l, rtile);
     }
-    bar();  // the next claimed index is published
+    bar(c);  // the next claimed index is published
   }
   return true;
 }
@@ -835,23 +903,31 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
   for (int b = 0; b < p.batch; ++b) n_items += ((p.seq_lens[b] / p.page + 1 + ppi - 1) / ppi) * nkv;
   if (n_items > p.max_attn_items) n_items = p.max_attn_items;
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.attn_claim);
-  LAS float* qs = c.s.xs;                              // [hpg][HD] fp32 queries
-  LAS float* mw = c.s.xs + 16 * HD;                    // [7][16] running max per worker
-  LAS float* lw = mw + kWorkers * 16;                  // [7][16] running sum
-  LAS float* ow = lw + kWorkers * 16;                  // [7][hpg][HD] unnormalised outputs
-  LAS float* part = ow + kWorkers * 16 * HD;           // [hpg][HD + 2] merged partial
+  const int nw = c.nw;
+  // The attention buffers go after this layer's staged normed input when both fit, so
+  // the MoE-up claimer that follows on this CU finds the input still staged.
+  const int attn_floats = 16 * HD + 2 * nw * 16 + nw * 16 * HD + 16 * (HD + 2);
+  const int xs_floats = (nw == kWaves - 1 ? kXsBytes1 : kXsBytes2) / 4;
+  const int keep = p.batch * p.hidden + attn_floats <= xs_floats ? p.batch * p.hidden : 0;
+  LAS float* ab = c.s.xs + keep;
+  LAS float* qs = ab;                                  // [hpg][HD] fp32 queries
+  LAS float* mw = ab + 16 * HD;                        // [nw][16] running max per worker
+  LAS float* lw = mw + nw * 16;                        // [nw][16] running sum
+  LAS float* ow = lw + nw * 16;                        // [nw][hpg][HD] unnormalised outputs
+  LAS float* part = ow + nw * 16 * HD;                 // [hpg][HD + 2] merged partial
   bool waited = false;
   if (c.ctl) {
     const int32_t first = ctl_claim(c, head);
     if (c.lane == 0) {
       c.s.mi[MI_NEXT] = first;
-      c.s.mi[MI_XS_LAYER] = -1;
+      if (keep == 0) c.s.mi[MI_XS_LAYER] = -1;
     }
   }
-  bar();
+  bar(c);
   for (int j = 0;; ++j) {
     const int idx = read_mi(c, MI_NEXT + (j & 1));
     if (idx >= n_items) break;
+    uint32_t nxt = 0;  // controller: claim reply for the next item
     int b, g = 0, chunk = 0, nchunks = 0, base_bg = 0;
     attn_map(p, idx, b, g, chunk, nchunks, base_bg);
     const int pos = p.seq_lens[b];
@@ -864,7 +940,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     if (!c.ctl) {
 #pragma unroll
       for (int i = 0; i < MAXP; ++i) {
-        lp[i] = c0 + c.wi + kWorkers * i;
+        lp[i] = c0 + c.wi + nw * i;
         kbase[i] = 0;
         vbase[i] = 0;
         if (lp[i] < c1) {
@@ -893,16 +969,28 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
         waited = true;
       }
       if (ok) {
+        // the query loads go first, the claim after them: writing the queries to LDS then
+        // waits for the loads only, and the claim reply arrives during the compute
         const GAS float* qsrc = p.q + ((int64_t)l * p.max_batch + b) * p.n_q * HD + (int64_t)g * hpg * HD;
-        for (int i = c.lane; i < hpg * HD / 4; i += 64)
-          *reinterpret_cast<LAS f32x4*>(qs + i * 4) = *reinterpret_cast<const GAS f32x4*>(qsrc + i * 4);
-        const int32_t nxt = ctl_claim(c, head);
-        if (c.lane == 0) c.s.mi[MI_NEXT + ((j + 1) & 1)] = nxt;
+        constexpr int QPL = 16 * HD / 4 / 64;  // f32x4 per lane for up to 16 heads
+        f32x4 qv[QPL];
+#pragma unroll
+        for (int u = 0; u < QPL; ++u) {
+          const int i = c.lane + 64 * u;
+          if (i < hpg * HD / 4) qv[u] = *reinterpret_cast<const GAS f32x4*>(qsrc + i * 4);
+        }
+        nxt = ctl_claim_issue(c, head);
+#pragma unroll
+        for (int u = 0; u < QPL; ++u) {
+          const int i = c.lane + 64 * u;
+          if (i < hpg * HD / 4) *reinterpret_cast<LAS f32x4*>(qs + i * 4) = qv[u];
+        }
       }
       ctl_set_ok(c, ok);
     }
-    bar();
+    bar(c);
     if (!read_ok(c)) return false;
+    if (c.ctl) ctl_claim_put(c, MI_NEXT + ((j + 1) & 1), nxt);
     if (!c.ctl) {
 #pragma unroll
       for (int i = 0; i < MAXP; ++i) {
@@ -982,14 +1070,14 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
           for (int r = 0; r < 4; ++r) ow[(c.wi * hpg + hq) * HD + dt * 16 + (c.lane >> 4) * 4 + r] = o[dt][r];
       }
     }
-    bar();
+    bar(c);
     // merge the workers: unnormalised o, running max M and sum L per head (all waves)
-    for (int t = threadIdx.x; t < hpg * HD; t += kThreads) {
+    for (int t = c.tid; t < hpg * HD; t += c.tthreads) {
       const int h = t / HD, dd = t % HD;
       float M = -INFINITY;
-      for (int ww = 0; ww < kWorkers; ++ww) M = fmaxf(M, mw[ww * 16 + h]);
+      for (int ww = 0; ww < nw; ++ww) M = fmaxf(M, mw[ww * 16 + h]);
       float acc = 0.0f, L = 0.0f;
-      for (int ww = 0; ww < kWorkers; ++ww) {
+      for (int ww = 0; ww < nw; ++ww) {
         const float sc = exp2f(mw[ww * 16 + h] - M);
         acc += sc * ow[(ww * hpg + h) * HD + dd];
         L += sc * lw[ww * 16 + h];
@@ -1000,57 +1088,63 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
         part[h * (HD + 2) + HD + 1] = L;
       }
     }
-    bar();
+    bar(c);
     if (c.ctl) {
       GAS float* dst = p.attn_part + (int64_t)idx * hpg * (HD + 2);
       for (int i = c.lane; i < hpg * (HD + 2); i += 64) st_pub(dst + i, part[i]);
       const uint32_t old = ctl_arrive(c, layer_ctr(p, l, p.ctr.attn_items + b * nkv + g));
       if (c.lane == 0) c.s.mi[MI_OLD] = (int32_t)old;
     }
-    bar();
+    bar(c);
     if ((uint32_t)read_mi(c, MI_OLD) + 1 == (uint32_t)nchunks) {
-      // last item of (b, g): combine all chunks (log-sum-exp merge, chunk order fixed)
+      // last item of (b, g): combine all chunks (log-sum-exp merge, chunk order fixed):
+      // per head the global max M and 1 / sum_c 2^(m_c - M) l_c, then the weighted sum
+      // of the chunks' unnormalised outputs.
       fence_acquire_agent();
       const GAS float* pb = p.attn_part + (int64_t)base_bg * hpg * (HD + 2);
-      LAS float* scl = c.s.xs;                         // [nchunks][hpg] merged weights
-      LAS float* mrow = c.s.xs + kAttnMaxChunks * 16;  // [hpg] inverse denominators
-      for (int h = c.wave; h < hpg; h += kWaves) {
+      LAS float* mrow = ab;       // [hpg] inverse denominators
+      LAS float* mmax = ab + 16;  // [hpg] maxima
+      for (int h = c.tw; h < hpg; h += nw + 1) {
         float M = -INFINITY;
         for (int ci = c.lane; ci < nchunks; ci += 64) M = fmaxf(M, pb[((int64_t)ci * hpg + h) * (HD + 2) + HD]);
         M = wave_max(M);
         float den = 0.0f;
         for (int ci = c.lane; ci < nchunks; ci += 64) {
           const GAS float* pc = pb + ((int64_t)ci * hpg + h) * (HD + 2);
-          const float sc = exp2f(pc[HD] - M);
-          scl[ci * hpg + h] = sc;
-          den += sc * pc[HD + 1];
+          den += exp2f(pc[HD] - M) * pc[HD + 1];
         }
         den = group_sum<64>(den);
-        if (c.lane == 0) mrow[h] = 1.0f / den;
+        if (c.lane == 0) {
+          mrow[h] = 1.0f / den;
+          mmax[h] = M;
+        }
       }
-      bar();
-      for (int t = threadIdx.x; t < hpg * (HD / 4); t += kThreads) {
+      bar(c);
+      for (int t = c.tid; t < hpg * (HD / 4); t += c.tthreads) {
         const int h = t / (HD / 4), d4 = (t % (HD / 4)) * 4;
+        const float M = mmax[h];
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int cb = 0; cb < nchunks; cb += 8) {
           f32x4 v[8];
+          float mc[8];
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
             v[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (cb + jj < nchunks)
-              v[jj] = *reinterpret_cast<const GAS f32x4*>(pb + ((int64_t)(cb + jj) * hpg + h) * (HD + 2) + d4);
+            mc[jj] = -INFINITY;
+            if (cb + jj < nchunks) {
+              const GAS float* pc = pb + ((int64_t)(cb + jj) * hpg + h) * (HD + 2);
+              v[jj] = *reinterpret_cast<const GAS f32x4*>(pc + d4);
+              mc[jj] = pc[HD];
+            }
           }
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const float sc = cb + jj < nchunks ? scl[(cb + jj) * hpg + h] : 0.0f;
-            acc += sc * v[jj];
-          }
+          for (int jj = 0; jj < 8; ++jj) acc += exp2f(mc[jj] - M) * v[jj];
         }
         GAS float* dst = p.attn_o + ((int64_t)l * p.max_batch + b) * p.n_q * HD + (int64_t)(g * hpg + h) * HD + d4;
         st_pub4(dst, acc * mrow[h]);
       }
       wait_vm_all();
-      bar();
+      bar(c);
       if (c.ctl) ctl_signal(c, layer_ctr(p, l, p.ctr.comb + g));
     }
   }
@@ -1058,14 +1152,19 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
 }
 
 // ------------------------------------------------------------------ dispatch
-// One non-inlined function per opcode: each gets its own register allocation, and
-// nothing but the task index lives across tasks in the interpreter loop.  Arguments are
-// made wave-uniform (scalar registers) on entry.
-#define MKD_CASE_K(KV, CALL) \
-  case KV: {                 \
-    constexpr int K = KV;    \
-    return CALL;             \
-  }
+// The interpreter is compiled once per model geometry (row lengths of the GEMV tiles and
+// the head dimension), so that each kernel holds only its own tile bodies: fewer code
+// paths share the register allocation of the single persistent function.  Every opcode
+// body is inlined; its arguments are made wave-uniform (scalar registers) on entry.
+template <int HID, int KO_, int INTER, int HD_>
+struct Geom {
+  static constexpr int kHidden = HID;   // QKV / router / MoE-up / LM-head row length
+  static constexpr int kKo = KO_;       // O-proj split (one KV group's columns)
+  static constexpr int kInter = INTER;  // MoE-down row length
+  static constexpr int kHd = HD_;       // head dimension
+};
+using GeomFull = Geom<2048, 1024, 768, 128>;
+using GeomTiny = Geom<256, 256, 128, 64>;
 
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -1074,43 +1173,53 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
 }
 
 #define MKD_EXEC(NAME, BODY)                                                                          \
-  __device__ __forceinline__ bool NAME(KParams* kp_in, LAS char* lds_in, const CAS int32_t* d_in, int32_t task_in) { \
+  template <class G>                                                                                  \
+  __device__ __forceinline__ bool NAME(KParams* kp_in, LAS char* lds_in, const CAS int32_t* d_in, int32_t task_in, \
+                                       int32_t team_in) {                                             \
     KParams* kp = (KParams*)uniform_u64((uint64_t)kp_in);                                             \
     const CAS int32_t* d = (const CAS int32_t*)uniform_u64((uint64_t)d_in);                           \
     LAS char* lds = (LAS char*)(uintptr_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_in); \
-    const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);                            \
-    Ctx c{kp, Smem(lds), d, __builtin_amdgcn_readfirstlane(task_in), wave, (int32_t)(threadIdx.x & 63), \
-          wave - 1, wave == 0};                                                                       \
+    const int32_t team = __builtin_amdgcn_readfirstlane(team_in);                                     \
+    const int32_t n_teams = kp->n_teams;                                                              \
+    const int32_t wpt = kWaves / n_teams;                                                             \
+    const int32_t tw = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6) - team * wpt);      \
+    const int32_t lane = (int32_t)(threadIdx.x & 63);                                                 \
+    Ctx c{kp, Smem(lds, team, n_teams), d, __builtin_amdgcn_readfirstlane(task_in), tw, lane, tw - 1,  \
+          wpt - 1, tw * 64 + lane, wpt * 64, reinterpret_cast<LAS uint32_t*>(lds + kLdsBar) + team,   \
+          tw == 0};                                                                                   \
     BODY                                                                                              \
   }
 
 MKD_EXEC(exec_embed, return op_embed(c);)
-MKD_EXEC(exec_qkv, switch (kp->hidden) { MKD_CASE_K(256, op_qkv<K>(c)) MKD_CASE_K(2048, op_qkv<K>(c)) } return false;)
-MKD_EXEC(exec_router, switch (kp->hidden) { MKD_CASE_K(256, op_rows_on_x<K>(c, false)) MKD_CASE_K(2048, op_rows_on_x<K>(c, false)) } return false;)
-MKD_EXEC(exec_lm_head, switch (kp->hidden) { MKD_CASE_K(256, op_rows_on_x<K>(c, true)) MKD_CASE_K(2048, op_rows_on_x<K>(c, true)) } return false;)
-MKD_EXEC(exec_oproj, switch (kp->n_q * kp->head_dim / kp->n_kv) { MKD_CASE_K(256, op_oproj<K>(c)) MKD_CASE_K(1024, op_oproj<K>(c)) } return false;)
-MKD_EXEC(exec_moe_up, switch (kp->hidden) { MKD_CASE_K(256, op_moe_up<K>(c)) MKD_CASE_K(2048, op_moe_up<K>(c)) } return false;)
-MKD_EXEC(exec_moe_down, switch (kp->inter) { MKD_CASE_K(128, op_moe_down<K>(c)) MKD_CASE_K(768, op_moe_down<K>(c)) } return false;)
-MKD_EXEC(exec_attn, if (kp->head_dim == 128) return op_attn<128>(c); if (kp->head_dim == 64) return op_attn<64>(c); return false;)
+MKD_EXEC(exec_qkv, return op_qkv<G::kHidden>(c);)
+MKD_EXEC(exec_router, return op_rows_on_x<G::kHidden>(c, false);)
+MKD_EXEC(exec_lm_head, return op_rows_on_x<G::kHidden>(c, true);)
+MKD_EXEC(exec_oproj, return op_oproj<G::kKo>(c);)
+MKD_EXEC(exec_moe_up, return op_moe_up<G::kHidden>(c);)
+MKD_EXEC(exec_moe_down, return op_moe_down<G::kInter>(c);)
+MKD_EXEC(exec_attn, return op_attn<G::kHd>(c);)
 
-__device__ __forceinline__ bool run_task(KParams* kp, LAS char* lds, const CAS int32_t* d, int32_t task) {
+template <class G>
+__device__ __forceinline__ bool run_task(KParams* kp, LAS char* lds, const CAS int32_t* d, int32_t task, int32_t team) {
   switch (d[D_OPCODE]) {
-    case OP_EMBED: return exec_embed(kp, lds, d, task);
-    case OP_QKV: return exec_qkv(kp, lds, d, task);
-    case OP_ROUTER: return exec_router(kp, lds, d, task);
-    case OP_LM_HEAD: return exec_lm_head(kp, lds, d, task);
-    case OP_OPROJ: return exec_oproj(kp, lds, d, task);
-    case OP_MOE_UP: return exec_moe_up(kp, lds, d, task);
-    case OP_MOE_DOWN: return exec_moe_down(kp, lds, d, task);
-    case OP_ATTN: return exec_attn(kp, lds, d, task);
+    case OP_EMBED: return exec_embed<G>(kp, lds, d, task, team);
+    case OP_QKV: return exec_qkv<G>(kp, lds, d, task, team);
+    case OP_ROUTER: return exec_router<G>(kp, lds, d, task, team);
+    case OP_LM_HEAD: return exec_lm_head<G>(kp, lds, d, task, team);
+    case OP_OPROJ: return exec_oproj<G>(kp, lds, d, task, team);
+    case OP_MOE_UP: return exec_moe_up<G>(kp, lds, d, task, team);
+    case OP_MOE_DOWN: return exec_moe_down<G>(kp, lds, d, task, team);
+    case OP_ATTN: return exec_attn<G>(kp, lds, d, task, team);
     default: return true;
   }
 }
 
-// Trace record of a finished task (controller lane 0; fields in LDS were set by the task).
-__device__ __forceinline__ void trace_task(KParams* kp, LAS int32_t* mi, const CAS int32_t* d, uint64_t t0) {
+// Trace record of a finished task (the team controller's lane 0; fields in LDS were set
+// by the task).  `list` = workgroup * teams + team.
+__device__ __forceinline__ void trace_task(KParams* kp, LAS int32_t* mi, const CAS int32_t* d, uint64_t t0,
+                                           bool leader, int list) {
   GAS uint64_t* trace = gas(kp->trace);
-  if (trace && threadIdx.x == 0) {
+  if (trace && leader) {
     const int32_t gi = d[D_GIDX];
     if (gi >= 0 && gi < kp->trace_cap) {
       const uint64_t ready = ((uint64_t)(uint32_t)mi[MI_READY_HI] << 32) | (uint32_t)mi[MI_READY_LO];
@@ -1119,10 +1228,10 @@ __device__ __forceinline__ void trace_task(KParams* kp, LAS int32_t* mi, const C
       r[0] = t0;
       r[1] = ready ? ready : t0;
       r[2] = tend;
-      // meta: opcode (8 bits) | workgroup (12) | items (12) | staged - start (16, 10 ns) | done - start (16)
+      // meta: opcode (8 bits) | list (12) | items (12) | staged - start (16, 10 ns) | done - start (16)
       const uint32_t st = mi[MI_T_STAGED] ? (uint32_t)mi[MI_T_STAGED] - (uint32_t)t0 : 0u;
       const uint32_t dn = mi[MI_T_DONE] ? (uint32_t)mi[MI_T_DONE] - (uint32_t)t0 : 0u;
-      r[3] = (uint64_t)((uint32_t)d[D_OPCODE] & 0xFFu) | ((uint64_t)(blockIdx.x & 0xFFFu) << 8) |
+      r[3] = (uint64_t)((uint32_t)d[D_OPCODE] & 0xFFu) | ((uint64_t)((uint32_t)list & 0xFFFu) << 8) |
              ((uint64_t)((uint32_t)mi[MI_ITEMS] & 0xFFFu) << 20) | ((uint64_t)min(st, 0xFFFFu) << 32) |
              ((uint64_t)min(dn, 0xFFFFu) << 48);
     }
@@ -1130,12 +1239,13 @@ __device__ __forceinline__ void trace_task(KParams* kp, LAS int32_t* mi, const C
 }
 
 // Controller-owned per-task state (no other wave reads it, so no barrier is needed).
-__device__ __forceinline__ void reset_task_state(LAS int32_t* mi, bool first) {
-  if (threadIdx.x == 0) {
+__device__ __forceinline__ void reset_task_state(LAS int32_t* mi, bool first, bool leader) {
+  if (leader) {
     if (first) {
       mi[MI_WAIT_CTR] = -1;
       mi[MI_WAIT_TGT] = 0;
       mi[MI_XS_LAYER] = -1;
+      mi[MI_ROUTE_LAYER] = -1;
     }
     mi[MI_ITEMS] = 0;
     mi[MI_READY_LO] = 0;
@@ -1145,15 +1255,24 @@ __device__ __forceinline__ void reset_task_state(LAS int32_t* mi, bool first) {
   }
 }
 
-// Persistent interpreter: workgroup i walks task list i.  All waves call every task; the
-// tasks' own barriers keep controller and workers in step.
+// Persistent interpreter: team t of workgroup i walks task list i * teams + t.  Every wave
+// of a team calls every task of its list; the tasks' own barriers keep its controller and
+// workers in step.
+template <class G>
 __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params prm) {
   __shared__ __align__(16) char lds_raw[kLdsBytes];
   LAS char* lds = (LAS char*)lds_raw;
   KParams* kp = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();
-  LAS int32_t* mi = reinterpret_cast<LAS int32_t*>(lds + kLdsMisc);
+  const int n_teams = prm.n_teams;
+  const int wpt = kWaves / n_teams;
+  const int team = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) / wpt);
+  const bool leader = (int)threadIdx.x == team * wpt * 64;
+  LAS int32_t* mi = Smem(lds, team, n_teams).mi;
+  if (threadIdx.x < 2) reinterpret_cast<LAS uint32_t*>(lds + kLdsBar)[threadIdx.x] = 0u;
+  __syncthreads();
+  const int list = (int)blockIdx.x * n_teams + team;
   const CAS int32_t* offs = cas(prm.cu_offsets);
-  const int begin = offs[blockIdx.x], end = offs[blockIdx.x + 1];
+  const int begin = offs[list], end = offs[list + 1];
   for (int t = begin; t < end; ++t) {
     // Opaque per task: argument fields are re-read (scalar cache) inside each task instead
     // of being hoisted out of the loop and kept live across every opcode body.
@@ -1161,26 +1280,29 @@ __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params prm) {
     asm volatile("" : "+s"(kpv));
     KParams* kpt = (KParams*)kpv;
     const CAS int32_t* d = cas(kpt->tasks) + (int64_t)t * D_WORDS;
-    reset_task_state(mi, t == begin);
+    reset_task_state(mi, t == begin, leader);
     const uint64_t t0 = kpt->trace ? wall_clock64() : 0;
-    const bool ok = run_task(kpt, lds, d, t);
-    trace_task(kpt, mi, d, t0);
+    const bool ok = run_task<G>(kpt, lds, d, t, team);
+    trace_task(kpt, mi, d, t0, leader, list);
     if (!ok) break;
   }
 }
 
-// Ablation: one launch per wave of tasks; block i runs task first + i.
+// Ablation: one launch per wave of tasks; block i (one team) runs task first + i.
+template <class G>
 __global__ void __launch_bounds__(kThreads, 1) mk_wave(Params prm, int32_t first) {
   __shared__ __align__(16) char lds_raw[kLdsBytes];
   LAS char* lds = (LAS char*)lds_raw;
   KParams* kp = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();
-  LAS int32_t* mi = reinterpret_cast<LAS int32_t*>(lds + kLdsMisc);
+  LAS int32_t* mi = Smem(lds, 0, prm.n_teams).mi;
+  if (threadIdx.x == 0) reinterpret_cast<LAS uint32_t*>(lds + kLdsBar)[0] = 0u;
+  __syncthreads();
   const int32_t t = first + (int32_t)blockIdx.x;
   const CAS int32_t* d = cas(prm.tasks) + (int64_t)t * D_WORDS;
-  reset_task_state(mi, true);
+  reset_task_state(mi, true, threadIdx.x == 0);
   const uint64_t t0 = prm.trace ? wall_clock64() : 0;
-  run_task(kp, lds, d, t);
-  trace_task(kp, mi, d, t0);
+  run_task<G>(kp, lds, d, t, 0);
+  trace_task(kp, mi, d, t0, threadIdx.x == 0, (int)blockIdx.x);
 }
 
 __global__ void mk_clear(uint32_t* counters, int32_t n) {
@@ -1197,14 +1319,28 @@ hipError_t launch_clear(uint32_t* counters, int32_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Geometry instance of a configuration: 0 = full (hidden 2048), 1 = tiny (hidden 256), -1 = none.
+int geometry_index(int hidden, int ko, int inter, int hd) {
+  if (hidden == GeomFull::kHidden && ko == GeomFull::kKo && inter == GeomFull::kInter && hd == GeomFull::kHd) return 0;
+  if (hidden == GeomTiny::kHidden && ko == GeomTiny::kKo && inter == GeomTiny::kInter && hd == GeomTiny::kHd) return 1;
+  return -1;
+}
+
 hipError_t launch_persistent(const Params& p, int n_wg, hipStream_t s) {
   void* args[] = {const_cast<Params*>(&p)};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mk_persistent), dim3(n_wg), dim3(kThreads),
+  const int gi = geometry_index(p.hidden, p.n_q * p.head_dim / p.n_kv, p.inter, p.head_dim);
+  if (gi < 0) return hipErrorInvalidValue;
+  const void* fn = gi == 0 ? reinterpret_cast<const void*>(&mk_persistent<GeomFull>)
+                           : reinterpret_cast<const void*>(&mk_persistent<GeomTiny>);
+  return hipLaunchCooperativeKernel(fn, dim3(n_wg), dim3(kThreads),
                                     args, 0, s);
 }
 
 hipError_t launch_wave(const Params& p, int32_t first, int32_t count, hipStream_t s) {
-  hipLaunchKernelGGL(mk_wave, dim3(count), dim3(kThreads), 0, s, p, first);
+  const int gi = geometry_index(p.hidden, p.n_q * p.head_dim / p.n_kv, p.inter, p.head_dim);
+  if (gi == 0) hipLaunchKernelGGL(mk_wave<GeomFull>, dim3(count), dim3(kThreads / p.n_teams), 0, s, p, first);
+  else if (gi == 1) hipLaunchKernelGGL(mk_wave<GeomTiny>, dim3(count), dim3(kThreads / p.n_teams), 0, s, p, first);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -7,15 +7,20 @@
 
 namespace mkd {
 
-PlanShape make_shape(const Geometry& g, const PlanOptions& o) {
+int32_t plan_teams(const PlanOptions& o, int32_t batch) {
+  if (o.teams == 1 || o.teams == 2) return o.teams;
+  return batch <= o.two_team_max_batch ? 2 : 1;
+}
+
+PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t n_teams) {
   PlanShape s{};
   s.rt_rows = o.rt_rows;
   s.n_rt = g.hidden / o.rt_rows;
   s.n_ds = o.n_ds;
   s.up_rows = o.up_rows;
   s.n_up_tiles = g.inter / o.up_rows;
-  s.pages_per_item = o.pages_per_item;
-  s.qkv_rows = 2 * o.qkv_pair_rows;
+  s.pages_per_item = n_teams == 2 ? o.pages_per_item_2 : o.pages_per_item;
+  s.qkv_rows = 2 * o.qkv_max_pairs;
   s.router_rows = o.router_rows;
   s.lm_rows = o.lm_rows;
   return s;
@@ -76,18 +81,24 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   if (batch < 1 || batch > max_batch) return "batch out of range";
   if (n_cu < 1) return "n_cu must be positive";
   if (g.hidden % o.rt_rows) return "hidden must be a multiple of rt_rows";
+  if (g.hidden / o.rt_rows > 64) return "hidden / rt_rows must be at most 64";
   if (g.inter % o.up_rows) return "moe_inter must be a multiple of up_rows";
-  if ((g.head_dim / 2) % o.qkv_pair_rows) return "head_dim/2 must be a multiple of qkv_pair_rows";
-  if (o.pages_per_item < 1 || o.pages_per_item > 14) return "pages_per_item must be in [1, 14]";
+  if (o.qkv_max_pairs < 1) return "qkv_max_pairs must be positive";
+  const int n_teams = plan_teams(o, batch);
+  if (n_teams == 2 && batch > 4) return "two teams hold at most 4 sequences";
+  if (g.n_experts > 256) return "at most 256 experts";
+  if (o.pages_per_item < 1 || o.pages_per_item > 7 * MKD_MAXP) return "pages_per_item exceeds 7 workers' pages";
+  if (o.pages_per_item_2 < 1 || o.pages_per_item_2 > 3 * MKD_MAXP) return "pages_per_item_2 exceeds 3 workers' pages";
   if (o.n_ds < 1 || o.n_ds > 16) return "n_ds must be in [1, 16]";
   // a GEMV tile holds at most 5 row steps per worker wave (7 workers, >= 1 row per step)
-  if (o.rt_rows > 35 || 2 * o.up_rows > 35 || 2 * o.qkv_pair_rows > 35 || o.router_rows > 35 || o.lm_rows > 35)
+  if (o.rt_rows > 35 || 2 * o.up_rows > 35 || 2 * o.qkv_max_pairs > 35 || o.router_rows > 35 || o.lm_rows > 35)
     return "GEMV tiles are limited to 35 rows";
   Plan& P = *out;
   P = Plan();
   P.batch = batch;
   P.n_cu = n_cu;
-  P.shape = make_shape(g, o);
+  P.n_teams = n_teams;
+  P.shape = make_shape(g, o, n_teams);
   P.ctr = make_counters(g, P.shape, max_batch);
   const PlanShape& s = P.shape;
   const CounterLayout& c = P.ctr;
@@ -100,9 +111,13 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   auto end_wave = [&]() { P.waves.back().count = P.n_tasks() - P.waves.back().first; };
 
   const int n_qkv_heads = g.n_q + 2 * g.n_kv;
-  const int n_qkv_tiles = n_qkv_heads * (g.head_dim / 2 / o.qkv_pair_rows);
+  const int half = g.head_dim / 2;
+  // tiles per head: about n_cu / heads, within [ceil(half / max_pairs), half]; the pairs of
+  // a head are split as evenly as possible
+  const int qkv_tph = std::min(half, std::max((half + o.qkv_max_pairs - 1) / o.qkv_max_pairs, n_cu / n_qkv_heads));
+  const int n_qkv_tiles = n_qkv_heads * qkv_tph;
   const int n_router_tiles = (g.n_experts + o.router_rows - 1) / o.router_rows;
-  const int n_attn = o.n_attn_claimers > 0 ? o.n_attn_claimers : std::max(1, n_cu / 2);
+  const int n_attn = o.n_attn_claimers > 0 ? o.n_attn_claimers : n_cu;
   const int n_up = o.n_up_claimers > 0 ? o.n_up_claimers : n_cu;
   const int n_down = o.n_down_claimers > 0 ? o.n_down_claimers : n_cu;
 
@@ -116,8 +131,10 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
       switch (kind) {
         case W_QKV:
           for (int hh = 0; hh < n_qkv_heads; ++hh)
-            for (int j0 = 0; j0 < g.head_dim / 2; j0 += o.qkv_pair_rows)
-              em.emit(OP_QKV, l, hh, j0, o.qkv_pair_rows, 0, L(l, c.x_ready), s.n_rt, L(l, c.qkv_done));
+            for (int t = 0; t < qkv_tph; ++t) {
+              const int j0 = t * half / qkv_tph, j1 = (t + 1) * half / qkv_tph;
+              em.emit(OP_QKV, l, hh, j0, j1 - j0, 0, L(l, c.x_ready), s.n_rt, L(l, c.qkv_done));
+            }
           break;
         case W_ROUTER:
           for (int r0 = 0; r0 < g.n_experts; r0 += o.router_rows)
@@ -153,19 +170,39 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
             -1);
   end_wave();
 
-  // deal task k to CU k mod n_cu, keeping global order within each CU
+  // Deal the tasks round robin, keeping global order within each list.  One team: task k
+  // goes to CU k mod n_cu.  Two teams: each branch has its own round robin over the CUs'
+  // team slot; embedding and LM-head tiles fill team 0 of every CU, then team 1.
   const int n = P.n_tasks();
-  std::vector<std::vector<int32_t>> lists(n_cu);
-  for (int k = 0; k < n; ++k) lists[k % n_cu].push_back(k);
-  P.cu_offsets.assign(n_cu + 1, 0);
+  const int n_lists = n_cu * n_teams;
+  std::vector<std::vector<int32_t>> lists(n_lists);
+  if (n_teams == 1) {
+    for (int k = 0; k < n; ++k) lists[k % n_cu].push_back(k);
+  } else {
+    int64_t rr[2] = {0, 0}, rr_all = 0;
+    for (const Wave& w : P.waves) {
+      for (int k = w.first; k < w.first + w.count; ++k) {
+        if (w.kind < 0) {
+          const int cu = (int)(rr_all % n_cu), t = (int)((rr_all / n_cu) % 2);
+          ++rr_all;
+          lists[cu * 2 + t].push_back(k);
+        } else {
+          const int t = (w.kind == W_QKV || w.kind == W_ATTN || w.kind == W_OPROJ) ? 0 : 1;
+          lists[(rr[t] % n_cu) * 2 + t].push_back(k);
+          ++rr[t];
+        }
+      }
+    }
+  }
+  P.cu_offsets.assign(n_lists + 1, 0);
   P.per_cu.reserve(P.global.size());
-  for (int cu = 0; cu < n_cu; ++cu) {
-    P.cu_offsets[cu] = (int32_t)(P.per_cu.size() / D_WORDS);
-    for (int32_t k : lists[cu])
+  for (int li = 0; li < n_lists; ++li) {
+    P.cu_offsets[li] = (int32_t)(P.per_cu.size() / D_WORDS);
+    for (int32_t k : lists[li])
       P.per_cu.insert(P.per_cu.end(), P.global.begin() + (size_t)k * D_WORDS,
                       P.global.begin() + (size_t)(k + 1) * D_WORDS);
   }
-  P.cu_offsets[n_cu] = (int32_t)(P.per_cu.size() / D_WORDS);
+  P.cu_offsets[n_lists] = (int32_t)(P.per_cu.size() / D_WORDS);
   return validate_plan(g, P);
 }
 
@@ -225,15 +262,21 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
     if (up_end < 0 || down_first < 0 || down_first < up_end)
       return "layer " + std::to_string(l) + ": MoE-down claimers must follow the MoE-up wave";
   }
-  // per-CU lists in increasing global order
-  for (int cu = 0; cu + 1 < (int)P.cu_offsets.size(); ++cu) {
+  // every list in increasing global order, every task in exactly one list
+  if ((int)P.cu_offsets.size() != P.n_cu * P.n_teams + 1) return "wrong number of task lists";
+  std::vector<char> seen(n, 0);
+  for (int li = 0; li + 1 < (int)P.cu_offsets.size(); ++li) {
     int32_t prev = -1;
-    for (int t = P.cu_offsets[cu]; t < P.cu_offsets[cu + 1]; ++t) {
+    for (int t = P.cu_offsets[li]; t < P.cu_offsets[li + 1]; ++t) {
       const int32_t gi = P.per_cu[(size_t)t * D_WORDS + D_GIDX];
-      if (gi <= prev) return "cu " + std::to_string(cu) + ": list not in global order";
+      if (gi <= prev) return "list " + std::to_string(li) + ": not in global order";
+      if (gi < 0 || gi >= n || seen[gi]) return "task " + std::to_string(gi) + " listed twice or out of range";
+      seen[gi] = 1;
       prev = gi;
     }
   }
+  for (int k = 0; k < n; ++k)
+    if (!seen[k]) return "task " + std::to_string(k) + " is in no list";
   return "";
 }
 

@@ -14,6 +14,13 @@
 
 #include "mkd_common.h"
 
+#ifndef MKD_MAXP
+#define MKD_MAXP 1  // attention pages per worker wave (kernel register budget)
+#endif
+#ifndef MKD_TEAMS
+#define MKD_TEAMS 1
+#endif
+
 namespace mkd {
 
 struct Geometry {
@@ -27,16 +34,22 @@ struct PlanOptions {
   int32_t rt_rows = 32;        // residual rows per O-proj / MoE-down tile
   int32_t n_ds = 8;            // MoE-down expert splits per row tile
   int32_t up_rows = 8;         // activation rows per MoE-up item (weights: 2x rows)
-  int32_t pages_per_item = 14; // attention pages per claimed item (<= 14: 7 workers x 2 pages)
-  int32_t qkv_pair_rows = 8;   // RoPE pairs per QKV tile (tile = 2x rows)
+  int32_t pages_per_item = 7 * MKD_MAXP;  // attention pages per claimed item, one team of 7 workers
+  int32_t pages_per_item_2 = 3 * MKD_MAXP;  // the same with two teams of 3 workers each
+  int32_t teams = MKD_TEAMS;    // teams per workgroup: 1, 2, or 0 = 2 when batch <= two_team_max_batch
+  int32_t two_team_max_batch = 4;
+  int32_t qkv_max_pairs = 17;  // RoPE pairs per QKV tile at most (tile = 2x rows); a head is
+                               // split into about n_cu / heads tiles so that one pass of QKV
+                               // tiles covers the compute units once
   int32_t router_rows = 16;
   int32_t lm_rows = 32;
   int32_t n_attn_claimers = 0; // 0: automatic
   int32_t n_up_claimers = 0;
   int32_t n_down_claimers = 0;
-  // Order of the waves inside a layer.  Default follows the pages' default order
-  // (qkv -> router -> attention -> MoE up/down -> O-proj).
+  // Order of the waves inside a layer: the pages' default order (qkv -> router ->
+  // attention -> MoE up/down -> O-proj), which measured fastest of the orders tried.
   int32_t order[W_KINDS] = {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_OPROJ};
+
 };
 
 struct Wave {
@@ -49,22 +62,28 @@ struct Wave {
 struct Plan {
   int32_t batch = 0;
   int32_t n_cu = 0;
+  int32_t n_teams = 1;              // task lists per CU
   PlanShape shape{};
   CounterLayout ctr{};
   std::vector<int32_t> global;      // [n][32] tasks in global (flattened) order
   std::vector<Wave> waves;          // ranges of `global`
-  std::vector<int32_t> per_cu;      // [n][32] tasks grouped by CU, each in global order
-  std::vector<int32_t> cu_offsets;  // [n_cu + 1]
+  std::vector<int32_t> per_cu;      // [n][32] tasks grouped by list (cu * n_teams + team), each in global order
+  std::vector<int32_t> cu_offsets;  // [n_cu * n_teams + 1]
   int32_t n_tasks() const { return (int32_t)(global.size() / D_WORDS); }
 };
 
 // Shape constants and counter layout (independent of the batch size except
 // attn_items, sized by max_batch).
-PlanShape make_shape(const Geometry& g, const PlanOptions& o);
+PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t n_teams);
+// Teams per workgroup the plan for `batch` uses.
+int32_t plan_teams(const PlanOptions& o, int32_t batch);
 CounterLayout make_counters(const Geometry& g, const PlanShape& s, int32_t max_batch);
 
-// Build the plan for `batch` sequences on `n_cu` compute units.  Returns "" on
-// success, else a description of the violated constraint.
+// Build the plan for `batch` sequences on `n_cu` compute units.  With two teams per
+// workgroup, the attention branch (QKV, attention, O-proj) goes to team 0 and the MoE
+// branch (router, expert up, expert down) to team 1 of every CU; embedding and LM-head
+// tiles are dealt over both.  Returns "" on success, else a description of the violated
+// constraint.
 std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batch, int32_t batch,
                        int32_t n_cu, Plan* out);
 

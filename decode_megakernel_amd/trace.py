@@ -77,7 +77,25 @@ def summarize(rec: dict) -> dict:
         "layer_span_us_median": round(float(np.median(lay)), 2) if len(lay) else 0.0,
         "workgroup_busy_fraction_mean": round(float(busy.mean() / span), 4) if span > 0 else 0.0,
         "layers": layers,
+        "layer_phases": layer_phases(rec, int(np.median(rec["layer"][v]))) if v.any() else {},
     }
+
+
+def layer_phases(rec: dict, layer: int) -> dict:
+    """Per opcode of one layer: [min, median, max] of task start, input-ready and end
+    times (us, relative to the layer's first task start), and the median work time."""
+    v = rec["valid"] & (rec["layer"] == layer)
+    if not v.any():
+        return {}
+    t0 = rec["start"][v].min()
+    out = {"layer": int(layer)}
+    for op in np.unique(rec["op"][v]):
+        m = v & (rec["op"] == op)
+        q = lambda x: [round(float(x.min() - t0), 1), round(float(np.median(x) - t0), 1), round(float(x.max() - t0), 1)]
+        out[OPNAMES.get(int(op), str(op))] = {
+            "n": int(m.sum()), "start": q(rec["start"][m]), "ready": q(rec["ready"][m]), "end": q(rec["end"][m]),
+            "work_median": round(float(np.median(rec["end"][m] - rec["ready"][m])), 2)}
+    return out
 
 
 def chrome_trace(rec: dict, path: str) -> None:

@@ -82,9 +82,11 @@ typedef struct mkd_engine mkd_engine;
 
 /* Create an engine for `cfg` on HIP device `hip_device`, able to decode batches of
    up to `max_batch` sequences whose page-table rows hold `max_pages_per_seq`
-   entries.  Allocates the engine's device workspace.  Geometry limits:
-   hidden % 256 == 0, head_dim in {64, 128}, n_q_heads / n_kv_heads <= 16,
-   n_experts <= 512, top_k <= 16, moe_inter % 128 == 0, max_batch <= 16.
+   entries.  Allocates the engine's device workspace.  Geometry limits (the kernel is
+   compiled for these row lengths): hidden in {256, 2048}, n_q_heads * head_dim /
+   n_kv_heads in {256, 1024}, moe_inter in {128, 768}, head_dim in {64, 128},
+   n_q_heads / n_kv_heads <= 16, n_kv_heads <= 16, n_experts <= 256, top_k <= 16,
+   page_size == 16, max_batch <= 16, max_pages_per_seq <= 24576.
    hip_device = -1 creates a host-only engine (plan inspection, no decoding).
    On error *out is set to NULL. */
 int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch,
@@ -154,7 +156,7 @@ int mkd_debug_read(mkd_engine* eng, int32_t what, void* dst, size_t bytes);
 /* Optional per-task trace of later steps (the tracing subsystem): dev_buf is a device
    buffer of `bytes` bytes receiving, for the task at global index i of the step's
    schedule, four uint64 at offset 32*i: wall-clock (100 MHz) start, time its input
-   counter was satisfied, end, and meta = opcode (8 bits) | workgroup << 8 (12 bits) |
+   counter was satisfied, end, and meta = opcode (8 bits) | task list << 8 (12 bits) |
    claimed items << 20 (12 bits) | ticks from start until the inputs were staged << 32
    (16 bits) | ticks from start until the compute finished << 48 (16 bits).  Tasks
    beyond the buffer are not recorded.  dev_buf = NULL disables it.
@@ -163,12 +165,15 @@ int mkd_set_trace(mkd_engine* eng, void* dev_buf, size_t bytes);
 
 /* Plan inspection (host only; works on an engine created with hip_device = -1):
    writes the task descriptors the scheduler builds for `batch` sequences onto
-   `n_cu` compute units.  desc receives n_tasks * 32 int32 in execution order per
-   CU, cu_offsets [n_cu+1] the start of each CU's list.  *n_tasks is set to the
-   total; MKD_ERR_CAPACITY if max_tasks is too small.  The descriptor layout
-   (32 int32; field 0 = opcode) is documented in decode_megakernel_amd/csrc/mkd_common.h. */
+   `n_cu` compute units.  Each CU runs n_teams task lists side by side (1 or 2;
+   *n_teams receives it if n_teams is not NULL); list cu * n_teams + t belongs to team
+   t of CU cu.  desc receives n_tasks * 32 int32, list after list, each in execution
+   order; cu_offsets (room for 2 * n_cu + 1 entries) receives the start of each list
+   and the total.  *n_tasks is set to the total; MKD_ERR_CAPACITY if max_tasks is too
+   small.  The descriptor layout (32 int32; field 0 = opcode) is documented in
+   decode_megakernel_amd/csrc/mkd_common.h. */
 int mkd_plan_inspect(mkd_engine* eng, int32_t batch, int32_t n_cu, int32_t* desc,
-                     int32_t max_tasks, int32_t* cu_offsets, int32_t* n_tasks);
+                     int32_t max_tasks, int32_t* cu_offsets, int32_t* n_tasks, int32_t* n_teams);
 
 #ifdef __cplusplus
 }

@@ -51,12 +51,23 @@ def _waves(desc):
                                              (synth.FULL, 1, 256), (synth.FULL, 16, 256)])
 def test_plan_structure(geom, batch, n_cu):
     e = mkd.Engine(geom, -1, 16, 64)
-    desc, offs = e.plan(batch, n_cu)
+    desc, offs, teams = e.plan(batch, n_cu)
+    assert teams in (1, 2)
+    assert len(offs) == n_cu * teams + 1
     assert offs[0] == 0 and offs[-1] == desc.shape[0] and (np.diff(offs) >= 0).all()
-    # round robin: CU c holds global indices c, c + n_cu, ...
-    for cu in range(n_cu):
-        gidx = desc[offs[cu]:offs[cu + 1], 10]
-        assert (gidx % n_cu == cu).all() and (np.diff(gidx) > 0).all()
+    # every task in exactly one list, each list in global order
+    assert sorted(desc[:, 10].tolist()) == list(range(desc.shape[0]))
+    for li in range(n_cu * teams):
+        gidx = desc[offs[li]:offs[li + 1], 10]
+        assert (np.diff(gidx) > 0).all()
+    if teams == 1:  # round robin: CU c holds global indices c, c + n_cu, ...
+        for cu in range(n_cu):
+            assert (desc[offs[cu]:offs[cu + 1], 10] % n_cu == cu).all()
+    else:  # attention branch on team 0, MoE branch on team 1
+        team_of = np.repeat(np.arange(n_cu * teams) % teams, np.diff(offs))
+        ops_ = desc[:, 0]
+        assert (team_of[np.isin(ops_, [OP_QKV, OP_ATTN, OP_OPROJ])] == 0).all()
+        assert (team_of[np.isin(ops_, [OP_ROUTER, OP_MOE_UP, OP_MOE_DOWN])] == 1).all()
     ops = desc[:, 0]
     gq = geom.n_q_heads + 2 * geom.n_kv_heads
     n_rt = geom.hidden // 32
