@@ -46,7 +46,7 @@ enum DescField : int32_t {
   D_OPCODE = 0,
   D_LAYER = 1,
   D_ARG0 = 2,   // first row / tile index / claimer index
-  D_ARG1 = 3,   // row count / kv group
+  D_ARG1 = 3,   // row count / kv group / claimer count
   D_ARG2 = 4,
   D_ARG3 = 5,
   D_WAIT = 6,   // counter index to wait on (-1: none)

@@ -199,23 +199,17 @@ __device__ __forceinline__ void ctl_signal(Ctx& c, GAS uint32_t* ctr) {
   }
 }
 
-// Claim the next item of a shared queue.
-__device__ __forceinline__ int32_t ctl_claim(Ctx& c, GAS uint32_t* head) {
-  int32_t v = 0;
-  if (c.lane == 0) {
-    v = (int32_t)ctr_add(head, 1u);
-    c.s.mi[MI_ITEMS] += 1;
-  }
-  return __shfl(v, 0, 64);
-}
-
-// Issue a claim without waiting for the reply: the returned value (lane 0) is only
+// Claimer queues: claimer i of n takes item i first without touching the queue, then
+// items n + (queue head), so the claimers' first items cost no atomic and the queue
+// only sees the later claims, spread over time.  The claimer index and count are the
+// descriptor's ARG0 and ARG1.
+// Issue a claim without waiting for the reply: the returned item (lane 0) is only
 // consumed by ctl_claim_put, placed where the reply has had time to arrive (the
 // wait-counter pass waits for it there).
 __device__ __forceinline__ uint32_t ctl_claim_issue(Ctx& c, GAS uint32_t* head) {
   uint32_t v = 0;
   if (c.lane == 0) {
-    v = ctr_add(head, 1u);
+    v = (uint32_t)c.d[D_ARG1] + ctr_add(head, 1u);
     c.s.mi[MI_ITEMS] += 1;
   }
   return v;
@@ -278,8 +272,8 @@ __device__ __forceinline__ uint32_t gemv_chunk_off(const Ctx& c, const RowSrc& s
 // (its row steps w, w+7, ... times CPL) stream through a ring of kRing loads: the first
 // kRing are issued before the first barrier (weight prefetch while the controller waits
 // for the inputs), the rest as chunks are consumed.  Every ring slot issues exactly one
-// load per round (slots past F reload the worker's first chunk, a cache hit), so the
-// addresses are a wave-uniform base plus a 32-bit lane offset and the loop body is
+// load per round (slots past F load a small dummy line that stays in the cache; the
+// addresses are a wave-uniform base plus a 32-bit lane offset), so the loop body is
 // straight-line and the wait-counter pass keeps kRing loads in flight.
 // rowsum[row * nb + j] = W[row] . x_j, x_j = xs + tok[j] * K, rows < R.  NB bounds nb.
 template <int K, int NB>
@@ -289,10 +283,10 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
   const int S = (R + G::RPS - 1) / G::RPS;
   const int ns = c.wi < S ? (S - c.wi + c.nw - 1) / c.nw : 0;
   const int F = ns * G::CPL;
-  const uint32_t off0 = gemv_chunk_off<K>(c, src, 0);
+  const GAS u32x4* dum = reinterpret_cast<const GAS u32x4*>(gas(c.kp->dummy)) + c.lane;
   u32x4 ring[kRing];
 #pragma unroll
-  for (int r = 0; r < kRing; ++r) ring[r] = ld_stream16(src.base + (r < F ? gemv_chunk_off<K>(c, src, r) : off0));
+  for (int r = 0; r < kRing; ++r) ring[r] = ld_stream16(r < F ? (const GAS void*)(src.base + gemv_chunk_off<K>(c, src, r)) : (const GAS void*)dum);
   bar(c);
   if (!read_ok(const_cast<Ctx&>(c))) return false;
   float acc[NB];
@@ -307,7 +301,7 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
       const int f = base + r;
       const u32x4 w = ring[r];
       const int fn = f + kRing;
-      ring[r] = ld_stream16(src.base + (fn < F ? gemv_chunk_off<K>(c, src, fn) : off0));
+      ring[r] = ld_stream16(fn < F ? (const GAS void*)(src.base + gemv_chunk_off<K>(c, src, fn)) : (const GAS void*)dum);
       if (f < F) {
         const int cc = f % G::CPL;
         const int kc = c.lane % G::LPR + G::LPR * cc;
@@ -741,11 +735,9 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   const int UR = p.shape.up_rows, NT = p.shape.n_up_tiles, H = p.hidden, I = p.inter, k = p.top_k;
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.up_claim);
   if (c.ctl) {
-    // the claim does not depend on the routing (the index is interpreted after it)
-    const uint32_t first = ctl_claim_issue(c, head);
     const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
     if (ok) ctl_stage_x_normed(c, l);
-    ctl_claim_put(c, MI_NEXT, first);
+    ctl_claim_put(c, MI_NEXT, (uint32_t)c.d[D_ARG0]);
     ctl_set_ok(c, ok);
   }
   bar(c);
@@ -796,9 +788,8 @@ __device__ __forceinline__ bool op_moe_down(Ctx& c) {
   const int R = p.shape.rt_rows, NDS = p.shape.n_ds, H = p.hidden, I = p.inter, B = p.batch, k = p.top_k;
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.down_claim);
   if (c.ctl) {
-    const uint32_t first = ctl_claim_issue(c, head);
     const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
-    ctl_claim_put(c, MI_NEXT, first);
+    ctl_claim_put(c, MI_NEXT, (uint32_t)c.d[D_ARG0]);
     if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
     ctl_set_ok(c, ok);
   }
@@ -917,9 +908,8 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
   LAS float* part = ow + nw * 16 * HD;                 // [hpg][HD + 2] merged partial
   bool waited = false;
   if (c.ctl) {
-    const int32_t first = ctl_claim(c, head);
     if (c.lane == 0) {
-      c.s.mi[MI_NEXT] = first;
+      c.s.mi[MI_NEXT] = c.d[D_ARG0];
       if (keep == 0) c.s.mi[MI_XS_LAYER] = -1;
     }
   }
@@ -937,30 +927,36 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     u32x2 vr[MAXP][NV];
     int lp[MAXP];
     int64_t kbase[MAXP], vbase[MAXP];
+    // element offsets of page lpg's K and V blocks for (layer l, group g); false (and an
+    // error report) for a page-table entry outside the pool
+    auto page_base = [&](int lpg, int64_t& kb, int64_t& vb) -> bool {
+      const int phys = lpg < p.max_pages ? p.page_table[(int64_t)b * p.max_pages + lpg] : -1;
+      if (phys < 0 || phys >= p.n_pages) {
+        if (c.lane == 0) report_error(p, 2u, c.task, -1, (uint32_t)phys, (uint32_t)p.n_pages);
+        return false;
+      }
+      kb = ((((int64_t)l * 2 + 0) * p.n_pages + phys) * nkv + g) * (int64_t)p.page * HD;
+      vb = ((((int64_t)l * 2 + 1) * p.n_pages + phys) * nkv + g) * (int64_t)p.page * HD;
+      return true;
+    };
+    // K operand: lane holds token (lane & 15), dims kk*32 + (lane>>4)*8 + [0, 8);
+    // V^T operand: lane holds dim dt*16 + (lane & 15), tokens (lane>>4)*4 + [0, 4)
+    auto load_page = [&](u32x4 (&kq)[NK], u32x2 (&vq)[NV], int64_t kb, int64_t vb) {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        kq[kk] = ld_stream16(p.kv_pool + kb + (c.lane & 15) * HD + kk * 32 + (c.lane >> 4) * 8);
+#pragma unroll
+      for (int dt = 0; dt < NV; ++dt)
+        vq[dt] = ld_stream8(p.kv_pool + vb + (dt * 16 + (c.lane & 15)) * 16 + (c.lane >> 4) * 4);
+    };
     if (!c.ctl) {
 #pragma unroll
       for (int i = 0; i < MAXP; ++i) {
         lp[i] = c0 + c.wi + nw * i;
         kbase[i] = 0;
         vbase[i] = 0;
-        if (lp[i] < c1) {
-          const int phys = lp[i] < p.max_pages ? p.page_table[(int64_t)b * p.max_pages + lp[i]] : -1;
-          if (phys < 0 || phys >= p.n_pages) {
-            if (c.lane == 0) report_error(p, 2u, c.task, -1, (uint32_t)phys, (uint32_t)p.n_pages);
-            lp[i] = c1;  // skip
-          } else {
-            kbase[i] = ((((int64_t)l * 2 + 0) * p.n_pages + phys) * nkv + g) * (int64_t)p.page * HD;
-            vbase[i] = ((((int64_t)l * 2 + 1) * p.n_pages + phys) * nkv + g) * (int64_t)p.page * HD;
-          }
-        }
-        if (lp[i] < c1 && lp[i] != last) {
-#pragma unroll
-          for (int kk = 0; kk < NK; ++kk)
-            kr[i][kk] = ld_stream16(p.kv_pool + kbase[i] + (c.lane & 15) * HD + kk * 32 + (c.lane >> 4) * 8);
-#pragma unroll
-          for (int dt = 0; dt < NV; ++dt)
-            vr[i][dt] = ld_stream8(p.kv_pool + vbase[i] + (dt * 16 + (c.lane & 15)) * 16 + (c.lane >> 4) * 4);
-        }
+        if (lp[i] < c1 && !page_base(lp[i], kbase[i], vbase[i])) lp[i] = c1;  // skip
+        if (lp[i] < c1 && lp[i] != last) load_page(kr[i], vr[i], kbase[i], vbase[i]);
       }
     } else {
       bool ok = true;
@@ -992,19 +988,10 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     if (!read_ok(c)) return false;
     if (c.ctl) ctl_claim_put(c, MI_NEXT + ((j + 1) & 1), nxt);
     if (!c.ctl) {
+      // the page holding the new token is read after the wait (the acquire made it visible)
 #pragma unroll
-      for (int i = 0; i < MAXP; ++i) {
-        if (lp[i] < c1 && lp[i] == last) {
-#pragma unroll
-          for (int kk = 0; kk < NK; ++kk)
-            kr[i][kk] = *reinterpret_cast<const GAS u32x4*>(p.kv_pool + kbase[i] + (c.lane & 15) * HD + kk * 32 +
-                                                            (c.lane >> 4) * 8);
-#pragma unroll
-          for (int dt = 0; dt < NV; ++dt)
-            vr[i][dt] = *reinterpret_cast<const GAS u32x2*>(p.kv_pool + vbase[i] + (dt * 16 + (c.lane & 15)) * 16 +
-                                                            (c.lane >> 4) * 4);
-        }
-      }
+      for (int i = 0; i < MAXP; ++i)
+        if (lp[i] < c1 && lp[i] == last) load_page(kr[i], vr[i], kbase[i], vbase[i]);
       // Q^T operand: lane holds head (lane & 15), dims kk*32 + (lane>>4)*8 + [0, 8)
       const int hq = c.lane & 15;
       const float qscale = 1.4426950408889634f / sqrtf((float)HD);
@@ -1025,18 +1012,16 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
       f32x4 o[NV];
 #pragma unroll
       for (int dt = 0; dt < NV; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < MAXP; ++i) {
-        if (lp[i] >= c1) continue;
+      auto do_page = [&](const u32x4 (&kq)[NK], const u32x2 (&vq)[NV], int lpg) {
         f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[i][kk]),
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kq[kk]),
                                                       __builtin_bit_cast(bf16x8, qb[kk]), s, 0, 0, 0);
-        if (lp[i] == last) {
+        if (lpg == last) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (lp[i] * p.page + (c.lane >> 4) * 4 + r > pos) s[r] = -INFINITY;
+            if (lpg * p.page + (c.lane >> 4) * 4 + r > pos) s[r] = -INFINITY;
         }
         float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
@@ -1056,8 +1041,18 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
 #pragma unroll
         for (int dt = 0; dt < NV; ++dt) {
           o[dt] *= alpha;
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vr[i][dt]), pb, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vq[dt]), pb, o[dt], 0, 0, 0);
         }
+      };
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i)
+        if (lp[i] < c1) do_page(kr[i], vr[i], lp[i]);
+      // further pages of this worker stream through the first page's registers
+      for (int lpg = c0 + c.wi + nw * MAXP; lpg < c1; lpg += nw) {
+        int64_t kb = 0, vb = 0;
+        if (!page_base(lpg, kb, vb)) continue;
+        load_page(kr[0], vr[0], kb, vb);
+        do_page(kr[0], vr[0], lpg);
       }
       if (c.lane < 16) {
         mw[c.wi * 16 + c.lane] = m;

@@ -87,8 +87,8 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   const int n_teams = plan_teams(o, batch);
   if (n_teams == 2 && batch > 4) return "two teams hold at most 4 sequences";
   if (g.n_experts > 256) return "at most 256 experts";
-  if (o.pages_per_item < 1 || o.pages_per_item > 7 * MKD_MAXP) return "pages_per_item exceeds 7 workers' pages";
-  if (o.pages_per_item_2 < 1 || o.pages_per_item_2 > 3 * MKD_MAXP) return "pages_per_item_2 exceeds 3 workers' pages";
+  if (o.pages_per_item < 1 || o.pages_per_item > 64) return "pages_per_item must be in [1, 64]";
+  if (o.pages_per_item_2 < 1 || o.pages_per_item_2 > 64) return "pages_per_item_2 must be in [1, 64]";
   if (o.n_ds < 1 || o.n_ds > 16) return "n_ds must be in [1, 16]";
   // a GEMV tile holds at most 5 row steps per worker wave (7 workers, >= 1 row per step)
   if (o.rt_rows > 35 || 2 * o.up_rows > 35 || 2 * o.qkv_max_pairs > 35 || o.router_rows > 35 || o.lm_rows > 35)
@@ -143,15 +143,15 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
           break;
         case W_ATTN:
           for (int i = 0; i < n_attn; ++i)
-            em.emit(OP_ATTN, l, i, 0, 0, 0, L(l, c.qkv_done), n_qkv_tiles, -1);
+            em.emit(OP_ATTN, l, i, n_attn, 0, 0, L(l, c.qkv_done), n_qkv_tiles, -1);
           break;
         case W_MOE_UP:
           for (int i = 0; i < n_up; ++i)
-            em.emit(OP_MOE_UP, l, i, 0, 0, 0, L(l, c.router_done), n_router_tiles, -1);
+            em.emit(OP_MOE_UP, l, i, n_up, 0, 0, L(l, c.router_done), n_router_tiles, -1);
           break;
         case W_MOE_DOWN:
           for (int i = 0; i < n_down; ++i)
-            em.emit(OP_MOE_DOWN, l, i, 0, 0, 0, L(l, c.router_done), n_router_tiles, -1);
+            em.emit(OP_MOE_DOWN, l, i, n_down, 0, 0, L(l, c.router_done), n_router_tiles, -1);
           break;
         case W_OPROJ:
           for (int rt = 0; rt < s.n_rt; ++rt)

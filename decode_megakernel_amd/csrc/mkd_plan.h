@@ -34,8 +34,8 @@ struct PlanOptions {
   int32_t rt_rows = 32;        // residual rows per O-proj / MoE-down tile
   int32_t n_ds = 8;            // MoE-down expert splits per row tile
   int32_t up_rows = 8;         // activation rows per MoE-up item (weights: 2x rows)
-  int32_t pages_per_item = 7 * MKD_MAXP;  // attention pages per claimed item, one team of 7 workers
-  int32_t pages_per_item_2 = 3 * MKD_MAXP;  // the same with two teams of 3 workers each
+  int32_t pages_per_item = 14;  // attention pages per claimed item, one team of 7 workers
+  int32_t pages_per_item_2 = 6;  // the same with two teams of 3 workers each
   int32_t teams = MKD_TEAMS;    // teams per workgroup: 1, 2, or 0 = 2 when batch <= two_team_max_batch
   int32_t two_team_max_batch = 4;
   int32_t qkv_max_pairs = 17;  // RoPE pairs per QKV tile at most (tile = 2x rows); a head is
