@@ -78,16 +78,72 @@ __device__ __forceinline__ float dot8(const u32x4 w, const f32x4 a, const f32x4 
 }
 
 // ------------------------------------------------------------------ wave reductions
-template <int WIDTH>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = WIDTH / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+// Cross-lane sums and maxima with DPP row rotations (every lane of a 16-lane row ends with
+// the row's result after four rotate-and-combine steps) and readlane for combining rows:
+// no LDS round trip per step, unlike a shuffle through ds_bpermute.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+// DPP row_ror:n = 0x120 + n
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0x128>(v);
+  v += dpp_f<0x124>(v);
+  v += dpp_f<0x122>(v);
+  v += dpp_f<0x121>(v);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0x128>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x122>(v));
+  v = fmaxf(v, dpp_f<0x121>(v));
   return v;
+}
+__device__ __forceinline__ int row16_min(int v) {
+  v = min(v, dpp_i<0x128>(v));
+  v = min(v, dpp_i<0x124>(v));
+  v = min(v, dpp_i<0x122>(v));
+  v = min(v, dpp_i<0x121>(v));
+  return v;
+}
+__device__ __forceinline__ float lane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// Sum over aligned groups of WIDTH lanes, returned to every lane of the group.
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (WIDTH == 64) {
+    const float r = row16_sum(v);
+    return (lane_f(r, 0) + lane_f(r, 16)) + (lane_f(r, 32) + lane_f(r, 48));
+  } else if constexpr (WIDTH == 32) {
+    const float r = row16_sum(v);
+    const float lo = lane_f(r, 0) + lane_f(r, 16), hi = lane_f(r, 32) + lane_f(r, 48);
+    return (threadIdx.x & 32) ? hi : lo;
+  } else if constexpr (WIDTH == 16) {
+    return row16_sum(v);
+  } else {
+#pragma unroll
+    for (int off = WIDTH / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+  }
+}
+__device__ __forceinline__ float wave_max(float v) {
+  const float r = row16_max(v);
+  return fmaxf(fmaxf(lane_f(r, 0), lane_f(r, 16)), fmaxf(lane_f(r, 32), lane_f(r, 48)));
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  const int r = row16_min(v);
+  return min(min(__builtin_amdgcn_readlane(r, 0), __builtin_amdgcn_readlane(r, 16)),
+             min(__builtin_amdgcn_readlane(r, 32), __builtin_amdgcn_readlane(r, 48)));
+}
+// Number of lanes below this one whose bit is set in `mask`.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 // ------------------------------------------------------------------ counters

@@ -97,7 +97,6 @@ constexpr int MI_NEXT = 10;      // [2] claimed item indices (ping-pong)
 constexpr int MI_OLD = 12;       // previous counter value of the last arrive
 constexpr int MI_T_STAGED = 14;  // trace: low 32 bits of the clock when inputs were staged
 constexpr int MI_T_DONE = 15;    // trace: low 32 bits of the clock when the workers finished
-constexpr int MI_SCAN = 24;      // [8] block-scan scratch
 constexpr int MI_TOK = 32;       // [16] token list of the current GEMV
 
 // Routing table offsets inside Smem::route (int32 units; at most B*k <= 256 entries
@@ -614,29 +613,6 @@ __device__ __forceinline__ bool op_oproj(Ctx& c) {
 }
 
 // ------------------------------------------------------------------ routing (all waves)
-// Exclusive prefix sum of one int per thread over the team; total receives the sum.
-__device__ __forceinline__ int team_exscan(const Ctx& c, int v, LAS int32_t* tmp, int& total) {
-  const int lane = c.lane, w = c.tw;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) tmp[w] = x;
-  bar(c);
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const int t = i <= c.nw ? tmp[i] : 0;
-    pre += i < w ? t : 0;
-    tot += t;
-  }
-  bar(c);
-  total = tot;
-  return pre + x - v;
-}
-
 // ROUTER_TOPK + ROUTE_FINALIZE + MOE_GATHER in LDS: top-k of each token's router logits
 // (descending, ties to the lower expert index), softmax over the selected logits, then
 // the active experts in ascending order and, per expert, its (token, slot) entries in
@@ -651,11 +627,14 @@ __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
   LAS int32_t* rt = c.s.route;
   LAS float* rw = reinterpret_cast<LAS float*>(rt + RT_W);
   const int lane = c.lane;
+  // top-k of token b by wave b mod (team waves): k rounds of a wave argmax, each a DPP
+  // maximum of the lanes' best remaining logits and a DPP minimum of the expert indices
+  // that reach it (ties go to the lower index)
   for (int b = c.tw; b < B; b += c.nw + 1) {
     const GAS float* r = p.router + ((int64_t)l * p.max_batch + b) * E;
-    float v[8];
+    float v[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
       v[i] = e < E ? r[e] : -INFINITY;
     }
@@ -663,22 +642,18 @@ __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
         if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
       }
+      const float M = wave_max(bv);
+      const int BI = wave_min_i(bv == M ? bi : 0x7FFFFFFF);
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (lane + 64 * i == bi) v[i] = -INFINITY;
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i == BI) v[i] = -INFINITY;
       if (lane == 0) {
-        rt[RT_IDS + b * 16 + j] = bi;
-        rw[b * 16 + j] = bv;  // logit for now
+        rt[RT_IDS + b * 16 + j] = BI;
+        rw[b * 16 + j] = M;  // logit for now
       }
     }
     if (lane == 0) {
@@ -693,27 +668,39 @@ __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
     }
   }
   bar(c);
-  // per-expert entry counts, one thread per expert, then block-wide exclusive scans give
-  // each active expert its rank and its offset in the flat (token, slot) list.
-  const int e = c.tid;  // E <= threads of a team
-  int m_e = 0;
-  if (e < E)
-    for (int b = 0; b < B; ++b)
-      for (int j = 0; j < k; ++j) m_e += rt[RT_IDS + b * 16 + j] == e;
-  int n_entries = 0, n_act = 0;
-  const int off = team_exscan(c, m_e, c.s.mi + MI_SCAN, n_entries);
-  const int rank = team_exscan(c, m_e > 0 ? 1 : 0, c.s.mi + MI_SCAN, n_act);
-  if (m_e > 0) {
-    rt[RT_ACT + rank] = e;
-    rt[RT_OFF + rank] = off;
-    int at = off;
-    for (int b = 0; b < B; ++b)
-      for (int j = 0; j < k; ++j)
-        if (rt[RT_IDS + b * 16 + j] == e) rt[RT_FLAT + at++] = b * k + j;
-  }
-  if (c.tid == 0) {
-    rt[RT_OFF + n_act] = n_entries;
-    rt[RT_NACT] = n_act;
+  // Active experts (ascending) with their CSR offsets into the flat (token, slot) list, by
+  // the first wave: lane = expert of a 64-expert block; ballots give each active expert
+  // its rank and the exclusive prefix of the entry counts (counts <= 16: five bit planes).
+  if (c.tw == 0) {
+    int n_act = 0, n_ent = 0;
+    for (int blk = 0; blk < E; blk += 64) {
+      const int e = blk + lane;
+      int m = 0;
+      for (int t = 0; t < B * k; ++t) m += rt[RT_IDS + (t / k) * 16 + t % k] == e ? 1 : 0;
+      if (e >= E) m = 0;
+      const uint64_t act = __ballot(m > 0);
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t plane = __ballot((m >> bit) & 1);
+        pre += lanes_below(plane) << bit;
+        tot += __builtin_popcountll(plane) << bit;
+      }
+      if (m > 0) {
+        const int rank = n_act + lanes_below(act);
+        int at = n_ent + pre;
+        rt[RT_ACT + rank] = e;
+        rt[RT_OFF + rank] = at;
+        for (int t = 0; t < B * k; ++t)
+          if (rt[RT_IDS + (t / k) * 16 + t % k] == e) rt[RT_FLAT + at++] = t;  // t = b * k + j
+      }
+      n_act += __builtin_popcountll(act);
+      n_ent += tot;
+    }
+    if (lane == 0) {
+      rt[RT_OFF + n_act] = n_ent;
+      rt[RT_NACT] = n_act;
+    }
   }
   if (write_debug && c.tid < B * k) {
     const int b = c.tid / k, j = c.tid % k;
