@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy
 METRIC = "decode tok/s + achieved HBM TB/s (% of SoL), 30B-A3B MoE bs1 @8K ctx"
 
 
@@ -242,7 +243,48 @@ def run(args):
                                                       "workgroup_busy_fraction_mean")}
     del W, pool
     torch.cuda.empty_cache()
+    if args.calibrate_copy:
+        # plain device-to-device copies of a known size, for scaling the HBM byte counters
+        # (FETCH_SIZE / WRITE_SIZE) that a profiler reads for the step kernel
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 2.0, out=dst)  # an elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        del src, dst
     return out, wl
+
+
+def read_counter_csv(path, counter):
+    """{kernel name: [value per dispatch]} of one counter from a rocprofv3 counter CSV."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def traffic_from_counters(fetch_csv, write_csv, kernel="mk_persistent"):
+    """HBM bytes per launch of the step kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
+    then WRITE_SIZE, KiB per dispatch), each scaled by the reading for the calibration
+    kernel (an elementwise multiply reading and writing COPY_BYTES):
+    bytes = counter * COPY_BYTES / counter(calibration)."""
+    import numpy as np
+    res = {}
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        vals = read_counter_csv(path, counter)
+        step = [v for k, vs in vals.items() if kernel in k for v in vs]
+        copy = [v for k, vs in vals.items() if "MulFunctor" in k for v in vs]
+        if not step or not copy:
+            raise SystemExit(f"{path}: no {kernel} or calibration copy dispatches for {counter}")
+        scale = COPY_BYTES / float(np.median(copy))
+        res[name] = {"counter_kib_median": float(np.median(step)), "copy_kib_median": float(np.median(copy)),
+                     "bytes_per_count": scale, "bytes": float(np.median(step)) * scale}
+    res["traffic_bytes_per_launch"] = res["fetch"]["bytes"] + res["write"]["bytes"]
+    return res
 
 
 def main():
@@ -258,7 +300,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace", default="", help="write a per-task trace summary (JSON) here")
     ap.add_argument("--chrome", action="store_true", help="with --trace: also write the Chrome trace")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the run, multiply 1 GiB into another 1 GiB buffer three times "
+                         "(calibration of the HBM byte counters)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="reduce two rocprofv3 counter CSVs to HBM bytes per step launch and write "
+                         "profiles/mk_persistent_full_b1_ctx8k_traffic.json (no GPU run)")
     args = ap.parse_args()
+    if args.traffic:
+        res = traffic_from_counters(*args.traffic)
+        res["kernel_source"] = kernel_source_hash()
+        res["sources"] = list(args.traffic)
+        with open(os.path.join(ROOT, "profiles", "mk_persistent_full_b1_ctx8k_traffic.json"), "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design "
                                    "note, not an implemented path", "n_gpus": args.gpus}))

@@ -170,7 +170,12 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 // publishes such data by waiting for its own stores to complete and then adding to the
 // counter: no agent-scope release fence, whose L2 write-back of every dirty line costs
 // microseconds.  Consumers still acquire (invalidate) before reading with plain loads.
+// Outputs the host reads (logits, debug buffers) use them too, so that they are in memory
+// whatever release the end of the dispatch performs.
 __device__ __forceinline__ void st_pub(GAS float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_pub(GAS int32_t* p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_pub(GAS uint16_t* p, uint16_t v) {

@@ -407,9 +407,10 @@ int mkd_debug_read(mkd_engine* e, int32_t what, void* dst, size_t bytes) {
   if (bytes < (size_t)(outer * B * inner)) return fail(e, MKD_ERR_ARG, "debug buffer too small");
   hipError_t rc = hipSetDevice(e->device);
   if (rc == hipSuccess) rc = hipStreamSynchronize(e->last_stream);
-  if (rc == hipSuccess)
-    rc = hipMemcpy2D(dst, (size_t)(B * inner), src, (size_t)(mb * inner), (size_t)(B * inner), (size_t)outer,
-                     hipMemcpyDeviceToHost);
+  // one copy per layer row (a strided 2-D copy was seen to leave the destination
+  // untouched under a profiler's interception)
+  for (int64_t o = 0; o < outer && rc == hipSuccess; ++o)
+    rc = hipMemcpy((char*)dst + o * B * inner, src + o * mb * inner, (size_t)(B * inner), hipMemcpyDeviceToHost);
   if (rc != hipSuccess) return hip_fail(e, rc, "debug read");
   return MKD_OK;
 }

@@ -579,7 +579,7 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
     for (int i = c.lane; i < R * B; i += 64) {
       const int r = i / B, b = i % B;
       const float v = c.s.rowsum[i] * c.s.mf[b];
-      if (lm_head) p.logits[(int64_t)b * p.vocab + r0 + r] = v;
+      if (lm_head) st_pub(p.logits + (int64_t)b * p.vocab + r0 + r, v);
       else st_pub(p.router + ((int64_t)l * p.max_batch + b) * p.n_experts + r0 + r, v);
     }
     if (c.d[D_SIGNAL] >= 0) ctl_signal(c, p.counters + c.d[D_SIGNAL]);
@@ -704,8 +704,8 @@ __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
   }
   if (write_debug && c.tid < B * k) {
     const int b = c.tid / k, j = c.tid % k;
-    p.topk_ids[((int64_t)l * p.max_batch + b) * k + j] = rt[RT_IDS + b * 16 + j];
-    p.topk_w[((int64_t)l * p.max_batch + b) * k + j] = rw[b * 16 + j];
+    st_pub(p.topk_ids + ((int64_t)l * p.max_batch + b) * k + j, rt[RT_IDS + b * 16 + j]);
+    st_pub(p.topk_w + ((int64_t)l * p.max_batch + b) * k + j, rw[b * 16 + j]);
   }
   bar(c);
   if (c.tid == 0) c.s.mi[MI_ROUTE_LAYER] = l;
