@@ -16,16 +16,16 @@ namespace mkd {
 //   QKV_PROJ            -> OP_QKV (RoPE and the paged-KV append in the epilogue)
 //   ROUTER_GEMM         -> OP_ROUTER
 //   ROUTER_TOPK, ROUTE_FINALIZE, MOE_GATHER
-//                       -> computed redundantly at the start of OP_MOE_UP and
-//                          OP_MOE_DOWN claimers (no extra counter hop)
+//                       -> computed in LDS at the start of the OP_MOE_UP claimer of each
+//                          CU and reused by its OP_OUT task (no extra counter hop)
 //   ATTN_DRAIN + ATTN_DECODE -> OP_ATTN (claims (seq, kv group, page chunk) items)
 //   ATTN_COMBINE        -> done by the last attention item of a (seq, kv group)
-//   MOE_UPGATE_ACT_DRAIN -> OP_MOE_UP, MOE_DOWN_DRAIN -> OP_MOE_DOWN
-//   MOE_COMBINE         -> weighted sums folded into OP_MOE_DOWN partials
-//   O_PROJ              -> OP_OPROJ (split-K over KV groups)
-//   fused residual add + RMSNorm -> finalisation by the last arriver of a residual
-//                          row tile (O-proj splits + MoE-down splits), consumers
-//                          apply the norm on the fly
+//   MOE_UPGATE_ACT_DRAIN -> OP_MOE_UP
+//   O_PROJ, MOE_DOWN_DRAIN, MOE_COMBINE and the fused residual add + RMSNorm
+//                       -> OP_OUT, one task per residual row tile: the tile's O-proj rows
+//                          over every KV group, its expert down rows over every active
+//                          expert weighted by the router scores, and h_{l+1} with the
+//                          tile's sum of squares (consumers apply the norm on the fly)
 //   LM_HEAD             -> OP_LM_HEAD; OP_EMBED seeds the residual stream.
 enum Opcode : int32_t {
   OP_NOP = 0,
@@ -34,10 +34,9 @@ enum Opcode : int32_t {
   OP_ROUTER = 3,
   OP_ATTN = 4,
   OP_MOE_UP = 5,
-  OP_MOE_DOWN = 6,
-  OP_OPROJ = 7,
-  OP_LM_HEAD = 8,
-  OP_COUNT = 9,
+  OP_OUT = 6,
+  OP_LM_HEAD = 7,
+  OP_COUNT = 8,
 };
 
 // ---------------------------------------------------------------- descriptor
@@ -66,11 +65,9 @@ struct CounterLayout {
   int32_t router_done; // router tiles done
   int32_t attn_claim;  // attention queue head
   int32_t up_claim;    // MoE up queue head
-  int32_t down_claim;  // MoE down queue head
   int32_t comb;        // [n_kv] combined (seq) count per kv group
   int32_t attn_items;  // [max_batch][n_kv] items finished per (seq, group)
   int32_t up_done;     // [n_experts] up tiles finished per expert
-  int32_t rt;          // [n_rt] arrivals per residual row tile
   int32_t global_base; // start of the step-global block (after n_layers+1 layer blocks)
   int32_t total;       // total counters
 };
@@ -91,7 +88,6 @@ enum GlobalCounter : int32_t {
 struct PlanShape {
   int32_t n_rt;            // residual row tiles (hidden / rt_rows)
   int32_t rt_rows;         // rows per residual row tile
-  int32_t n_ds;            // MoE-down expert splits per row tile
   int32_t up_rows;         // activation rows per MoE-up item (gate+up = 2x rows of weights)
   int32_t n_up_tiles;      // moe_inter / up_rows
   int32_t pages_per_item;  // attention pages per claimed item
@@ -129,12 +125,10 @@ struct Params {
   float* q;           // [L][maxB][nq*hd] post-RoPE queries
   float* attn_part;   // [max_items][hpg][hd + 2] unnormalised o, then m, l
   float* attn_o;      // [L][maxB][nq*hd]
-  float* a_part;      // [L][nkv][maxB][H] O-proj split outputs
   float* router;      // [L][maxB][E]
   int32_t* topk_ids;  // [L][maxB][k]
   float* topk_w;      // [L][maxB][k]
   float* moe_act;     // [L][maxB*k][I]
-  float* m_part;      // [L][n_ds][maxB][H]
   const double* inv_freq;  // [hd/2] RoPE frequencies base^(-2i/hd), fp64
   float* rope;             // [maxB][hd/2][2] cos, sin of this step's positions
   const void* dummy;       // 1 KB of zeros: target of the GEMV ring's idle slots

@@ -215,12 +215,10 @@ struct DParams {
   GAS float* q;
   GAS float* attn_part;
   GAS float* attn_o;
-  GAS float* a_part;
   GAS float* router;
   GAS int32_t* topk_ids;
   GAS float* topk_w;
   GAS float* moe_act;
-  GAS float* m_part;
   const CAS double* inv_freq;
   GAS float* rope;
   GAS uint32_t* counters;
@@ -251,22 +249,22 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.rms_eps = p.rms_eps;
   d.batch = p.batch; d.max_batch = p.max_batch; d.max_pages = p.max_pages; d.n_pages = p.n_pages;
   d.n_teams = p.n_teams;
-  d.shape.n_rt = p.shape.n_rt; d.shape.rt_rows = p.shape.rt_rows; d.shape.n_ds = p.shape.n_ds;
+  d.shape.n_rt = p.shape.n_rt; d.shape.rt_rows = p.shape.rt_rows;
   d.shape.up_rows = p.shape.up_rows; d.shape.n_up_tiles = p.shape.n_up_tiles;
   d.shape.pages_per_item = p.shape.pages_per_item; d.shape.qkv_rows = p.shape.qkv_rows;
   d.shape.router_rows = p.shape.router_rows; d.shape.lm_rows = p.shape.lm_rows;
   d.ctr.per_layer = p.ctr.per_layer; d.ctr.x_ready = p.ctr.x_ready; d.ctr.qkv_done = p.ctr.qkv_done;
   d.ctr.router_done = p.ctr.router_done; d.ctr.attn_claim = p.ctr.attn_claim; d.ctr.up_claim = p.ctr.up_claim;
-  d.ctr.down_claim = p.ctr.down_claim; d.ctr.comb = p.ctr.comb; d.ctr.attn_items = p.ctr.attn_items;
-  d.ctr.up_done = p.ctr.up_done; d.ctr.rt = p.ctr.rt; d.ctr.global_base = p.ctr.global_base;
+  d.ctr.comb = p.ctr.comb; d.ctr.attn_items = p.ctr.attn_items;
+  d.ctr.up_done = p.ctr.up_done; d.ctr.global_base = p.ctr.global_base;
   d.ctr.total = p.ctr.total;
   d.embed = gas(p.embed); d.norm = gas(p.norm); d.w_qkv = gas(p.w_qkv); d.w_o = gas(p.w_o);
   d.w_router = gas(p.w_router); d.w_gate_up = gas(p.w_gate_up); d.w_down = gas(p.w_down);
   d.tokens = cas(p.tokens); d.seq_lens = cas(p.seq_lens); d.page_table = cas(p.page_table);
   d.kv_pool = gas(p.kv_pool); d.logits = gas(p.logits);
   d.h = gas(p.h); d.ss = gas(p.ss); d.q = gas(p.q); d.attn_part = gas(p.attn_part); d.attn_o = gas(p.attn_o);
-  d.a_part = gas(p.a_part); d.router = gas(p.router); d.topk_ids = gas(p.topk_ids); d.topk_w = gas(p.topk_w);
-  d.moe_act = gas(p.moe_act); d.m_part = gas(p.m_part); d.inv_freq = cas(p.inv_freq);
+  d.router = gas(p.router); d.topk_ids = gas(p.topk_ids); d.topk_w = gas(p.topk_w);
+  d.moe_act = gas(p.moe_act); d.inv_freq = cas(p.inv_freq);
   d.rope = gas(p.rope);
   d.counters = gas(p.counters); d.tasks = cas(p.tasks); d.cu_offsets = cas(p.cu_offsets);
   d.max_attn_items = p.max_attn_items; d.spin_limit = p.spin_limit;

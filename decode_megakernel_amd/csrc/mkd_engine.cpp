@@ -25,7 +25,7 @@ namespace mkd {
 hipError_t launch_clear(uint32_t* counters, int32_t n, hipStream_t s);
 hipError_t launch_persistent(const Params& p, int n_wg, hipStream_t s);
 hipError_t launch_wave(const Params& p, int32_t first, int32_t count, hipStream_t s);
-int geometry_index(int hidden, int ko, int inter, int hd);
+int geometry_index(int hidden, int inter, int hd);
 }  // namespace mkd
 
 using namespace mkd;
@@ -95,9 +95,11 @@ std::string check_config(const mkd_config& c, int32_t max_batch, int32_t max_pag
     return "all dimensions must be positive";
   if (c.n_q_heads % c.n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
   if (c.n_q_heads / c.n_kv_heads > 16) return "at most 16 query heads per KV group";
-  if (geometry_index(c.hidden, c.n_q_heads * c.head_dim / c.n_kv_heads, c.moe_inter, c.head_dim) < 0)
-    return "(hidden, n_q_heads*head_dim/n_kv_heads, moe_inter, head_dim) must be (2048, 1024, 768, 128) or "
-           "(256, 256, 128, 64): the kernel is compiled for these geometries";
+  if (geometry_index(c.hidden, c.moe_inter, c.head_dim) < 0)
+    return "(hidden, moe_inter, head_dim) must be (2048, 768, 128) or (256, 128, 64): the kernel is compiled "
+           "for these geometries";
+  if ((c.n_q_heads * c.head_dim) % c.hidden || (c.n_q_heads * c.head_dim) / c.hidden > 4)
+    return "n_q_heads * head_dim must be 1, 2 or 4 times hidden";
   if (c.n_experts > 256) return "at most 256 experts";
   if (c.top_k > 16 || c.top_k > c.n_experts) return "top_k must be <= 16 and <= n_experts";
   if (c.page_size != 16) return "page_size must be 16";
@@ -134,7 +136,6 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
                      cfg->n_experts, cfg->top_k, cfg->moe_inter, cfg->vocab, cfg->page_size};
   e->max_batch = max_batch;
   e->max_pages = max_pages_per_seq;
-  if (cfg->hidden <= 256) e->opts.rt_rows = 32;
   e->shape = make_shape(e->geom, e->opts, 1);
   e->ctr = make_counters(e->geom, e->shape, max_batch);
   {
@@ -173,12 +174,10 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
       {sizeof(float) * L * B * QD, (void**)&p.q},
       {sizeof(float) * (size_t)e->max_attn_items * hpg * (cfg->head_dim + 2), (void**)&p.attn_part},
       {sizeof(float) * L * B * QD, (void**)&p.attn_o},
-      {sizeof(float) * L * cfg->n_kv_heads * B * H, (void**)&p.a_part},
       {sizeof(float) * L * B * E, (void**)&p.router},
       {sizeof(int32_t) * L * B * K, (void**)&p.topk_ids},
       {sizeof(float) * L * B * K, (void**)&p.topk_w},
       {sizeof(float) * L * B * K * cfg->moe_inter, (void**)&p.moe_act},
-      {sizeof(float) * L * e->shape.n_ds * B * H, (void**)&p.m_part},
       {sizeof(double) * cfg->head_dim / 2, (void**)&p.inv_freq},
       {sizeof(float) * B * cfg->head_dim, (void**)&p.rope},
       {1024, (void**)&p.dummy},

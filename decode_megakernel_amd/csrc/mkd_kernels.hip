@@ -179,6 +179,37 @@ __device__ __forceinline__ bool ctl_wait(Ctx& c, GAS uint32_t* ctr, uint32_t tar
   return __shfl(ok, 0, 64) != 0;
 }
 
+// Spin until counters[lane] >= target for every lane < n (one poll of all n counters per
+// round), then acquire.  Returns false when the step is aborted.  Controller wave only.
+__device__ __forceinline__ bool ctl_wait_lanes(Ctx& c, GAS uint32_t* ctr, int n, uint32_t target) {
+  const DParams p = device_view(*c.kp);
+  bool ok = true;
+  int32_t spins = 0;
+  while (true) {
+    const uint32_t v = c.lane < n ? ctr_load(ctr) : target;
+    const uint64_t pending = __ballot(v < target);
+    if (pending == 0) break;
+    if ((spins & 63) == 63 && aborted(p)) {
+      ok = false;
+      break;
+    }
+    if (++spins > p.spin_limit) {
+      const int first = __builtin_ctzll(pending);
+      if (c.lane == first) report_error(p, 1u, c.task, (int32_t)(ctr - p.counters), v, target);
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  fence_acquire_agent();
+  if (ok && c.lane == 0 && c.s.mi[MI_READY_LO] == 0 && c.s.mi[MI_READY_HI] == 0) {
+    const uint64_t t = wall_clock64();
+    c.s.mi[MI_READY_LO] = (int32_t)(uint32_t)t;
+    c.s.mi[MI_READY_HI] = (int32_t)(uint32_t)(t >> 32);
+  }
+  return ok;
+}
+
 // Publish the controller's stores (written through with st_pub: waiting for their
 // completion suffices) and add one to the counter; returns the old value.
 __device__ __forceinline__ uint32_t ctl_arrive(Ctx& c, GAS uint32_t* ctr) {
@@ -224,20 +255,34 @@ __device__ __forceinline__ int32_t read_mi(Ctx& c, int slot) { return __builtin_
 __device__ __forceinline__ bool read_ok(Ctx& c) { return read_mi(c, MI_OK) != 0; }
 
 // ------------------------------------------------------------------ GEMV tile (workers)
-// Weight rows of a tile come from up to two row segments (gate|up, or the two
-// halves of a RoPE head) with a common leading dimension.
+// Weight rows of a tile: up to four segments of n1 rows each (the last may be shorter)
+// with a common leading dimension, at element offsets seg0..seg3 from a wave-uniform
+// base (32 bits: a tile's rows lie within a few hundred MB of its base).  With separate
+// activation blocks (the output tasks: O-proj column blocks, or different experts, in the
+// segments; n1 = 2^xsh), the rows of segment s multiply xs + s * xstep + tok[j] * xld;
+// otherwise every row multiplies xs + tok[j] * xld (xld = 0: the row length).  Two
+// segments hold the two halves of RoPE pairs or gate|up rows.
 struct RowSrc {
-  const GAS uint16_t* base;  // first row of the first segment (wave-uniform)
-  uint32_t seg2;             // element offset of the second segment's first row
-  uint32_t ld;               // leading dimension (elements)
-  int32_t n1;                // rows in the first segment
-  // element offset of row i from base (32 bits: a tile spans a few MB at most)
+  const GAS uint16_t* base;
+  uint32_t seg0, seg1, seg2, seg3;
+  uint32_t ld;
+  int32_t n1;
+  int32_t xld;
+  int32_t xstep, xsh;
+  // segments from a table (expert ids in LDS): segment s starts at eids[s] * escale + seg0
+  const LAS int32_t* eids;
+  uint32_t escale;
   __device__ uint32_t row_off(int i) const {
-    return i < n1 ? (uint32_t)i * ld : seg2 + (uint32_t)(i - n1) * ld;
+    if (eids) return (uint32_t)eids[i >> xsh] * escale + seg0 + (uint32_t)(i & (n1 - 1)) * ld;
+    if (i < n1) return seg0 + (uint32_t)i * ld;
+    if (i < 2 * n1) return seg1 + (uint32_t)(i - n1) * ld;
+    if (i < 3 * n1) return seg2 + (uint32_t)(i - 2 * n1) * ld;
+    return seg3 + (uint32_t)(i - 3 * n1) * ld;
   }
+  __device__ int32_t x_off(int i) const { return (i >> xsh) * xstep; }
 };
 __device__ __forceinline__ RowSrc row_src(const GAS uint16_t* b1, const GAS uint16_t* b2, int64_t ld, int n1) {
-  return RowSrc{b1, (uint32_t)(b2 - b1), (uint32_t)ld, n1};
+  return RowSrc{b1, 0u, (uint32_t)(b2 - b1), 0u, 0u, (uint32_t)ld, n1, 0, 0, 0, nullptr, 0u};
 }
 
 // Lane mapping of a K-long bf16 row onto a worker wave: LPR lanes per row, CPL
@@ -274,8 +319,8 @@ __device__ __forceinline__ uint32_t gemv_chunk_off(const Ctx& c, const RowSrc& s
 // load per round (slots past F load a small dummy line that stays in the cache; the
 // addresses are a wave-uniform base plus a 32-bit lane offset), so the loop body is
 // straight-line and the wait-counter pass keeps kRing loads in flight.
-// rowsum[row * nb + j] = W[row] . x_j, x_j = xs + tok[j] * K, rows < R.  NB bounds nb.
-template <int K, int NB>
+// rowsum[row * nb + j] = W[row] . x_j, x_j = xs + xo(row) + tok[j] * xld, rows < R.  NB bounds nb.
+template <int K, int NB, bool XSEG>
 __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R, const LAS float* xs,
                                           const LAS int32_t* tok, int nb, LAS float* rowsum) {
   using G = Gemv<K>;
@@ -292,8 +337,9 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = 0.0f;
   int toff[NB];  // token row offsets into xs (wave-uniform)
+  const int xld = src.xld ? src.xld : K;
 #pragma unroll
-  for (int j = 0; j < NB; ++j) toff[j] = (NB == 1 || j < nb) ? __builtin_amdgcn_readfirstlane(tok[j]) * K : 0;
+  for (int j = 0; j < NB; ++j) toff[j] = (NB == 1 || j < nb) ? __builtin_amdgcn_readfirstlane(tok[j]) * xld : 0;
   for (int base = 0; base < F; base += kRing) {
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
@@ -304,10 +350,11 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
       if (f < F) {
         const int cc = f % G::CPL;
         const int kc = c.lane % G::LPR + G::LPR * cc;
+        const int xrow = XSEG ? src.x_off((c.wi + c.nw * (f / G::CPL)) * G::RPS + c.lane / G::LPR) : 0;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           if (NB == 1 || j < nb) {
-            const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(xs + toff[j] + kc * 8);
+            const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(xs + xrow + toff[j] + kc * 8);
             acc[j] += dot8(w, xp[0], xp[1]);
           }
           // bound the activations in flight to 4 tokens (32 registers)
@@ -331,11 +378,12 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
   return true;
 }
 
-template <int K>
+// XSEG: the segments of the tile read different activation blocks (output tasks).
+template <int K, bool XSEG = false>
 __device__ __forceinline__ bool worker_gemv(const Ctx& c, const RowSrc& src, int R, const LAS float* xs,
                                             const LAS int32_t* tok, int nb, LAS float* rowsum) {
-  if (nb == 1) return gemv_tile<K, 1>(c, src, R, xs, tok, nb, rowsum);
-  return gemv_tile<K, kMaxBatch>(c, src, R, xs, tok, nb, rowsum);
+  if (nb == 1) return gemv_tile<K, 1, XSEG>(c, src, R, xs, tok, nb, rowsum);
+  return gemv_tile<K, kMaxBatch, XSEG>(c, src, R, xs, tok, nb, rowsum);
 }
 
 // Controller side of the same two barriers.  A pending claim reply (next_slot >= 0) is
@@ -361,11 +409,23 @@ __device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_slot
 __device__ __forceinline__ void ctl_stage_x_normed(Ctx& c, int l) {
   if (read_mi(c, MI_XS_LAYER) == l) return;
   const DParams p = device_view(*c.kp);
-  const int B = p.batch, H = p.hidden, NRT = p.shape.n_rt;  // NRT <= 64
+  const int B = p.batch, H = p.hidden, NRT = p.shape.n_rt;  // NRT <= 256
+  // per token, its NRT partial sums: lane r < NRT holds tile r (four per lane); the load
+  // addresses are clamped into the token's row so the loads need no branch
   float part[16];
 #pragma unroll
-  for (int b = 0; b < 16; ++b)
-    part[b] = (b < B && c.lane < NRT) ? p.ss[((int64_t)l * p.max_batch + b) * NRT + c.lane] : 0.0f;
+  for (int b = 0; b < 16; ++b) {
+    float t = 0.0f;
+    if (b < B) {
+      const GAS float* row = p.ss + ((int64_t)l * p.max_batch + b) * NRT;
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = row[min(c.lane + 64 * q, NRT - 1)];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) t += c.lane + 64 * q < NRT ? v[q] : 0.0f;
+    }
+    part[b] = t;
+  }
   const GAS uint16_t* gamma = p.norm + (int64_t)l * H;
   const int n8 = B * (H / 8);
 #pragma unroll 4
@@ -393,68 +453,6 @@ __device__ __forceinline__ void ctl_stage_x_normed(Ctx& c, int l) {
   }
   if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
   if (c.lane == 0) c.s.mi[MI_XS_LAYER] = l;
-}
-
-// Stage nb rows of K floats from global memory (row stride `stride`) into xs.
-template <int K>
-__device__ __forceinline__ void ctl_stage_rows(Ctx& c, const GAS float* src, int64_t stride, int nb) {
-  for (int i = c.lane; i < nb * (K / 4); i += 64) {
-    const int b = i / (K / 4), k4 = (i % (K / 4)) * 4;
-    *reinterpret_cast<LAS f32x4*>(c.s.xs + b * K + k4) = *reinterpret_cast<const GAS f32x4*>(src + b * stride + k4);
-  }
-  if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
-  if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
-}
-
-// ------------------------------------------------------------------ residual finalisation (controller)
-// The fused residual add + RMSNorm at the end of a layer ("Where the speedup comes
-// from": parallel layers are rejoined only by it).  The last arriver of residual row
-// tile rt writes h_{l+1} = h_l + sum_g a_g + sum_ds m_ds for those rows and their sum of
-// squares; consumers of layer l+1 normalise on the fly.
-__device__ __forceinline__ void ctl_finalize_rows(Ctx& c, int l, int rt) {
-  const DParams p = device_view(*c.kp);
-  fence_acquire_agent();
-  const int R = p.shape.rt_rows, H = p.hidden, B = p.batch;
-  const int r0 = rt * R;
-  const int64_t hstride = (int64_t)p.max_batch * H;
-  LAS float* red = c.s.rowsum;  // [B][R] squares (the tile's row sums are consumed)
-  for (int i = c.lane; i < B * R; i += 64) {
-    const int b = i / R, r = r0 + i % R;
-    const int64_t hb = (int64_t)b * H + r;
-    float v = p.h[(int64_t)l * hstride + hb];
-    for (int g0 = 0; g0 < p.n_kv; g0 += 4) {
-      float t[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        t[j] = g0 + j < p.n_kv ? p.a_part[((int64_t)l * p.n_kv + g0 + j) * hstride + hb] : 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v += t[j];
-    }
-    for (int d0 = 0; d0 < p.shape.n_ds; d0 += 8) {
-      float t[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        t[j] = d0 + j < p.shape.n_ds ? p.m_part[((int64_t)l * p.shape.n_ds + d0 + j) * hstride + hb] : 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v += t[j];
-    }
-    st_pub(p.h + (int64_t)(l + 1) * hstride + hb, v);
-    red[i] = v * v;
-  }
-  for (int b = 0; b < B; ++b) {
-    float t = 0.0f;
-    for (int r = c.lane; r < R; r += 64) t += red[b * R + r];
-    t = group_sum<64>(t);
-    if (c.lane == 0) st_pub(p.ss + ((int64_t)(l + 1) * p.max_batch + b) * p.shape.n_rt + rt, t);
-  }
-  ctl_signal(c, layer_ctr(p, l + 1, p.ctr.x_ready));
-}
-
-// Arrive on a residual row tile; the last of its n_kv + n_ds producers finalises it.
-__device__ __forceinline__ void ctl_arrive_rt(Ctx& c, int l, int rt) {
-  const DParams p = device_view(*c.kp);
-  const uint32_t old = ctl_arrive(c, layer_ctr(p, l, p.ctr.rt + rt));
-  if (old + 1 == (uint32_t)(p.n_kv + p.shape.n_ds)) ctl_finalize_rows(c, l, rt);
 }
 
 // ------------------------------------------------------------------ OP_EMBED (controller)
@@ -587,31 +585,6 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
   return true;
 }
 
-// ------------------------------------------------------------------ OP_OPROJ
-// Split-K over KV groups (Figure 7: the O-proj of a KV group starts as soon as that
-// group's attention output lands): rows [rt*R, +R) of W_o, columns of group g.
-template <int K>
-__device__ __forceinline__ bool op_oproj(Ctx& c) {
-  const DParams p = device_view(*c.kp);
-  const int l = c.d[D_LAYER], rt = c.d[D_ARG0], g = c.d[D_ARG1];
-  const int R = p.shape.rt_rows, H = p.hidden, KO = p.n_q * p.head_dim, B = p.batch;
-  const GAS uint16_t* base = p.w_o + ((int64_t)l * H + (int64_t)rt * R) * KO + (int64_t)g * K;
-  const RowSrc src = row_src(base, base, KO, R);
-  if (!c.ctl) {
-    return worker_gemv<K>(c, src, R, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum);
-  } else {
-    const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
-    if (ok) ctl_stage_rows<K>(c, p.attn_o + (int64_t)l * p.max_batch * KO + (int64_t)g * K, KO, B);
-    if (!ctl_gemv_barriers(c, ok)) return false;
-    for (int i = c.lane; i < R * B; i += 64) {
-      const int r = i / B, b = i % B;
-      st_pub(p.a_part + (((int64_t)l * p.n_kv + g) * p.max_batch + b) * H + rt * R + r, c.s.rowsum[i]);
-    }
-    ctl_arrive_rt(c, l, rt);
-  }
-  return true;
-}
-
 // ------------------------------------------------------------------ routing (all waves)
 // ROUTER_TOPK + ROUTE_FINALIZE + MOE_GATHER in LDS: top-k of each token's router logits
 // (descending, ties to the lower expert index), softmax over the selected logits, then
@@ -707,8 +680,10 @@ __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
     st_pub(p.topk_ids + ((int64_t)l * p.max_batch + b) * k + j, rt[RT_IDS + b * 16 + j]);
     st_pub(p.topk_w + ((int64_t)l * p.max_batch + b) * k + j, rw[b * 16 + j]);
   }
-  bar(c);
+  // published before the barrier, so that every wave of the team sees the same value at
+  // the next check (a task may start right after this one without another barrier)
   if (c.tid == 0) c.s.mi[MI_ROUTE_LAYER] = l;
+  bar(c);
 }
 
 // ------------------------------------------------------------------ OP_MOE_UP (claimer)
@@ -762,77 +737,153 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   return true;
 }
 
-// ------------------------------------------------------------------ OP_MOE_DOWN (claimer)
-// Claims (residual row tile rt, expert split ds): for each active expert of the split
-// (every n_ds-th in ascending order) the workers stream W_down[e][rows of rt] while the
-// controller waits for that expert's up tiles and stages its activations; y_e is
-// weighted by the router scores into the split's partial m_ds[b][rows]; the last
-// producer of the row tile finalises the residual.
-template <int K>
-__device__ __forceinline__ bool op_moe_down(Ctx& c) {
+// ------------------------------------------------------------------ OP_OUT
+// Residual row tile rt, rows [r0, r0 + R) with R = rt_rows:
+//   a = W_o[rows] . attn_o        (all KV groups; the nq*hd columns are split into blocks of
+//                                  hidden length, the segments of one GEMV, summed in order)
+//   m = sum over active experts e (ascending) of w_{b,e} * W_down[e][rows] . act_{e,b}
+//   h_{l+1}[rows] = h_l[rows] + a + m, and the tile's sum of squares per token.
+// One task per row tile finishes the rows on its CU, so the O-proj and expert-down
+// partial outputs never leave the CU and no last-arriver step is needed (section
+// "Where the speedup comes from": the fused residual add + RMSNorm rejoins the two
+// branches; "Tasks": MOE_COMBINE weights the expert outputs by the router scores).
+// The O-proj part waits for the combined attention of every group, each expert group
+// for its experts' up tiles; each GEMV's weights stream before its wait.
+template <int KH, int KI>
+__device__ __forceinline__ bool op_out(Ctx& c) {
   const DParams p = device_view(*c.kp);
-  const int l = c.d[D_LAYER];
-  const int R = p.shape.rt_rows, NDS = p.shape.n_ds, H = p.hidden, I = p.inter, B = p.batch, k = p.top_k;
-  GAS uint32_t* head = layer_ctr(p, l, p.ctr.down_claim);
+  const int l = c.d[D_LAYER], rt = c.d[D_ARG0];
+  const int R = p.shape.rt_rows, r0 = rt * R, H = p.hidden, B = p.batch, k = p.top_k, E = p.n_experts;
+  const int QD = p.n_q * p.head_dim, NSO = QD / KH;  // O-proj column blocks (<= 4)
+  const int xs_floats = (c.nw == kWaves - 1 ? kXsBytes1 : kXsBytes2) / 4;
+  LAS float* acc_a = c.s.rowsum + kMaccOffset;  // [R][B] O-proj rows
+  LAS float* acc_m = acc_a + R * kMaxBatch;     // [R][B] expert rows
+  const int64_t hstride = (int64_t)p.max_batch * H;
+  // this tile's residual rows of layer l, loaded now and used at the end
+  float hold[2];
   if (c.ctl) {
-    const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
-    ctl_claim_put(c, MI_NEXT, (uint32_t)c.d[D_ARG0]);
-    if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
-    ctl_set_ok(c, ok);
-  }
-  bar(c);
-  if (!read_ok(c)) return false;
-  route_layer(c, l, false);
-  const LAS int32_t* rt = c.s.route;
-  const LAS float* rw = reinterpret_cast<const LAS float*>(rt + RT_W);
-  const int n_act = __builtin_amdgcn_readfirstlane(rt[RT_NACT]);
-  LAS float* macc = c.s.rowsum + kMaccOffset;  // [R][B], controller only
-  for (int j = 0;; ++j) {
-    const int idx = read_mi(c, MI_NEXT + (j & 1));
-    if (idx >= p.shape.n_rt * NDS) break;
-    const int rtile = idx / NDS, ds = idx % NDS;
-    uint32_t nxt = 0;
-    if (c.ctl) {
-      for (int i = c.lane; i < R * B; i += 64) macc[i] = 0.0f;
-      nxt = ctl_claim_issue(c, head);  // reply stored at the end of the item
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = c.lane + 64 * u;
+      hold[u] = i < R * B ? p.h[(int64_t)l * hstride + (int64_t)(i % B) * H + r0 + i / B] : 0.0f;
     }
-    for (int a = ds; a < n_act; a += NDS) {
-      const int e = __builtin_amdgcn_readfirstlane(rt[RT_ACT + a]);
-      const int o0 = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a]);
-      const int n_e = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a + 1]) - o0;
-      const GAS uint16_t* base = p.w_down + (((int64_t)l * p.n_experts + e) * H + (int64_t)rtile * R) * I;
-      const RowSrc src = row_src(base, base, I, R);
+    for (int i = c.lane; i < 2 * R * kMaxBatch; i += 64) acc_a[i] = 0.0f;
+  }
+  // routing tables of layer l (normally left in LDS by this CU's MoE-up claimer)
+  if (read_mi(c, MI_ROUTE_LAYER) != l) {
+    if (c.ctl) {
+      const int n_router_tiles = (E + p.shape.router_rows - 1) / p.shape.router_rows;
+      ctl_set_ok(c, ctl_wait(c, layer_ctr(p, l, p.ctr.router_done), (uint32_t)n_router_tiles));
+    }
+    bar(c);
+    if (!read_ok(c)) return false;
+    route_layer(c, l, false);
+  }
+  // (1) O-proj: NSO * R rows of length KH; token groups that fit in LDS
+  {
+    RowSrc so;
+    so.base = p.w_o + ((int64_t)l * H + r0) * QD;
+    so.seg0 = 0u; so.seg1 = (uint32_t)KH; so.seg2 = 2u * KH; so.seg3 = 3u * KH;
+    so.ld = (uint32_t)QD; so.n1 = R; so.xld = QD;
+    so.xstep = KH; so.xsh = 31 - __builtin_clz(R);
+    so.eids = nullptr; so.escale = 0u;
+    const int TG = min(kMaxBatch, xs_floats / QD);
+    for (int t0 = 0; t0 < B; t0 += TG) {
+      const int nb = min(TG, B - t0);
       if (!c.ctl) {
-        if (!worker_gemv<K>(c, src, R, c.s.xs, c.s.mi + MI_TOK, n_e, c.s.rowsum)) return false;
+        if (!worker_gemv<KH, true>(c, so, NSO * R, c.s.xs, c.s.mi + MI_TOK, nb, c.s.rowsum)) return false;
       } else {
-        const bool ok = ctl_wait(c, layer_ctr(p, l, p.ctr.up_done + e), (uint32_t)p.shape.n_up_tiles);
+        bool ok = true;
+        if (t0 == 0) ok = ctl_wait_lanes(c, layer_ctr(p, l, p.ctr.comb) + c.lane, p.n_kv, (uint32_t)B);
         if (ok) {
-          for (int i = c.lane; i < n_e * (K / 4); i += 64) {
-            const int jj = i / (K / 4), k4 = (i % (K / 4)) * 4;
-            const int slot = rt[RT_FLAT + o0 + jj];
-            *reinterpret_cast<LAS f32x4*>(c.s.xs + jj * K + k4) =
-                *reinterpret_cast<const GAS f32x4*>(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * I + k4);
-          }
+          const GAS float* src = p.attn_o + ((int64_t)l * p.max_batch + t0) * QD;
+          for (int i = c.lane; i < nb * (QD / 4); i += 64)
+            *reinterpret_cast<LAS f32x4*>(c.s.xs + i * 4) = *reinterpret_cast<const GAS f32x4*>(src + i * 4);
           if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
+          if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
         }
         if (!ctl_gemv_barriers(c, ok)) return false;
-        for (int i = c.lane; i < R * n_e; i += 64) {
-          const int r = i / n_e, jj = i % n_e;
-          const int slot = rt[RT_FLAT + o0 + jj];
-          const int b = slot / k, sj = slot % k;
-          macc[r * B + b] += rw[b * 16 + sj] * c.s.rowsum[r * n_e + jj];
+        for (int i = c.lane; i < R * nb; i += 64) {
+          const int r = i / nb, j = i % nb;
+          float a = 0.0f;
+          for (int sg = 0; sg < NSO; ++sg) a += c.s.rowsum[(sg * R + r) * nb + j];
+          acc_a[r * kMaxBatch + t0 + j] = a;
         }
       }
     }
-    if (c.ctl) {
-      for (int i = c.lane; i < R * B; i += 64) {
-        const int r = i / B, b = i % B;
-        st_pub(p.m_part + (((int64_t)l * NDS + ds) * p.max_batch + b) * H + (int64_t)rtile * R + r, macc[i]);
+  }
+  // (2) expert down rows: one GEMV per group of up to EPG active experts (all of them at
+  // small batch), segment s = expert a0 + s, rows addressed through the routing table
+  {
+    const LAS int32_t* rtab = c.s.route;
+    const LAS float* rw = reinterpret_cast<const LAS float*>(rtab + RT_W);
+    const int n_act = __builtin_amdgcn_readfirstlane(rtab[RT_NACT]);
+    const int EPG = max(1, min(xs_floats / (B * KI), (kMaxBatch * 40) / (R * B)));
+    for (int a0 = 0; a0 < n_act; a0 += EPG) {
+      const int na = min(EPG, n_act - a0);
+      int nb = 1;
+      for (int a = a0; a < a0 + na; ++a)
+        nb = max(nb, __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a + 1]) - __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a]));
+      RowSrc sd;
+      sd.base = p.w_down + (int64_t)l * E * H * KI;
+      sd.seg0 = (uint32_t)r0 * KI; sd.seg1 = sd.seg2 = sd.seg3 = 0u;
+      sd.ld = (uint32_t)KI; sd.n1 = R; sd.xld = KI;
+      sd.xstep = B * KI; sd.xsh = 31 - __builtin_clz(R);
+      sd.eids = rtab + RT_ACT + a0; sd.escale = (uint32_t)(H * KI);
+      if (!c.ctl) {
+        if (!worker_gemv<KI, true>(c, sd, na * R, c.s.xs, c.s.mi + MI_TOK, nb, c.s.rowsum)) return false;
+      } else {
+        GAS uint32_t* up = layer_ctr(p, l, p.ctr.up_done);
+        const int my_e = c.lane < na ? rtab[RT_ACT + a0 + c.lane] : 0;
+        const bool ok = ctl_wait_lanes(c, up + my_e, na, (uint32_t)p.shape.n_up_tiles);
+        if (ok) {
+          // activations: expert a0 + sg, token slot j at xs + sg*B*KI + j*KI
+          for (int sg = 0; sg < na; ++sg) {
+            const int ob = rtab[RT_OFF + a0 + sg], n_e = rtab[RT_OFF + a0 + sg + 1] - ob;
+            for (int i = c.lane; i < n_e * (KI / 4); i += 64) {
+              const int j = i / (KI / 4), k4 = (i % (KI / 4)) * 4;
+              const int slot = rtab[RT_FLAT + ob + j];
+              *reinterpret_cast<LAS f32x4*>(c.s.xs + sg * B * KI + j * KI + k4) =
+                  *reinterpret_cast<const GAS f32x4*>(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * KI + k4);
+            }
+          }
+          if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
+          if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
+        }
+        if (!ctl_gemv_barriers(c, ok)) return false;
+        // router-weighted sum, experts in ascending order (one expert per pass: a token
+        // appears once per expert, so no two lanes update the same element)
+        for (int sg = 0; sg < na; ++sg) {
+          const int ob = rtab[RT_OFF + a0 + sg], n_e = rtab[RT_OFF + a0 + sg + 1] - ob;
+          for (int i = c.lane; i < R * n_e; i += 64) {
+            const int r = i / n_e, j = i % n_e;
+            const int slot = rtab[RT_FLAT + ob + j];
+            const int b = slot / k, sj = slot % k;
+            acc_m[r * kMaxBatch + b] += rw[b * 16 + sj] * c.s.rowsum[(sg * R + r) * nb + j];
+          }
+        }
       }
-      ctl_claim_put(c, MI_NEXT + ((j + 1) & 1), nxt);
-      ctl_arrive_rt(c, l, rtile);
     }
-    bar(c);  // the next claimed index is published
+  }
+  // (3) h_{l+1}[rows] = h_l + a + m and the tile's sums of squares
+  if (c.ctl) {
+    LAS float* red = c.s.rowsum;  // [B][R] squares
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = c.lane + 64 * u;
+      if (i < R * B) {
+        const int r = i / B, b = i % B;
+        const float v = hold[u] + acc_a[r * kMaxBatch + b] + acc_m[r * kMaxBatch + b];
+        st_pub(p.h + (int64_t)(l + 1) * hstride + (int64_t)b * H + r0 + r, v);
+        red[b * R + r] = v * v;
+      }
+    }
+    if (c.lane < B) {
+      float t = 0.0f;
+      for (int r = 0; r < R; ++r) t += red[c.lane * R + r];
+      st_pub(p.ss + ((int64_t)(l + 1) * p.max_batch + c.lane) * p.shape.n_rt + rt, t);
+    }
+    ctl_signal(c, p.counters + c.d[D_SIGNAL]);
   }
   return true;
 }
@@ -1138,15 +1189,14 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
 // the head dimension), so that each kernel holds only its own tile bodies: fewer code
 // paths share the register allocation of the single persistent function.  Every opcode
 // body is inlined; its arguments are made wave-uniform (scalar registers) on entry.
-template <int HID, int KO_, int INTER, int HD_>
+template <int HID, int INTER, int HD_>
 struct Geom {
-  static constexpr int kHidden = HID;   // QKV / router / MoE-up / LM-head row length
-  static constexpr int kKo = KO_;       // O-proj split (one KV group's columns)
-  static constexpr int kInter = INTER;  // MoE-down row length
+  static constexpr int kHidden = HID;   // QKV / router / MoE-up / O-proj block / LM-head row length
+  static constexpr int kInter = INTER;  // expert down row length
   static constexpr int kHd = HD_;       // head dimension
 };
-using GeomFull = Geom<2048, 1024, 768, 128>;
-using GeomTiny = Geom<256, 256, 128, 64>;
+using GeomFull = Geom<2048, 768, 128>;
+using GeomTiny = Geom<256, 128, 64>;
 
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -1176,9 +1226,8 @@ MKD_EXEC(exec_embed, return op_embed(c);)
 MKD_EXEC(exec_qkv, return op_qkv<G::kHidden>(c);)
 MKD_EXEC(exec_router, return op_rows_on_x<G::kHidden>(c, false);)
 MKD_EXEC(exec_lm_head, return op_rows_on_x<G::kHidden>(c, true);)
-MKD_EXEC(exec_oproj, return op_oproj<G::kKo>(c);)
 MKD_EXEC(exec_moe_up, return op_moe_up<G::kHidden>(c);)
-MKD_EXEC(exec_moe_down, return op_moe_down<G::kInter>(c);)
+MKD_EXEC(exec_out, return (op_out<G::kHidden, G::kInter>(c));)
 MKD_EXEC(exec_attn, return op_attn<G::kHd>(c);)
 
 template <class G>
@@ -1188,9 +1237,8 @@ __device__ __forceinline__ bool run_task(KParams* kp, LAS char* lds, const CAS i
     case OP_QKV: return exec_qkv<G>(kp, lds, d, task, team);
     case OP_ROUTER: return exec_router<G>(kp, lds, d, task, team);
     case OP_LM_HEAD: return exec_lm_head<G>(kp, lds, d, task, team);
-    case OP_OPROJ: return exec_oproj<G>(kp, lds, d, task, team);
     case OP_MOE_UP: return exec_moe_up<G>(kp, lds, d, task, team);
-    case OP_MOE_DOWN: return exec_moe_down<G>(kp, lds, d, task, team);
+    case OP_OUT: return exec_out<G>(kp, lds, d, task, team);
     case OP_ATTN: return exec_attn<G>(kp, lds, d, task, team);
     default: return true;
   }
@@ -1302,15 +1350,15 @@ hipError_t launch_clear(uint32_t* counters, int32_t n, hipStream_t s) {
 }
 
 // Geometry instance of a configuration: 0 = full (hidden 2048), 1 = tiny (hidden 256), -1 = none.
-int geometry_index(int hidden, int ko, int inter, int hd) {
-  if (hidden == GeomFull::kHidden && ko == GeomFull::kKo && inter == GeomFull::kInter && hd == GeomFull::kHd) return 0;
-  if (hidden == GeomTiny::kHidden && ko == GeomTiny::kKo && inter == GeomTiny::kInter && hd == GeomTiny::kHd) return 1;
+int geometry_index(int hidden, int inter, int hd) {
+  if (hidden == GeomFull::kHidden && inter == GeomFull::kInter && hd == GeomFull::kHd) return 0;
+  if (hidden == GeomTiny::kHidden && inter == GeomTiny::kInter && hd == GeomTiny::kHd) return 1;
   return -1;
 }
 
 hipError_t launch_persistent(const Params& p, int n_wg, hipStream_t s) {
   void* args[] = {const_cast<Params*>(&p)};
-  const int gi = geometry_index(p.hidden, p.n_q * p.head_dim / p.n_kv, p.inter, p.head_dim);
+  const int gi = geometry_index(p.hidden, p.inter, p.head_dim);
   if (gi < 0) return hipErrorInvalidValue;
   const void* fn = gi == 0 ? reinterpret_cast<const void*>(&mk_persistent<GeomFull>)
                            : reinterpret_cast<const void*>(&mk_persistent<GeomTiny>);
@@ -1319,7 +1367,7 @@ hipError_t launch_persistent(const Params& p, int n_wg, hipStream_t s) {
 }
 
 hipError_t launch_wave(const Params& p, int32_t first, int32_t count, hipStream_t s) {
-  const int gi = geometry_index(p.hidden, p.n_q * p.head_dim / p.n_kv, p.inter, p.head_dim);
+  const int gi = geometry_index(p.hidden, p.inter, p.head_dim);
   if (gi == 0) hipLaunchKernelGGL(mk_wave<GeomFull>, dim3(count), dim3(kThreads / p.n_teams), 0, s, p, first);
   else if (gi == 1) hipLaunchKernelGGL(mk_wave<GeomTiny>, dim3(count), dim3(kThreads / p.n_teams), 0, s, p, first);
   else return hipErrorInvalidValue;

@@ -16,7 +16,6 @@ PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t n_teams) {
   PlanShape s{};
   s.rt_rows = o.rt_rows;
   s.n_rt = g.hidden / o.rt_rows;
-  s.n_ds = o.n_ds;
   s.up_rows = o.up_rows;
   s.n_up_tiles = g.inter / o.up_rows;
   s.pages_per_item = n_teams == 2 ? o.pages_per_item_2 : o.pages_per_item;
@@ -34,15 +33,12 @@ CounterLayout make_counters(const Geometry& g, const PlanShape& s, int32_t max_b
   c.router_done = at++;
   c.attn_claim = at++;
   c.up_claim = at++;
-  c.down_claim = at++;
   c.comb = at;
   at += g.n_kv;
   c.attn_items = at;
   at += max_batch * g.n_kv;
   c.up_done = at;
   at += g.n_experts;
-  c.rt = at;
-  at += s.n_rt;
   c.per_layer = (at + 15) / 16 * 16;
   c.global_base = c.per_layer * (g.n_layers + 1);
   c.total = c.global_base + G_COUNT;
@@ -81,7 +77,12 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   if (batch < 1 || batch > max_batch) return "batch out of range";
   if (n_cu < 1) return "n_cu must be positive";
   if (g.hidden % o.rt_rows) return "hidden must be a multiple of rt_rows";
-  if (g.hidden / o.rt_rows > 64) return "hidden / rt_rows must be at most 64";
+  if (o.rt_rows & (o.rt_rows - 1)) return "rt_rows must be a power of two";
+  if (g.hidden / o.rt_rows > 256) return "hidden / rt_rows must be at most 256";
+  if ((g.n_q * g.head_dim) % g.hidden || (g.n_q * g.head_dim) / g.hidden > 4)
+    return "n_q * head_dim must be 1, 2 or 4 times hidden";
+  if (o.rt_rows * ((g.n_q * g.head_dim) / g.hidden) > 35 || 4 * o.rt_rows > 35)
+    return "output tiles are limited to 35 GEMV rows";
   if (g.inter % o.up_rows) return "moe_inter must be a multiple of up_rows";
   if (o.qkv_max_pairs < 1) return "qkv_max_pairs must be positive";
   const int n_teams = plan_teams(o, batch);
@@ -89,7 +90,6 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   if (g.n_experts > 256) return "at most 256 experts";
   if (o.pages_per_item < 1 || o.pages_per_item > 64) return "pages_per_item must be in [1, 64]";
   if (o.pages_per_item_2 < 1 || o.pages_per_item_2 > 64) return "pages_per_item_2 must be in [1, 64]";
-  if (o.n_ds < 1 || o.n_ds > 16) return "n_ds must be in [1, 16]";
   // a GEMV tile holds at most 5 row steps per worker wave (7 workers, >= 1 row per step)
   if (o.rt_rows > 35 || 2 * o.up_rows > 35 || 2 * o.qkv_max_pairs > 35 || o.router_rows > 35 || o.lm_rows > 35)
     return "GEMV tiles are limited to 35 rows";
@@ -119,7 +119,6 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   const int n_router_tiles = (g.n_experts + o.router_rows - 1) / o.router_rows;
   const int n_attn = o.n_attn_claimers > 0 ? o.n_attn_claimers : n_cu;
   const int n_up = o.n_up_claimers > 0 ? o.n_up_claimers : n_cu;
-  const int n_down = o.n_down_claimers > 0 ? o.n_down_claimers : n_cu;
 
   begin_wave(-1, 0);
   for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_EMBED, 0, rt, 0, 0, 0, -1, 0, L(0, c.x_ready));
@@ -149,14 +148,10 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
           for (int i = 0; i < n_up; ++i)
             em.emit(OP_MOE_UP, l, i, n_up, 0, 0, L(l, c.router_done), n_router_tiles, -1);
           break;
-        case W_MOE_DOWN:
-          for (int i = 0; i < n_down; ++i)
-            em.emit(OP_MOE_DOWN, l, i, n_down, 0, 0, L(l, c.router_done), n_router_tiles, -1);
-          break;
-        case W_OPROJ:
-          for (int rt = 0; rt < s.n_rt; ++rt)
-            for (int gg = 0; gg < g.n_kv; ++gg)
-              em.emit(OP_OPROJ, l, rt, gg, 0, 0, L(l, c.comb + gg), batch, -1);
+        case W_OUT:
+          // waits inside the task: the combined attention of every KV group, then the up
+          // tiles of every active expert (dynamic: routing decides the experts)
+          for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_OUT, l, rt, 0, 0, 0, -1, 0, L(l + 1, c.x_ready));
           break;
         default:
           return "bad wave order";
@@ -187,7 +182,7 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
           ++rr_all;
           lists[cu * 2 + t].push_back(k);
         } else {
-          const int t = (w.kind == W_QKV || w.kind == W_ATTN || w.kind == W_OPROJ) ? 0 : 1;
+          const int t = (w.kind == W_QKV || w.kind == W_ATTN) ? 0 : 1;
           lists[(rr[t] % n_cu) * 2 + t].push_back(k);
           ++rr[t];
         }
@@ -216,9 +211,9 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
     if (d[D_GIDX] != k) return "task " + std::to_string(k) + ": global index mismatch";
     if (d[D_SIGNAL] >= 0) arrivals[d[D_SIGNAL]].push_back(k);
   }
-  // dynamic producers: residual row tiles are finalised by the last of their
-  // O-proj / MoE-down producers (x_ready of the next layer), attention combines
-  // arrive on comb; both come from waves of the same layer.
+  // static producers cover x_ready (embedding tasks for layer 0, output tasks of layer
+  // l-1 for layer l), qkv_done and router_done; attention combines arrive on comb from
+  // the attention claimers (dynamic: the last item of a (sequence, group)).
   for (int k = 0; k < n; ++k) {
     const int32_t* d = P.global.data() + (size_t)k * D_WORDS;
     const int op = d[D_OPCODE];
@@ -227,16 +222,7 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
     if (d[D_WAIT] >= c.global_base) return "task " + std::to_string(k) + ": wait on a status counter";
     const int layer = d[D_WAIT] / c.per_layer, off = d[D_WAIT] % c.per_layer;
     int64_t avail = 0;
-    if (off == c.x_ready && layer > 0) {
-      // finalised by layer-1's O-proj / MoE-down waves: they must all precede k
-      bool oproj = false, down = false;
-      for (const Wave& w : P.waves)
-        if (w.layer == layer - 1 && w.first + w.count <= k) {
-          oproj |= w.kind == W_OPROJ;
-          down |= w.kind == W_MOE_DOWN && w.count > 0;
-        }
-      avail = (oproj && down) ? P.shape.n_rt : 0;
-    } else if (off >= c.comb && off < c.comb + g.n_kv) {
+    if (off >= c.comb && off < c.comb + g.n_kv) {
       bool attn = false;
       for (const Wave& w : P.waves)
         if (w.layer == layer && w.kind == W_ATTN && w.count > 0 && w.first + w.count <= k) attn = true;
@@ -251,16 +237,18 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
              ") waits for " + std::to_string(d[D_TARGET]) + " arrivals on counter " + std::to_string(d[D_WAIT]) +
              " but only " + std::to_string(avail) + " producers precede it";
   }
-  // MoE-down claimers wait on up counters filled by MoE-up claimers: up before down.
+  // Output tasks wait inside the task on the combine counters (attention claimers) and
+  // the experts' up counters (MoE-up claimers): both waves precede the output wave.
   for (int l = 0; l < g.n_layers; ++l) {
-    int up_end = -1, down_first = -1;
+    int attn_end = -1, up_end = -1, out_first = -1;
     for (const Wave& w : P.waves)
       if (w.layer == l) {
+        if (w.kind == W_ATTN) attn_end = w.first + w.count;
         if (w.kind == W_MOE_UP) up_end = w.first + w.count;
-        if (w.kind == W_MOE_DOWN) down_first = w.first;
+        if (w.kind == W_OUT) out_first = w.first;
       }
-    if (up_end < 0 || down_first < 0 || down_first < up_end)
-      return "layer " + std::to_string(l) + ": MoE-down claimers must follow the MoE-up wave";
+    if (attn_end < 0 || up_end < 0 || out_first < 0 || out_first < attn_end || out_first < up_end)
+      return "layer " + std::to_string(l) + ": the output wave must follow the attention and MoE-up waves";
   }
   // every list in increasing global order, every task in exactly one list
   if ((int)P.cu_offsets.size() != P.n_cu * P.n_teams + 1) return "wrong number of task lists";

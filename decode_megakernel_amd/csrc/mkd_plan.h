@@ -28,11 +28,10 @@ struct Geometry {
 };
 
 // Wave kinds of one layer, in the order they can be arranged.
-enum WaveKind : int32_t { W_QKV = 0, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_OPROJ, W_KINDS };
+enum WaveKind : int32_t { W_QKV = 0, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT, W_KINDS };
 
 struct PlanOptions {
-  int32_t rt_rows = 32;        // residual rows per O-proj / MoE-down tile
-  int32_t n_ds = 8;            // MoE-down expert splits per row tile
+  int32_t rt_rows = 8;         // residual rows per output task (O-proj + expert down rows)
   int32_t up_rows = 8;         // activation rows per MoE-up item (weights: 2x rows)
   int32_t pages_per_item = 14;  // attention pages per claimed item, one team of 7 workers
   int32_t pages_per_item_2 = 6;  // the same with two teams of 3 workers each
@@ -45,11 +44,9 @@ struct PlanOptions {
   int32_t lm_rows = 32;
   int32_t n_attn_claimers = 0; // 0: automatic
   int32_t n_up_claimers = 0;
-  int32_t n_down_claimers = 0;
   // Order of the waves inside a layer: the pages' default order (qkv -> router ->
-  // attention -> MoE up/down -> O-proj), which measured fastest of the orders tried.
-  int32_t order[W_KINDS] = {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_OPROJ};
-
+  // attention -> MoE -> output), which measured fastest of the orders tried.
+  int32_t order[W_KINDS] = {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT};
 };
 
 struct Wave {
@@ -80,8 +77,8 @@ int32_t plan_teams(const PlanOptions& o, int32_t batch);
 CounterLayout make_counters(const Geometry& g, const PlanShape& s, int32_t max_batch);
 
 // Build the plan for `batch` sequences on `n_cu` compute units.  With two teams per
-// workgroup, the attention branch (QKV, attention, O-proj) goes to team 0 and the MoE
-// branch (router, expert up, expert down) to team 1 of every CU; embedding and LM-head
+// workgroup, the attention branch (QKV, attention) goes to team 0 and the MoE branch
+// (router, expert up) with the output tasks to team 1 of every CU; embedding and LM-head
 // tiles are dealt over both.  Returns "" on success, else a description of the violated
 // constraint.
 std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batch, int32_t batch,

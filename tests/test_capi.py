@@ -12,7 +12,7 @@ import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OP_EMBED, OP_QKV, OP_ROUTER, OP_ATTN, OP_MOE_UP, OP_MOE_DOWN, OP_OPROJ, OP_LM_HEAD = range(1, 9)
+OP_EMBED, OP_QKV, OP_ROUTER, OP_ATTN, OP_MOE_UP, OP_OUT, OP_LM_HEAD = range(1, 8)
 
 
 def test_exports_every_declared_symbol():
@@ -66,13 +66,13 @@ def test_plan_structure(geom, batch, n_cu):
     else:  # attention branch on team 0, MoE branch on team 1
         team_of = np.repeat(np.arange(n_cu * teams) % teams, np.diff(offs))
         ops_ = desc[:, 0]
-        assert (team_of[np.isin(ops_, [OP_QKV, OP_ATTN, OP_OPROJ])] == 0).all()
-        assert (team_of[np.isin(ops_, [OP_ROUTER, OP_MOE_UP, OP_MOE_DOWN])] == 1).all()
+        assert (team_of[np.isin(ops_, [OP_QKV, OP_ATTN])] == 0).all()
+        assert (team_of[np.isin(ops_, [OP_ROUTER, OP_MOE_UP, OP_OUT])] == 1).all()
     ops = desc[:, 0]
     gq = geom.n_q_heads + 2 * geom.n_kv_heads
-    n_rt = geom.hidden // 32
+    n_rt = geom.hidden // 8
     assert (ops == OP_EMBED).sum() == n_rt
-    assert (ops == OP_OPROJ).sum() == geom.n_layers * n_rt * geom.n_kv_heads
+    assert (ops == OP_OUT).sum() == geom.n_layers * n_rt
     assert (ops == OP_LM_HEAD).sum() == -(-geom.vocab // 32)
     qkv = desc[ops == OP_QKV]
     # QKV tiles cover every (head, rope pair) exactly once per layer
@@ -87,6 +87,12 @@ def test_plan_structure(geom, batch, n_cu):
         a = attn[attn[:, 1] == layer]
         t = qkv[qkv[:, 1] == layer]
         assert (a[:, 6] == t[0, 8]).all() and (a[:, 7] == len(t)).all()
-    # O-proj waits for the batch's combined attention of its KV group
-    op = desc[ops == OP_OPROJ]
-    assert (op[:, 7] == batch).all()
+    # one output task per residual row tile and layer, each arriving once on the next
+    # layer's input counter, which every consumer of that layer waits for in full
+    out = desc[ops == OP_OUT]
+    for layer in range(geom.n_layers):
+        o = out[out[:, 1] == layer]
+        assert sorted(o[:, 2].tolist()) == list(range(n_rt))
+        assert len(np.unique(o[:, 8])) == 1
+        nxt = qkv[qkv[:, 1] == layer + 1] if layer + 1 < geom.n_layers else desc[ops == OP_LM_HEAD]
+        assert (nxt[:, 6] == o[0, 8]).all() and (nxt[:, 7] == n_rt).all()
