@@ -1024,7 +1024,6 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     }
     bar(c);
     if (!read_ok(c)) return false;
-    if (c.ctl) ctl_claim_put(c, MI_NEXT + ((j + 1) & 1), nxt);
     if (!c.ctl) {
       // the page holding the new token is read after the wait (the acquire made it visible)
 #pragma unroll
@@ -1121,6 +1120,9 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
         part[h * (HD + 2) + HD + 1] = L;
       }
     }
+    // the claim reply for the next item, stored after the merge: the workers' compute and
+    // the merge give it time to arrive (the next item's index is read after the next barriers)
+    if (c.ctl) ctl_claim_put(c, MI_NEXT + ((j + 1) & 1), nxt);
     bar(c);
     if (c.ctl) {
       GAS float* dst = p.attn_part + (int64_t)idx * hpg * (HD + 2);
