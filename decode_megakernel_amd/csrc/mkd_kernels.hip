@@ -386,14 +386,17 @@ __device__ __forceinline__ bool worker_gemv(const Ctx& c, const RowSrc& src, int
   return gemv_tile<K, kMaxBatch, XSEG>(c, src, R, xs, tok, nb, rowsum);
 }
 
-// Controller side of the same two barriers.  A pending claim reply (next_slot >= 0) is
-// stored to its LDS slot while the workers compute.
-__device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_slot = -1, uint32_t claim = 0) {
+// Controller side of the same two barriers.  While the workers compute, a pending claim
+// reply (next_slot >= 0) is stored to its LDS slot and a deferred arrive (the previous
+// item's results, already stored) is completed on `flush`.
+__device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_slot = -1, uint32_t claim = 0,
+                                                  GAS uint32_t* flush = nullptr) {
   ctl_set_ok(c, ok);
   if (c.lane == 0 && c.s.mi[MI_T_STAGED] == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
   bar(c);
   if (!ok) return false;
   if (next_slot >= 0) ctl_claim_put(c, next_slot, claim);
+  if (flush) ctl_signal(c, flush);
   bar(c);
   if (c.lane == 0 && c.s.mi[MI_T_DONE] == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
   return true;
@@ -707,6 +710,9 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   route_layer(c, l, c.d[D_ARG0] == 0);
   const LAS int32_t* rt = c.s.route;
   const int n_items = __builtin_amdgcn_readfirstlane(rt[RT_NACT]) * NT;
+  // the arrive of item j is completed while the workers compute item j + 1, so the
+  // store round trip of its activations is off the workers' path
+  GAS uint32_t* pending = nullptr;
   for (int j = 0;; ++j) {
     const int idx = read_mi(c, MI_NEXT + (j & 1));
     if (idx >= n_items) break;
@@ -721,7 +727,7 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
     } else {
       if (c.lane < n_e) c.s.mi[MI_TOK + c.lane] = rt[RT_FLAT + o0 + c.lane] / k;
       const uint32_t nxt = ctl_claim_issue(c, head);
-      if (!ctl_gemv_barriers(c, true, MI_NEXT + ((j + 1) & 1), nxt)) return false;
+      if (!ctl_gemv_barriers(c, true, MI_NEXT + ((j + 1) & 1), nxt, pending)) return false;
       for (int i = c.lane; i < UR * n_e; i += 64) {
         const int r = i / n_e, jj = i % n_e;
         const int slot = rt[RT_FLAT + o0 + jj];  // b * k + j
@@ -730,10 +736,11 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
         const float act = gt / (1.0f + expf(-gt)) * u;
         st_pub(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * I + (int64_t)tile * UR + r, act);
       }
-      ctl_signal(c, layer_ctr(p, l, p.ctr.up_done + e));
+      pending = layer_ctr(p, l, p.ctr.up_done + e);
       if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
     }
   }
+  if (c.ctl && pending) ctl_signal(c, pending);
   return true;
 }
 
