@@ -93,7 +93,7 @@ constexpr int MI_READY_LO = 6;   // trace: when the current task's first wait co
 constexpr int MI_READY_HI = 7;
 constexpr int MI_XS_LAYER = 8;   // layer whose normed input xs holds (-1: none)
 constexpr int MI_ROUTE_LAYER = 9;  // layer whose routing tables the route area holds (-1: none)
-constexpr int MI_NEXT = 10;      // [2] claimed item indices (ping-pong)
+constexpr int MI_NEXT = 16;      // [2][2] claimed items (ping-pong): (item, task index) pairs
 constexpr int MI_OLD = 12;       // previous counter value of the last arrive
 constexpr int MI_T_STAGED = 14;  // trace: low 32 bits of the clock when inputs were staged
 constexpr int MI_T_DONE = 15;    // trace: low 32 bits of the clock when the workers finished
@@ -244,8 +244,19 @@ __device__ __forceinline__ uint32_t ctl_claim_issue(Ctx& c, GAS uint32_t* head) 
   }
   return v;
 }
-__device__ __forceinline__ void ctl_claim_put(Ctx& c, int slot, uint32_t v) {
-  if (c.lane == 0) c.s.mi[slot] = (int32_t)v;
+// Claim entry k (0 or 1) holds the item and the index of the task it belongs to, written
+// and read as one 64-bit LDS word.  A claimer loop ends when every wave reads an item
+// past the end of the queue; the controller may read it first and start its next task,
+// whose first claim overwrites entry 0 before a slower worker has read it.  The task
+// tag makes such an entry read as the end of the queue, which is right: the controller
+// only moves on after reading this task's end.
+__device__ __forceinline__ void ctl_claim_put(Ctx& c, int k, uint32_t v) {
+  if (c.lane == 0) *reinterpret_cast<LAS u32x2*>(c.s.mi + MI_NEXT + 2 * k) = u32x2{v, (uint32_t)c.task};
+}
+__device__ __forceinline__ int32_t read_claim(Ctx& c, int k) {
+  const u32x2 e = *reinterpret_cast<const LAS u32x2*>(c.s.mi + MI_NEXT + 2 * k);
+  const uint32_t item = __builtin_amdgcn_readfirstlane(e.x), tag = __builtin_amdgcn_readfirstlane(e.y);
+  return tag == (uint32_t)c.task ? (int32_t)item : 0x7FFFFFFF;
 }
 
 __device__ __forceinline__ void ctl_set_ok(Ctx& c, bool ok) {
@@ -387,15 +398,15 @@ __device__ __forceinline__ bool worker_gemv(const Ctx& c, const RowSrc& src, int
 }
 
 // Controller side of the same two barriers.  While the workers compute, a pending claim
-// reply (next_slot >= 0) is stored to its LDS slot and a deferred arrive (the previous
-// item's results, already stored) is completed on `flush`.
-__device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_slot = -1, uint32_t claim = 0,
+// reply (next_entry >= 0) is stored to its claim entry and a deferred arrive (the
+// previous item's results, already stored) is completed on `flush`.
+__device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_entry = -1, uint32_t claim = 0,
                                                   GAS uint32_t* flush = nullptr) {
   ctl_set_ok(c, ok);
   if (c.lane == 0 && c.s.mi[MI_T_STAGED] == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
   bar(c);
   if (!ok) return false;
-  if (next_slot >= 0) ctl_claim_put(c, next_slot, claim);
+  if (next_entry >= 0) ctl_claim_put(c, next_entry, claim);
   if (flush) ctl_signal(c, flush);
   bar(c);
   if (c.lane == 0 && c.s.mi[MI_T_DONE] == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
@@ -702,7 +713,7 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   if (c.ctl) {
     const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
     if (ok) ctl_stage_x_normed(c, l);
-    ctl_claim_put(c, MI_NEXT, (uint32_t)c.d[D_ARG0]);
+    ctl_claim_put(c, 0, (uint32_t)c.d[D_ARG0]);
     ctl_set_ok(c, ok);
   }
   bar(c);
@@ -714,7 +725,7 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   // store round trip of its activations is off the workers' path
   GAS uint32_t* pending = nullptr;
   for (int j = 0;; ++j) {
-    const int idx = read_mi(c, MI_NEXT + (j & 1));
+    const int idx = read_claim(c, j & 1);
     if (idx >= n_items) break;
     const int a = idx / NT, tile = idx % NT;
     const int e = __builtin_amdgcn_readfirstlane(rt[RT_ACT + a]);
@@ -727,7 +738,7 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
     } else {
       if (c.lane < n_e) c.s.mi[MI_TOK + c.lane] = rt[RT_FLAT + o0 + c.lane] / k;
       const uint32_t nxt = ctl_claim_issue(c, head);
-      if (!ctl_gemv_barriers(c, true, MI_NEXT + ((j + 1) & 1), nxt, pending)) return false;
+      if (!ctl_gemv_barriers(c, true, (j + 1) & 1, nxt, pending)) return false;
       for (int i = c.lane; i < UR * n_e; i += 64) {
         const int r = i / n_e, jj = i % n_e;
         const int slot = rt[RT_FLAT + o0 + jj];  // b * k + j
@@ -953,14 +964,12 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
   LAS float* part = ow + nw * 16 * HD;                 // [hpg][HD + 2] merged partial
   bool waited = false;
   if (c.ctl) {
-    if (c.lane == 0) {
-      c.s.mi[MI_NEXT] = c.d[D_ARG0];
-      if (keep == 0) c.s.mi[MI_XS_LAYER] = -1;
-    }
+    ctl_claim_put(c, 0, (uint32_t)c.d[D_ARG0]);
+    if (c.lane == 0 && keep == 0) c.s.mi[MI_XS_LAYER] = -1;
   }
   bar(c);
   for (int j = 0;; ++j) {
-    const int idx = read_mi(c, MI_NEXT + (j & 1));
+    const int idx = read_claim(c, j & 1);
     if (idx >= n_items) break;
     uint32_t nxt = 0;  // controller: claim reply for the next item
     int b, g = 0, chunk = 0, nchunks = 0, base_bg = 0;
@@ -1129,7 +1138,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     }
     // the claim reply for the next item, stored after the merge: the workers' compute and
     // the merge give it time to arrive (the next item's index is read after the next barriers)
-    if (c.ctl) ctl_claim_put(c, MI_NEXT + ((j + 1) & 1), nxt);
+    if (c.ctl) ctl_claim_put(c, (j + 1) & 1, nxt);
     bar(c);
     if (c.ctl) {
       GAS float* dst = p.attn_part + (int64_t)idx * hpg * (HD + 2);
@@ -1277,15 +1286,22 @@ __device__ __forceinline__ void trace_task(KParams* kp, LAS int32_t* mi, const C
   }
 }
 
-// Controller-owned per-task state (no other wave reads it, so no barrier is needed).
-__device__ __forceinline__ void reset_task_state(LAS int32_t* mi, bool first, bool leader) {
+// Team state that lives across tasks, set before the workgroup's first barrier: the
+// workers read the routing-table layer and the claim entries, so their initial values
+// must be visible before any task starts (LDS keeps the previous workgroup's contents).
+__device__ __forceinline__ void init_team_state(LAS int32_t* mi, bool leader) {
   if (leader) {
-    if (first) {
-      mi[MI_WAIT_CTR] = -1;
-      mi[MI_WAIT_TGT] = 0;
-      mi[MI_XS_LAYER] = -1;
-      mi[MI_ROUTE_LAYER] = -1;
-    }
+    mi[MI_WAIT_CTR] = -1;
+    mi[MI_WAIT_TGT] = 0;
+    mi[MI_XS_LAYER] = -1;
+    mi[MI_ROUTE_LAYER] = -1;
+    for (int k = 0; k < 4; ++k) mi[MI_NEXT + k] = -1;
+  }
+}
+
+// Controller-owned per-task state (no other wave reads it, so no barrier is needed).
+__device__ __forceinline__ void reset_task_state(LAS int32_t* mi, bool leader) {
+  if (leader) {
     mi[MI_ITEMS] = 0;
     mi[MI_READY_LO] = 0;
     mi[MI_READY_HI] = 0;
@@ -1308,6 +1324,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params prm) {
   const bool leader = (int)threadIdx.x == team * wpt * 64;
   LAS int32_t* mi = Smem(lds, team, n_teams).mi;
   if (threadIdx.x < 2) reinterpret_cast<LAS uint32_t*>(lds + kLdsBar)[threadIdx.x] = 0u;
+  init_team_state(mi, leader);
   __syncthreads();
   const int list = (int)blockIdx.x * n_teams + team;
   const CAS int32_t* offs = cas(prm.cu_offsets);
@@ -1319,7 +1336,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params prm) {
     asm volatile("" : "+s"(kpv));
     KParams* kpt = (KParams*)kpv;
     const CAS int32_t* d = cas(kpt->tasks) + (int64_t)t * D_WORDS;
-    reset_task_state(mi, t == begin, leader);
+    reset_task_state(mi, leader);
     const uint64_t t0 = kpt->trace ? wall_clock64() : 0;
     const bool ok = run_task<G>(kpt, lds, d, t, team);
     trace_task(kpt, mi, d, t0, leader, list);
@@ -1335,10 +1352,11 @@ __global__ void __launch_bounds__(kThreads, 1) mk_wave(Params prm, int32_t first
   KParams* kp = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();
   LAS int32_t* mi = Smem(lds, 0, prm.n_teams).mi;
   if (threadIdx.x == 0) reinterpret_cast<LAS uint32_t*>(lds + kLdsBar)[0] = 0u;
+  init_team_state(mi, threadIdx.x == 0);
+  reset_task_state(mi, threadIdx.x == 0);
   __syncthreads();
   const int32_t t = first + (int32_t)blockIdx.x;
   const CAS int32_t* d = cas(prm.tasks) + (int64_t)t * D_WORDS;
-  reset_task_state(mi, true, threadIdx.x == 0);
   const uint64_t t0 = prm.trace ? wall_clock64() : 0;
   run_task<G>(kp, lds, d, t, 0);
   trace_task(kp, mi, d, t0, threadIdx.x == 0, (int)blockIdx.x);
