@@ -599,105 +599,150 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
   return true;
 }
 
-// ------------------------------------------------------------------ routing (all waves)
+// ------------------------------------------------------------------ routing
 // ROUTER_TOPK + ROUTE_FINALIZE + MOE_GATHER in LDS: top-k of each token's router logits
 // (descending, ties to the lower expert index), softmax over the selected logits, then
 // the active experts in ascending order and, per expert, its (token, slot) entries in
-// ascending token order.  Called by every wave of the team after the controller's
-// acquire of the router counter; no wave has weight loads in flight here.  The tables
-// stay valid for the rest of the layer (the MoE-down claimer after the MoE-up claimer
-// on the same CU reuses them).
-__device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
-  if (!write_debug && read_mi(c, MI_ROUTE_LAYER) == l) return;
-  const DParams p = device_view(*c.kp);
-  const int B = p.batch, E = p.n_experts, k = p.top_k;  // E <= 256
+// ascending token order.  The tables stay valid for the rest of the layer (the output
+// task after the MoE-up claimer on the same CU reuses them).
+//
+// Top-k of token b by one wave: k rounds of a wave argmax, each a DPP maximum of the
+// lanes' best remaining logits and a DPP minimum of the expert indices that reach it
+// (ties go to the lower index); lane 0 writes the ids and the softmax weights.
+__device__ __forceinline__ void route_load(const Ctx& c, const DParams& p, int l, int b, float (&v)[4]) {
+  const int E = p.n_experts;  // E <= 256
+  const GAS float* r = p.router + ((int64_t)l * p.max_batch + b) * E;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = c.lane + 64 * i;
+    v[i] = e < E ? r[e] : -INFINITY;
+  }
+}
+__device__ __forceinline__ void route_select(const Ctx& c, const DParams& p, int b, float (&v)[4]) {
+  const int E = p.n_experts, k = p.top_k;
   LAS int32_t* rt = c.s.route;
   LAS float* rw = reinterpret_cast<LAS float*>(rt + RT_W);
   const int lane = c.lane;
-  // top-k of token b by wave b mod (team waves): k rounds of a wave argmax, each a DPP
-  // maximum of the lanes' best remaining logits and a DPP minimum of the expert indices
-  // that reach it (ties go to the lower index)
-  for (int b = c.tw; b < B; b += c.nw + 1) {
-    const GAS float* r = p.router + ((int64_t)l * p.max_batch + b) * E;
-    float v[4];
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      v[i] = e < E ? r[e] : -INFINITY;
+      if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
     }
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
+    const float M = wave_max(bv);
+    const int BI = wave_min_i(bv == M ? bi : 0x7FFFFFFF);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
-      }
-      const float M = wave_max(bv);
-      const int BI = wave_min_i(bv == M ? bi : 0x7FFFFFFF);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i == BI) v[i] = -INFINITY;
-      if (lane == 0) {
-        rt[RT_IDS + b * 16 + j] = BI;
-        rw[b * 16 + j] = M;  // logit for now
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i == BI) v[i] = -INFINITY;
     if (lane == 0) {
-      const float sel_v0 = rw[b * 16];
-      float sum = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const float ex = expf(rw[b * 16 + j] - sel_v0);
-        rw[b * 16 + j] = ex;
-        sum += ex;
-      }
-      for (int j = 0; j < k; ++j) rw[b * 16 + j] /= sum;
+      rt[RT_IDS + b * 16 + j] = BI;
+      rw[b * 16 + j] = M;  // logit for now
     }
   }
-  bar(c);
-  // Active experts (ascending) with their CSR offsets into the flat (token, slot) list, by
-  // the first wave: lane = expert of a 64-expert block; ballots give each active expert
-  // its rank and the exclusive prefix of the entry counts (counts <= 16: five bit planes).
-  if (c.tw == 0) {
-    int n_act = 0, n_ent = 0;
-    for (int blk = 0; blk < E; blk += 64) {
-      const int e = blk + lane;
-      int m = 0;
-      for (int t = 0; t < B * k; ++t) m += rt[RT_IDS + (t / k) * 16 + t % k] == e ? 1 : 0;
-      if (e >= E) m = 0;
-      const uint64_t act = __ballot(m > 0);
-      int pre = 0, tot = 0;
+  if (lane == 0) {
+    const float sel_v0 = rw[b * 16];
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const float ex = expf(rw[b * 16 + j] - sel_v0);
+      rw[b * 16 + j] = ex;
+      sum += ex;
+    }
+    for (int j = 0; j < k; ++j) rw[b * 16 + j] /= sum;
+  }
+}
+
+// Active experts (ascending) with their CSR offsets into the flat (token, slot) list, by
+// one wave: lane = expert of a 64-expert block; ballots give each active expert its rank
+// and the exclusive prefix of the entry counts (counts <= 16: five bit planes).
+__device__ __forceinline__ void route_csr(const Ctx& c, const DParams& p) {
+  const int B = p.batch, E = p.n_experts, k = p.top_k;
+  LAS int32_t* rt = c.s.route;
+  const int lane = c.lane;
+  int n_act = 0, n_ent = 0;
+  for (int blk = 0; blk < E; blk += 64) {
+    const int e = blk + lane;
+    int m = 0;
+    for (int t = 0; t < B * k; ++t) m += rt[RT_IDS + (t / k) * 16 + t % k] == e ? 1 : 0;
+    if (e >= E) m = 0;
+    const uint64_t act = __ballot(m > 0);
+    int pre = 0, tot = 0;
 #pragma unroll
-      for (int bit = 0; bit < 5; ++bit) {
-        const uint64_t plane = __ballot((m >> bit) & 1);
-        pre += lanes_below(plane) << bit;
-        tot += __builtin_popcountll(plane) << bit;
-      }
-      if (m > 0) {
-        const int rank = n_act + lanes_below(act);
-        int at = n_ent + pre;
-        rt[RT_ACT + rank] = e;
-        rt[RT_OFF + rank] = at;
-        for (int t = 0; t < B * k; ++t)
-          if (rt[RT_IDS + (t / k) * 16 + t % k] == e) rt[RT_FLAT + at++] = t;  // t = b * k + j
-      }
-      n_act += __builtin_popcountll(act);
-      n_ent += tot;
+    for (int bit = 0; bit < 5; ++bit) {
+      const uint64_t plane = __ballot((m >> bit) & 1);
+      pre += lanes_below(plane) << bit;
+      tot += __builtin_popcountll(plane) << bit;
     }
-    if (lane == 0) {
-      rt[RT_OFF + n_act] = n_ent;
-      rt[RT_NACT] = n_act;
+    if (m > 0) {
+      const int rank = n_act + lanes_below(act);
+      int at = n_ent + pre;
+      rt[RT_ACT + rank] = e;
+      rt[RT_OFF + rank] = at;
+      for (int t = 0; t < B * k; ++t)
+        if (rt[RT_IDS + (t / k) * 16 + t % k] == e) rt[RT_FLAT + at++] = t;  // t = b * k + j
     }
+    n_act += __builtin_popcountll(act);
+    n_ent += tot;
+  }
+  if (lane == 0) {
+    rt[RT_OFF + n_act] = n_ent;
+    rt[RT_NACT] = n_act;
+  }
+}
+
+// The tables of layer l by every wave of the team: tokens spread over the waves, then the
+// CSR by the first wave.  Called after a barrier that follows the controller's acquire of
+// the router counter; no wave has weight loads in flight here.  Tables already built for
+// layer l are kept; `write_debug` also stores the routing of every token for inspection.
+__device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
+  const DParams p = device_view(*c.kp);
+  const int B = p.batch, k = p.top_k;
+  if (read_mi(c, MI_ROUTE_LAYER) != l) {
+    for (int b = c.tw; b < B; b += c.nw + 1) {
+      float v[4];
+      route_load(c, p, l, b, v);
+      route_select(c, p, b, v);
+    }
+    bar(c);
+    if (c.tw == 0) route_csr(c, p);
+    // published before the barrier, so that every wave of the team sees the same value at
+    // the next check (a task may start right after this one without another barrier)
+    if (c.tid == 0) c.s.mi[MI_ROUTE_LAYER] = l;
+    bar(c);
   }
   if (write_debug && c.tid < B * k) {
+    const LAS int32_t* rt = c.s.route;
+    const LAS float* rw = reinterpret_cast<const LAS float*>(rt + RT_W);
     const int b = c.tid / k, j = c.tid % k;
     st_pub(p.topk_ids + ((int64_t)l * p.max_batch + b) * k + j, rt[RT_IDS + b * 16 + j]);
     st_pub(p.topk_w + ((int64_t)l * p.max_batch + b) * k + j, rw[b * 16 + j]);
   }
-  // published before the barrier, so that every wave of the team sees the same value at
-  // the next check (a task may start right after this one without another barrier)
-  if (c.tid == 0) c.s.mi[MI_ROUTE_LAYER] = l;
-  bar(c);
+}
+
+// The controller builds the tables of layer l alone, without barriers, when the router
+// tiles of layer l are already done (one poll, no wait): used while the workers compute
+// another task (attention), so that the MoE-up claimer that follows on this CU starts
+// with its routing in place.  The workers read the tables only after a later barrier.
+// Batches of at most kRouteAhead tokens: their logits are loaded together (one round trip).
+constexpr int kRouteAhead = 8;
+__device__ __forceinline__ void ctl_route_ahead(Ctx& c, int l) {
+  const DParams p = device_view(*c.kp);
+  if (p.batch > kRouteAhead || read_mi(c, MI_ROUTE_LAYER) == l) return;
+  const int n_router_tiles = (p.n_experts + p.shape.router_rows - 1) / p.shape.router_rows;
+  uint32_t seen = 0;
+  if (c.lane == 0) seen = ctr_load(layer_ctr(p, l, p.ctr.router_done));
+  if (__shfl((int)seen, 0, 64) < n_router_tiles) return;
+  fence_acquire_agent();
+  float v[kRouteAhead][4];
+#pragma unroll
+  for (int b = 0; b < kRouteAhead; ++b)
+    if (b < p.batch) route_load(c, p, l, b, v[b]);
+#pragma unroll
+  for (int b = 0; b < kRouteAhead; ++b)
+    if (b < p.batch) route_select(c, p, b, v[b]);
+  route_csr(c, p);
+  if (c.lane == 0) c.s.mi[MI_ROUTE_LAYER] = l;
 }
 
 // ------------------------------------------------------------------ OP_MOE_UP (claimer)
@@ -711,7 +756,9 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   const int UR = p.shape.up_rows, NT = p.shape.n_up_tiles, H = p.hidden, I = p.inter, k = p.top_k;
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.up_claim);
   if (c.ctl) {
-    const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
+    // routing tables of layer l built ahead mean that the router wait is satisfied
+    const bool ok =
+        read_mi(c, MI_ROUTE_LAYER) == l || ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
     if (ok) ctl_stage_x_normed(c, l);
     ctl_claim_put(c, 0, (uint32_t)c.d[D_ARG0]);
     ctl_set_ok(c, ok);
@@ -1040,6 +1087,9 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     }
     bar(c);
     if (!read_ok(c)) return false;
+    // the controller is idle until the merge: it builds this layer's routing tables for
+    // the MoE-up claimer that follows on this CU
+    if (c.ctl) ctl_route_ahead(c, l);
     if (!c.ctl) {
       // the page holding the new token is read after the wait (the acquire made it visible)
 #pragma unroll
