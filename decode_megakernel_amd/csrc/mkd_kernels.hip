@@ -270,9 +270,10 @@ __device__ __forceinline__ bool read_ok(Ctx& c) { return read_mi(c, MI_OK) != 0;
 // with a common leading dimension, at element offsets seg0..seg3 from a wave-uniform
 // base (32 bits: a tile's rows lie within a few hundred MB of its base).  With separate
 // activation blocks (the output tasks: O-proj column blocks, or different experts, in the
-// segments; n1 = 2^xsh), the rows of segment s multiply xs + s * xstep + tok[j] * xld;
-// otherwise every row multiplies xs + tok[j] * xld (xld = 0: the row length).  Two
-// segments hold the two halves of RoPE pairs or gate|up rows.
+// segments; n1 = 2^xsh), the rows of segment s multiply xs + s * xstep + tok[j] * xld, or
+// with an offset table xs + (xtab[s] - xbase) * xstep + tok[j] * xld; otherwise every row
+// multiplies xs + tok[j] * xld (xld = 0: the row length).  Two segments hold the two
+// halves of RoPE pairs or gate|up rows.
 struct RowSrc {
   const GAS uint16_t* base;
   uint32_t seg0, seg1, seg2, seg3;
@@ -283,6 +284,9 @@ struct RowSrc {
   // segments from a table (expert ids in LDS): segment s starts at eids[s] * escale + seg0
   const LAS int32_t* eids;
   uint32_t escale;
+  // activation blocks from a table (LDS), or evenly spaced when null
+  const LAS int32_t* xtab;
+  int32_t xbase;
   __device__ uint32_t row_off(int i) const {
     if (eids) return (uint32_t)eids[i >> xsh] * escale + seg0 + (uint32_t)(i & (n1 - 1)) * ld;
     if (i < n1) return seg0 + (uint32_t)i * ld;
@@ -290,10 +294,10 @@ struct RowSrc {
     if (i < 3 * n1) return seg2 + (uint32_t)(i - 2 * n1) * ld;
     return seg3 + (uint32_t)(i - 3 * n1) * ld;
   }
-  __device__ int32_t x_off(int i) const { return (i >> xsh) * xstep; }
+  __device__ int32_t x_off(int i) const { return ((xtab ? xtab[i >> xsh] - xbase : (i >> xsh))) * xstep; }
 };
 __device__ __forceinline__ RowSrc row_src(const GAS uint16_t* b1, const GAS uint16_t* b2, int64_t ld, int n1) {
-  return RowSrc{b1, 0u, (uint32_t)(b2 - b1), 0u, 0u, (uint32_t)ld, n1, 0, 0, 0, nullptr, 0u};
+  return RowSrc{b1, 0u, (uint32_t)(b2 - b1), 0u, 0u, (uint32_t)ld, n1, 0, 0, 0, nullptr, 0u, nullptr, 0};
 }
 
 // Lane mapping of a K-long bf16 row onto a worker wave: LPR lanes per row, CPL
@@ -852,6 +856,7 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
     so.ld = (uint32_t)QD; so.n1 = R; so.xld = QD;
     so.xstep = KH; so.xsh = 31 - __builtin_clz(R);
     so.eids = nullptr; so.escale = 0u;
+    so.xtab = nullptr; so.xbase = 0;
     const int TG = min(kMaxBatch, xs_floats / QD);
     for (int t0 = 0; t0 < B; t0 += TG) {
       const int nb = min(TG, B - t0);
@@ -893,29 +898,52 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
       sd.base = p.w_down + (int64_t)l * E * H * KI;
       sd.seg0 = (uint32_t)r0 * KI; sd.seg1 = sd.seg2 = sd.seg3 = 0u;
       sd.ld = (uint32_t)KI; sd.n1 = R; sd.xld = KI;
-      sd.xstep = B * KI; sd.xsh = 31 - __builtin_clz(R);
+      // activations entry-major: row (expert a0 + s, token j) at xs + (off[a0 + s] - off[a0] + j) * KI
+      const int ob0 = __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a0]);
+      sd.xstep = KI; sd.xsh = 31 - __builtin_clz(R);
       sd.eids = rtab + RT_ACT + a0; sd.escale = (uint32_t)(H * KI);
+      sd.xtab = rtab + RT_OFF + a0; sd.xbase = ob0;
       if (!c.ctl) {
         if (!worker_gemv<KI, true>(c, sd, na * R, c.s.xs, c.s.mi + MI_TOK, nb, c.s.rowsum)) return false;
       } else {
         GAS uint32_t* up = layer_ctr(p, l, p.ctr.up_done);
         const int my_e = c.lane < na ? rtab[RT_ACT + a0 + c.lane] : 0;
         const bool ok = ctl_wait_lanes(c, up + my_e, na, (uint32_t)p.shape.n_up_tiles);
+        // trace: an output task's "staged" time is when its first expert group's up tiles
+        // were all done, its "done" time when its last GEMV finished
+        if (c.lane == 0 && a0 == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
         if (ok) {
-          // activations: expert a0 + sg, token slot j at xs + sg*B*KI + j*KI
-          for (int sg = 0; sg < na; ++sg) {
-            const int ob = rtab[RT_OFF + a0 + sg], n_e = rtab[RT_OFF + a0 + sg + 1] - ob;
-            for (int i = c.lane; i < n_e * (KI / 4); i += 64) {
-              const int j = i / (KI / 4), k4 = (i % (KI / 4)) * 4;
-              const int slot = rtab[RT_FLAT + ob + j];
-              *reinterpret_cast<LAS f32x4*>(c.s.xs + sg * B * KI + j * KI + k4) =
-                  *reinterpret_cast<const GAS f32x4*>(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * KI + k4);
+          // activation rows of the group's (expert, token) entries, in CSR order; the
+          // loads of eight rows are all issued before their LDS stores
+          const int n_rows = __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a0 + na]) - ob0;
+          constexpr int QL = (KI / 4 + 63) / 64;  // 16-byte pieces per lane per row
+          for (int r0 = 0; r0 < n_rows; r0 += 8) {
+            f32x4 buf[8][QL];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int r = r0 + u;
+              const int slot = r < n_rows ? rtab[RT_FLAT + ob0 + r] : 0;
+              const GAS float* src = p.moe_act + ((int64_t)l * p.max_batch * k + slot) * KI;
+#pragma unroll
+              for (int q = 0; q < QL; ++q) {
+                const int k4 = (c.lane + 64 * q) * 4;
+                if (r < n_rows && k4 < KI) buf[u][q] = *reinterpret_cast<const GAS f32x4*>(src + k4);
+              }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+#pragma unroll
+              for (int q = 0; q < QL; ++q) {
+                const int k4 = (c.lane + 64 * q) * 4;
+                if (r0 + u < n_rows && k4 < KI) *reinterpret_cast<LAS f32x4*>(c.s.xs + (r0 + u) * KI + k4) = buf[u][q];
+              }
             }
           }
           if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
           if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
         }
         if (!ctl_gemv_barriers(c, ok)) return false;
+        if (c.lane == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
         // router-weighted sum, experts in ascending order (one expert per pass: a token
         // appears once per expert, so no two lanes update the same element)
         for (int sg = 0; sg < na; ++sg) {

@@ -55,7 +55,9 @@ def summarize(rec: dict) -> dict:
             "work_us_total": round(float(work.sum()), 1),
             "work_us_mean": round(float(work.mean()), 2),
             "items": int(rec["items"][m].sum()),
-            # for single-tile tasks: ready -> inputs staged, staged -> compute done, done -> end
+            # single-tile tasks: ready -> inputs staged, staged -> compute done, done -> end;
+            # output tasks: ready (attention combined) -> expert up tiles done, -> last GEMV
+            # done, -> end
             "stage_us_median": round(float(np.median(rec["staged"][has] - rec["ready"][has])), 2) if has.any() else None,
             "compute_us_median": round(float(np.median(rec["done"][has] - rec["staged"][has])), 2) if has.any() else None,
             "epilogue_us_median": round(float(np.median(rec["end"][has] - rec["done"][has])), 2) if has.any() else None,
