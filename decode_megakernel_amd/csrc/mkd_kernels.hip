@@ -232,14 +232,15 @@ __device__ __forceinline__ void ctl_signal(Ctx& c, GAS uint32_t* ctr) {
 // Claimer queues: claimer i of n takes item i first without touching the queue, then
 // items n + (queue head), so the claimers' first items cost no atomic and the queue
 // only sees the later claims, spread over time.  The claimer index and count are the
-// descriptor's ARG0 and ARG1.
+// descriptor's ARG0 and ARG1 (the MoE-up queue moves the static items to the claimers
+// that are free first; its queue items start at `base`).
 // Issue a claim without waiting for the reply: the returned item (lane 0) is only
 // consumed by ctl_claim_put, placed where the reply has had time to arrive (the
 // wait-counter pass waits for it there).
-__device__ __forceinline__ uint32_t ctl_claim_issue(Ctx& c, GAS uint32_t* head) {
+__device__ __forceinline__ uint32_t ctl_claim_issue(Ctx& c, GAS uint32_t* head, int32_t base) {
   uint32_t v = 0;
   if (c.lane == 0) {
-    v = (uint32_t)c.d[D_ARG1] + ctr_add(head, 1u);
+    v = (uint32_t)base + ctr_add(head, 1u);
     c.s.mi[MI_ITEMS] += 1;
   }
   return v;
@@ -749,6 +750,14 @@ __device__ __forceinline__ void ctl_route_ahead(Ctx& c, int l) {
   if (c.lane == 0) c.s.mi[MI_ROUTE_LAYER] = l;
 }
 
+// Attention items of this step: (sequence, KV group, chunk of pages_per_item pages).
+__device__ __forceinline__ int attn_item_count(const DParams& p) {
+  const int ppi = p.shape.pages_per_item;
+  int n = 0;
+  for (int b = 0; b < p.batch; ++b) n += ((p.seq_lens[b] / p.page + 1 + ppi - 1) / ppi) * p.n_kv;
+  return min(n, p.max_attn_items);
+}
+
 // ------------------------------------------------------------------ OP_MOE_UP (claimer)
 // Claims (active expert, tile of up_rows activation rows); weights = up_rows gate rows and
 // the matching up rows; epilogue silu(gate) * up for every token routed to the expert;
@@ -759,12 +768,20 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   const int l = c.d[D_LAYER];
   const int UR = p.shape.up_rows, NT = p.shape.n_up_tiles, H = p.hidden, I = p.inter, k = p.top_k;
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.up_claim);
+  // Static first items go to the claimers that had no attention item in this step
+  // (claimer i of both queues runs on the same CU, attention first): claimer i >= n_attn
+  // takes item i - n_attn.  The others reach this task only after their attention item
+  // (or its combine) and start from the queue, whose items follow the static ones, so no
+  // late CU holds an item back.
+  int n_static = 0;
   if (c.ctl) {
+    const int n_attn = attn_item_count(p), ci = c.d[D_ARG0];
+    n_static = max(0, c.d[D_ARG1] - n_attn);
     // routing tables of layer l built ahead mean that the router wait is satisfied
     const bool ok =
         read_mi(c, MI_ROUTE_LAYER) == l || ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
     if (ok) ctl_stage_x_normed(c, l);
-    ctl_claim_put(c, 0, (uint32_t)c.d[D_ARG0]);
+    ctl_claim_put(c, 0, ci >= n_attn ? (uint32_t)(ci - n_attn) : ctl_claim_issue(c, head, n_static));
     ctl_set_ok(c, ok);
   }
   bar(c);
@@ -788,7 +805,7 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
       if (!worker_gemv<K>(c, src, 2 * UR, c.s.xs, c.s.mi + MI_TOK, n_e, c.s.rowsum)) return false;
     } else {
       if (c.lane < n_e) c.s.mi[MI_TOK + c.lane] = rt[RT_FLAT + o0 + c.lane] / k;
-      const uint32_t nxt = ctl_claim_issue(c, head);
+      const uint32_t nxt = ctl_claim_issue(c, head, n_static);
       if (!ctl_gemv_barriers(c, true, (j + 1) & 1, nxt, pending)) return false;
       for (int i = c.lane; i < UR * n_e; i += 64) {
         const int r = i / n_e, jj = i % n_e;
@@ -1021,9 +1038,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
   const int l = c.d[D_LAYER];
   const int nkv = p.n_kv, ppi = p.shape.pages_per_item, hpg = p.n_q / nkv;
   constexpr int NK = HD / 32, NV = HD / 16, MAXP = kMaxPagesPerWave;
-  int n_items = 0;
-  for (int b = 0; b < p.batch; ++b) n_items += ((p.seq_lens[b] / p.page + 1 + ppi - 1) / ppi) * nkv;
-  if (n_items > p.max_attn_items) n_items = p.max_attn_items;
+  const int n_items = attn_item_count(p);
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.attn_claim);
   const int nw = c.nw;
   // The attention buffers go after this layer's staged normed input when both fit, so
@@ -1104,7 +1119,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
           const int i = c.lane + 64 * u;
           if (i < hpg * HD / 4) qv[u] = *reinterpret_cast<const GAS f32x4*>(qsrc + i * 4);
         }
-        nxt = ctl_claim_issue(c, head);
+        nxt = ctl_claim_issue(c, head, c.d[D_ARG1]);
 #pragma unroll
         for (int u = 0; u < QPL; ++u) {
           const int i = c.lane + 64 * u;
@@ -1112,6 +1127,8 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
         }
       }
       ctl_set_ok(c, ok);
+      // trace: "staged" = the first item's queries in LDS
+      if (c.lane == 0 && c.s.mi[MI_T_STAGED] == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
     }
     bar(c);
     if (!read_ok(c)) return false;
@@ -1223,6 +1240,8 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
       for (int i = c.lane; i < hpg * (HD + 2); i += 64) st_pub(dst + i, part[i]);
       const uint32_t old = ctl_arrive(c, layer_ctr(p, l, p.ctr.attn_items + b * nkv + g));
       if (c.lane == 0) c.s.mi[MI_OLD] = (int32_t)old;
+      // trace: "done" = the last item's partial published (a combine follows it or not)
+      if (c.lane == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
     }
     bar(c);
     if ((uint32_t)read_mi(c, MI_OLD) + 1 == (uint32_t)nchunks) {

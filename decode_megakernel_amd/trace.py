@@ -57,7 +57,8 @@ def summarize(rec: dict) -> dict:
             "items": int(rec["items"][m].sum()),
             # single-tile tasks: ready -> inputs staged, staged -> compute done, done -> end;
             # output tasks: ready (attention combined) -> expert up tiles done, -> last GEMV
-            # done, -> end
+            # done, -> end; attention claimers: ready -> first queries staged, -> last
+            # partial published, -> end (the combine, when this claimer was last)
             "stage_us_median": round(float(np.median(rec["staged"][has] - rec["ready"][has])), 2) if has.any() else None,
             "compute_us_median": round(float(np.median(rec["done"][has] - rec["staged"][has])), 2) if has.any() else None,
             "epilogue_us_median": round(float(np.median(rec["end"][has] - rec["done"][has])), 2) if has.any() else None,
@@ -110,6 +111,7 @@ def chrome_trace(rec: dict, path: str) -> None:
                        "dur": float(rec["ready"][i] - rec["start"][i]), "cat": "wait"})
         ev.append({"name": name, "ph": "X", "pid": 0, "tid": wg, "ts": float(rec["ready"][i]),
                    "dur": float(max(rec["end"][i] - rec["ready"][i], 0.0)), "cat": "work",
-                   "args": {"gidx": int(rec["gidx"][i]), "items": int(rec["items"][i])}})
+                   "args": {"gidx": int(rec["gidx"][i]), "items": int(rec["items"][i]),
+                            "staged": round(float(rec["staged"][i]), 3), "done": round(float(rec["done"][i]), 3)}})
     with open(path, "w") as f:
         json.dump({"traceEvents": ev, "displayTimeUnit": "ns"}, f)
