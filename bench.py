@@ -30,6 +30,8 @@ def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_megakernel_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".h", ".cpp")):
+            continue  # built objects
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
