@@ -12,12 +12,19 @@ int32_t plan_teams(const PlanOptions& o, int32_t batch) {
   return batch <= o.two_team_max_batch ? 2 : 1;
 }
 
+// MoE-up item rows: the largest divisor of the expert inter size not above the option.
+static int32_t up_rows_for(const Geometry& g, const PlanOptions& o) {
+  int32_t r = std::max(1, std::min(o.up_rows, g.inter));
+  while (g.inter % r) --r;
+  return r;
+}
+
 PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t n_teams) {
   PlanShape s{};
   s.rt_rows = o.rt_rows;
   s.n_rt = g.hidden / o.rt_rows;
-  s.up_rows = o.up_rows;
-  s.n_up_tiles = g.inter / o.up_rows;
+  s.up_rows = up_rows_for(g, o);
+  s.n_up_tiles = g.inter / s.up_rows;
   s.pages_per_item = n_teams == 2 ? o.pages_per_item_2 : o.pages_per_item;
   s.qkv_rows = 2 * o.qkv_max_pairs;
   s.router_rows = o.router_rows;
@@ -83,7 +90,7 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
     return "n_q * head_dim must be 1, 2 or 4 times hidden";
   if (o.rt_rows * ((g.n_q * g.head_dim) / g.hidden) > 35 || 4 * o.rt_rows > 35)
     return "output tiles are limited to 35 GEMV rows";
-  if (g.inter % o.up_rows) return "moe_inter must be a multiple of up_rows";
+  if (o.up_rows < 1) return "up_rows must be positive";
   if (o.qkv_max_pairs < 1) return "qkv_max_pairs must be positive";
   const int n_teams = plan_teams(o, batch);
   if (n_teams == 2 && batch > 4) return "two teams hold at most 4 sequences";

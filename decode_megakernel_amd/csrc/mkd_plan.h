@@ -38,7 +38,8 @@ enum WaveKind : int32_t { W_QKV = 0, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT, W_KINDS 
 
 struct PlanOptions {
   int32_t rt_rows = 8;         // residual rows per output task (O-proj + expert down rows)
-  int32_t up_rows = MKD_UP_ROWS;  // activation rows per MoE-up item (weights: 2x rows)
+  int32_t up_rows = MKD_UP_ROWS;  // activation rows per MoE-up item at most (weights: 2x rows); the
+                                  // largest divisor of the expert inter size not above it is used
   int32_t pages_per_item = MKD_PPI;  // attention pages per claimed item, one team of 7 workers
   int32_t pages_per_item_2 = 6;  // the same with two teams of 3 workers each
   int32_t teams = MKD_TEAMS;    // teams per workgroup: 1, 2, or 0 = 2 when batch <= two_team_max_batch
