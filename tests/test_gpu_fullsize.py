@@ -1,0 +1,256 @@
+"""GPU parity at the full sizes of the benchmark workloads, in the launch configuration
+bench.py times: the 48-layer model runs whole decode steps, one megakernel launch each.
+
+A whole reference step at these sizes costs seconds to minutes of CPU time, so the CPU
+reference recomputes sampled layers: the first, a middle and the last layer, each from
+the GPU's own residual stream entering it, replayed over every step of the test with
+the reference's own KV cache for that layer (so the K/V the GPU appended at one step is
+read back at the next).  The final norm and LM head are recomputed from the GPU's last
+hidden state.  Rules as in parity.py: per-row relative error <= 2e-2 on the layer output
+and the logits, the new K/V slots within the same bound and every other slot of their
+pages bit-exact, expert ids identical except near router ties, greedy argmax identical
+except reported near-ties.  Needs an MI355X (about 90 GB of device memory)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import REL_TOL, max_rel_rows, router_near_tie
+
+pytestmark = pytest.mark.gpu
+
+SAMPLED = (0, 23, 47)
+
+
+@pytest.fixture(scope="module")
+def weights():
+    import torch
+    from synth import device as sdev
+
+    torch.cuda.set_device(0)
+    wl = synth.full_workload(steps=1)
+    print("[setup] full-model weights on the GPU", flush=True)
+    W = sdev.device_weights(wl)
+    torch.cuda.synchronize()
+    yield W
+    del W
+    torch.cuda.empty_cache()
+
+
+def host_layer(wl, layer):
+    """bf16 bits of one layer's weights (slices of the seeded tensors)."""
+    g = wl.geom
+    H, E, I, QD = g.hidden, g.n_experts, g.moe_inter, g.n_q_heads * g.head_dim
+
+    def sl(name, per):
+        return synth.host_weight(wl, name, offset=layer * per, n=per)
+
+    return dict(gamma=sl("norm", H), w_qkv=sl("w_qkv", g.qkv_rows * H), w_o=sl("w_o", H * QD),
+                w_router=sl("w_router", E * H), w_gate_up=sl("w_gate_up", E * 2 * I * H),
+                w_down=sl("w_down", E * H * I))
+
+
+def page_slots(g, n_pages, page, grp_count):
+    """In-layer element indices of one physical page (K then V blocks, every group)."""
+    P, D = g.page_size, g.head_dim
+    idx = []
+    for kv in (0, 1):
+        for grp in range(grp_count):
+            base = ((kv * n_pages + page) * g.n_kv_heads + grp) * P * D
+            idx.append(base + np.arange(P * D))
+    return np.concatenate(idx)
+
+
+def new_slot_mask(g, page_idx, t):
+    """Within page_slots(...) of one page: True at the new token's K and V elements."""
+    P, D = g.page_size, g.head_dim
+    m = np.zeros(page_idx.size, bool)
+    per = P * D
+    for blk in range(2 * g.n_kv_heads):
+        kv = blk // g.n_kv_heads
+        if kv == 0:
+            m[blk * per + t * D + np.arange(D)] = True      # K: token-major
+        else:
+            m[blk * per + np.arange(D) * P + t] = True      # V: dim-major
+    return m
+
+
+class GpuRun:
+    """One engine over a KV pool; step() runs one decode step and returns host copies."""
+
+    def __init__(self, W, wl, max_batch):
+        import torch
+
+        import decode_megakernel_amd as mkd
+        from synth import device as sdev
+
+        self.torch, self.mkd, self.wl = torch, mkd, wl
+        self.pool = sdev.device_kv_pool(wl)
+        torch.cuda.synchronize()
+        self.eng = mkd.Engine(wl.geom, 0, max_batch=max_batch, max_pages_per_seq=wl.max_pages)
+        self.eng.load_weights(W)
+        self.eng.set_mode(mkd.MODE_MEGAKERNEL)
+
+    def step(self, tokens, seq_lens, page_table):
+        torch, mkd, g = self.torch, self.mkd, self.wl.geom
+        B = len(tokens)
+        t = torch.from_numpy(np.asarray(tokens, np.int32)).cuda()
+        sl = torch.from_numpy(np.asarray(seq_lens, np.int32)).cuda()
+        pt = torch.from_numpy(np.ascontiguousarray(page_table, np.int32)).cuda()
+        logits = torch.full((B, g.vocab), float("nan"), dtype=torch.float32, device="cuda")
+        self.eng.decode_step(t, sl, np.asarray(seq_lens, np.int32), pt, self.pool, self.wl.n_pages,
+                             logits, h_page_table=np.asarray(page_table, np.int32))
+        self.eng.sync_status()
+        return dict(logits=logits.cpu().numpy(), hidden=self.eng.debug_read(mkd.DEBUG_HIDDEN, B),
+                    ids=self.eng.debug_read(mkd.DEBUG_TOPK_IDS, B))
+
+    def pool_bits(self, layer, idx):
+        nl = self.wl.geom.kv_layer_numel(self.wl.n_pages)
+        sel = self.torch.from_numpy(layer * nl + np.asarray(idx, np.int64)).cuda()
+        return self.pool.index_select(0, sel).view(self.torch.int16).cpu().numpy().view(np.uint16)
+
+    def close(self):
+        self.eng.close()
+        del self.pool
+        self.torch.cuda.empty_cache()
+
+
+def check_layer_steps(wl, layer, steps_inputs, steps_out, gpu):
+    """Replays `layer` over the steps with the reference and checks every step."""
+    g = wl.geom
+    Wl = host_layer(wl, layer)
+    kv = synth.host_kv_layer(wl, layer)
+    rep = dict(layer=layer, hidden_rel=0.0, kv_rel=0.0, ties=0)
+    for s, ((tokens, seq_lens, pt), out) in enumerate(zip(steps_inputs, steps_out)):
+        h = np.array(out["hidden"][layer], dtype=np.float32, copy=True)
+        o = oracle.layer(g, seq_lens, pt, kv, wl.n_pages, Wl["gamma"], Wl["w_qkv"], Wl["w_o"],
+                         Wl["w_router"], Wl["w_gate_up"], Wl["w_down"], h, debug=True)
+        rel = max_rel_rows(out["hidden"][layer + 1], h)
+        rep["hidden_rel"] = max(rep["hidden_rel"], rel)
+        assert rel <= REL_TOL, f"layer {layer} step {s}: hidden rel {rel}"
+        # routing: identical except near ties of the reference's router logits
+        mism = np.any(out["ids"][layer] != o["ids"], axis=-1)
+        tie = router_near_tie(o["router"], g.top_k)
+        assert not (mism & ~tie).any(), f"layer {layer} step {s}: expert ids differ without a near tie"
+        rep["ties"] += int((mism & tie).sum())
+    # Pages that received a new token in any step (the GPU pool is read after the last
+    # step): the new slots within tolerance of the reference's, every other slot
+    # bit-exact.
+    new = {}
+    for tokens, seq_lens, pt in steps_inputs:
+        for b, pos in enumerate(seq_lens):
+            new.setdefault(int(pt[b][pos // g.page_size]), set()).add(pos % g.page_size)
+    for page, ts in new.items():
+        idx = page_slots(g, wl.n_pages, page, g.n_kv_heads)
+        m = np.zeros(idx.size, bool)
+        for t in ts:
+            m |= new_slot_mask(g, idx, t)
+        gb, rb = gpu.pool_bits(layer, idx), kv[idx]
+        assert np.array_equal(gb[~m], rb[~m]), f"layer {layer} page {page}: slots other than the new ones changed"
+        gk = oracle.bf16_to_f32(gb[m]).astype(np.float64)
+        rk = oracle.bf16_to_f32(rb[m]).astype(np.float64)
+        kr = float(np.max(np.abs(gk - rk)) / max(np.max(np.abs(rk)), 1e-30))
+        rep["kv_rel"] = max(rep["kv_rel"], kr)
+        assert kr <= REL_TOL, f"layer {layer} page {page}: new K/V rel {kr}"
+    return rep
+
+
+def check_lm_head(wl, steps_out):
+    g = wl.geom
+    gamma = synth.host_weight(wl, "norm", offset=g.n_layers * g.hidden, n=g.hidden)
+    embed = synth.host_weight(wl, "embed")
+    rep = dict(logits_rel=0.0, near_ties=0)
+    for s, out in enumerate(steps_out):
+        ref = oracle.lm_head(g, out["hidden"][g.n_layers], gamma, embed)
+        rel = max_rel_rows(out["logits"], ref)
+        rep["logits_rel"] = max(rep["logits_rel"], rel)
+        assert np.isfinite(out["logits"]).all(), f"step {s}: non-finite logits"
+        assert rel <= REL_TOL, f"step {s}: logits rel {rel}"
+        ga, ra = out["logits"].argmax(-1), ref.argmax(-1)
+        srt = -np.sort(-ref.astype(np.float64), axis=-1)
+        near = (srt[:, 0] - srt[:, 1]) < REL_TOL * np.max(np.abs(ref), axis=-1)
+        assert not ((ga != ra) & ~near).any(), f"step {s}: greedy argmax differs"
+        rep["near_ties"] += int(((ga != ra) & near).sum())
+    return rep
+
+
+def _report(name, reps):
+    print(f"[parity] {name}: " + "; ".join(str(r) for r in reps), flush=True)
+
+
+def test_full_model_greedy_steps(weights):
+    """The benchmark workload: 48 layers, batch 1, 8192 cached tokens, greedy decoding
+    (each step's argmax is the next step's token) over 4 steps."""
+    wl = synth.full_workload(ctx=8192, batch=1, steps=4)
+    print("[case] full model b1 ctx8192, 4 greedy steps", flush=True)
+    gpu = GpuRun(weights, wl, max_batch=1)
+    pt = synth.page_tables(wl)
+    tokens = synth.host_tokens(wl)
+    ins, outs = [], []
+    try:
+        for s in range(4):
+            seq_lens = [wl.seq_lens[0] + s]
+            out = gpu.step(tokens, seq_lens, pt)
+            ins.append((tokens.copy(), seq_lens, pt))
+            outs.append(out)
+            tokens = out["logits"].argmax(-1).astype(np.int32)
+        reps = [check_layer_steps(wl, l, ins, outs, gpu) for l in SAMPLED]
+        reps.append(check_lm_head(wl, outs))
+    finally:
+        gpu.close()
+    _report("full-b1-ctx8192-greedy", reps)
+
+
+def test_full_model_continuous_batching(weights):
+    """16 ragged sequences (lengths uniform in [512, 32768]) in one scattered page pool;
+    at the second step two sequences have finished and two others joined."""
+    rng = np.random.Generator(np.random.PCG64(20251202))
+    lens = [int(x) for x in rng.integers(512, 32769, size=18)]
+    wl = synth.make_workload("full-ragged18", synth.FULL, lens, spare_pages=40,
+                             max_pages=(max(lens) + 2) // 16 + 2)
+    print(f"[case] full model continuous batching, lengths {lens}", flush=True)
+    pt_all = synth.page_tables(wl)
+    gpu = GpuRun(weights, wl, max_batch=16)
+    ins, outs = [], []
+    try:
+        # step 0: sequences 0..15; step 1: 2 and 9 finished, 16 and 17 joined
+        rows0 = list(range(16))
+        rows1 = [r for r in rows0 if r not in (2, 9)] + [16, 17]
+        tok0 = synth.host_tokens(synth.make_workload("t", synth.FULL, lens[:16]), 0)
+        out0 = gpu.step(tok0, [lens[r] for r in rows0], pt_all[rows0])
+        ins.append((tok0, [lens[r] for r in rows0], pt_all[rows0]))
+        outs.append(out0)
+        nxt = dict(zip(rows0, out0["logits"].argmax(-1).astype(np.int32)))
+        tok1 = np.asarray([nxt.get(r, 7 * r + 1) for r in rows1], np.int32)
+        sl1 = [lens[r] + (1 if r in nxt else 0) for r in rows1]
+        out1 = gpu.step(tok1, sl1, pt_all[rows1])
+        reps = []
+        for layer in SAMPLED:
+            # the reference replays each step on the rows present in it; its KV layer holds
+            # every sequence, so step 0's appends are read at step 1
+            reps.append(check_layer_steps(wl, layer,
+                                          [(tok0, [lens[r] for r in rows0], pt_all[rows0]),
+                                           (tok1, sl1, pt_all[rows1])], [out0, out1], gpu))
+        reps.append(check_lm_head(wl, [out0, out1]))
+    finally:
+        gpu.close()
+    _report("full-ragged16-join-finish", reps)
+
+
+@pytest.mark.parametrize("batch,ctx", [(1, 262144), (4, 65536)])
+def test_full_model_long_context(weights, batch, ctx):
+    """Long contexts: batch 1 at 262144 cached tokens and batch 4 at 65536 each (about
+    26 GB of KV cache), one step."""
+    wl = synth.full_workload(ctx=ctx, batch=batch, steps=1)
+    print(f"[case] full model b{batch} ctx{ctx}", flush=True)
+    gpu = GpuRun(weights, wl, max_batch=batch)
+    pt = synth.page_tables(wl)
+    tokens = synth.host_tokens(wl)
+    try:
+        out = gpu.step(tokens, list(wl.seq_lens), pt)
+        reps = [check_layer_steps(wl, l, [(tokens, list(wl.seq_lens), pt)], [out], gpu)
+                for l in (0, 47)]
+        reps.append(check_lm_head(wl, [out]))
+    finally:
+        gpu.close()
+    _report(f"full-b{batch}-ctx{ctx}", reps)
