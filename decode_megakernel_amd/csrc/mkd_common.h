@@ -81,6 +81,7 @@ enum GlobalCounter : int32_t {
   G_ERR_SEEN = 4,  // value observed
   G_ERR_WANT = 5,  // target
   G_DONE_WGS = 6,  // workgroups that finished their list
+  G_TAGGED = -2,   // G_ERR_CTR value of a wait on tagged data (no counter)
   G_COUNT = 8,
 };
 
@@ -123,9 +124,9 @@ struct Params {
   float* h;           // [L+1][maxB][H]
   float* ss;          // [L+1][maxB][n_rt] per-row-tile sum of squares
   float* q;           // [L][maxB][nq*hd] post-RoPE queries
-  float* attn_part;   // [max_items][hpg][hd + 2] unnormalised o, then m, l
-  float* attn_o;      // [L][maxB][nq*hd]
-  float* router;      // [L][maxB][E]
+  uint64_t* attn_part;  // [max_items][hpg][hd + 2] tagged: unnormalised o, then m, l
+  uint64_t* attn_o;     // [L][maxB][nq*hd] tagged
+  uint64_t* router;   // [L][maxB][E] tagged
   int32_t* topk_ids;  // [L][maxB][k]
   float* topk_w;      // [L][maxB][k]
   float* moe_act;     // [L][maxB*k][I]
@@ -138,6 +139,7 @@ struct Params {
   const int32_t* cu_offsets; // [n_wg * n_teams + 1]: task list of team t of workgroup i is list i * n_teams + t
   int32_t max_attn_items;    // capacity of attn_part
   int32_t spin_limit;        // watchdog: polls before a wait gives up
+  uint32_t epoch;            // this step's number in [1, 2^24): tagged words carry (epoch << 8) | layer
   // optional per-task trace: trace[gidx][4] = {start, inputs ready, end, meta}
   // (100 MHz wall clock; meta = opcode | workgroup << 8 | claimed items << 20 |
   //  (inputs staged - start) << 32 | (workers done - start) << 48, both in clock ticks)

@@ -47,6 +47,13 @@ __device__ __forceinline__ u32x4 ld_stream16(const GAS void* p) {
 __device__ __forceinline__ u32x2 ld_stream8(const GAS void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const GAS u32x2*>(p));
 }
+// Streaming 16-byte load of each lane straight into LDS (global_load_lds_dwordx4, no
+// registers involved): lane i's bytes land at lds + 16 * i, lds being wave-uniform.  The
+// load counts on the vector-memory counter like any other; the LDS bytes may be read once
+// the issuing wave has waited for it (only the issuing wave reads them here).
+__device__ __forceinline__ void dma16(const GAS void* p, LAS void* lds) {
+  __builtin_amdgcn_global_load_lds(p, lds, 16, 0, 2 /* nt */);
+}
 
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -189,6 +196,29 @@ __device__ __forceinline__ void st_pub4(GAS float* p, f32x4 v) {
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Tagged words.  Data that one workgroup produces and another consumes during the step
+// travels as 64-bit words: the fp32 payload in the low half and the step's epoch in the
+// high half, written with one agent-scope store (single-copy atomic, written through to
+// the device-coherent level).  A consumer reads the words with agent-scope loads and
+// retries those whose tag is not yet this step's: the data is its own ready flag, so an
+// edge costs the producer's store and the consumer's load, where a counter costs the
+// store, the wait for its completion, the atomic add, the counter poll, the acquire and
+// then the load.  The tag names the step and the layer, (epoch << 8) | layer, because
+// some buffers (the attention partials) are reused by every layer of a step; words left
+// from earlier layers or steps carry other tags.
+__device__ __forceinline__ uint32_t layer_tag(uint32_t epoch, int layer) { return (epoch << 8) | (uint32_t)layer; }
+__device__ __forceinline__ uint64_t tag_word(float v, uint32_t ep) {
+  return (uint64_t)__float_as_uint(v) | ((uint64_t)ep << 32);
+}
+__device__ __forceinline__ void st_tag(GAS uint64_t* p, float v, uint32_t ep) {
+  __hip_atomic_store(p, tag_word(v, ep), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tag(const GAS uint64_t* p) {
+  return __hip_atomic_load(const_cast<GAS uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_is(uint64_t w, uint32_t ep) { return (uint32_t)(w >> 32) == ep; }
+__device__ __forceinline__ float tag_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
 // Device view of the kernel parameters: the same fields, with address-space
 // qualified pointers.
 struct DParams {
@@ -213,9 +243,9 @@ struct DParams {
   GAS float* h;
   GAS float* ss;
   GAS float* q;
-  GAS float* attn_part;
-  GAS float* attn_o;
-  GAS float* router;
+  GAS uint64_t* attn_part;
+  GAS uint64_t* attn_o;
+  GAS uint64_t* router;
   GAS int32_t* topk_ids;
   GAS float* topk_w;
   GAS float* moe_act;
@@ -226,6 +256,7 @@ struct DParams {
   const CAS int32_t* cu_offsets;
   int32_t max_attn_items;
   int32_t spin_limit;
+  uint32_t epoch;
   GAS uint64_t* trace;
   int32_t trace_cap;
 };
@@ -267,7 +298,7 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.moe_act = gas(p.moe_act); d.inv_freq = cas(p.inv_freq);
   d.rope = gas(p.rope);
   d.counters = gas(p.counters); d.tasks = cas(p.tasks); d.cu_offsets = cas(p.cu_offsets);
-  d.max_attn_items = p.max_attn_items; d.spin_limit = p.spin_limit;
+  d.max_attn_items = p.max_attn_items; d.spin_limit = p.spin_limit; d.epoch = p.epoch;
   d.trace = gas(p.trace); d.trace_cap = p.trace_cap;
   return d;
 }

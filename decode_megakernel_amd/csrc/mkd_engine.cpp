@@ -65,6 +65,8 @@ struct mkd_engine {
   hipStream_t last_stream = nullptr;
   uint64_t* trace = nullptr;
   int32_t trace_cap = 0;
+  uint32_t epoch = 0;  // number of the last step, in [1, 2^24) (0: none yet; the workspace starts zeroed)
+  std::vector<std::pair<void*, size_t>> tagged;  // workspace buffers of tagged words
   ~mkd_engine() {
     if (device >= 0) {
       hipSetDevice(device);
@@ -168,13 +170,16 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
   const int64_t L = cfg->n_layers, B = max_batch, H = cfg->hidden, E = cfg->n_experts, K = cfg->top_k;
   const int64_t QD = (int64_t)cfg->n_q_heads * cfg->head_dim, hpg = cfg->n_q_heads / cfg->n_kv_heads;
   Params& p = e->base;
+  const size_t part_bytes = sizeof(uint64_t) * (size_t)e->max_attn_items * hpg * (cfg->head_dim + 2);
+  const size_t attn_o_bytes = sizeof(uint64_t) * L * B * QD;
+  const size_t router_bytes = sizeof(uint64_t) * L * B * E;
   std::vector<std::pair<size_t, void**>> slots = {
       {sizeof(float) * (L + 1) * B * H, (void**)&p.h},
       {sizeof(float) * (L + 1) * B * e->shape.n_rt, (void**)&p.ss},
       {sizeof(float) * L * B * QD, (void**)&p.q},
-      {sizeof(float) * (size_t)e->max_attn_items * hpg * (cfg->head_dim + 2), (void**)&p.attn_part},
-      {sizeof(float) * L * B * QD, (void**)&p.attn_o},
-      {sizeof(float) * L * B * E, (void**)&p.router},
+      {part_bytes, (void**)&p.attn_part},
+      {attn_o_bytes, (void**)&p.attn_o},
+      {router_bytes, (void**)&p.router},
       {sizeof(int32_t) * L * B * K, (void**)&p.topk_ids},
       {sizeof(float) * L * B * K, (void**)&p.topk_w},
       {sizeof(float) * L * B * K * cfg->moe_inter, (void**)&p.moe_act},
@@ -196,6 +201,7 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
     *s.second = (char*)e->ws + at;
     at += align256(s.first);
   }
+  e->tagged = {{p.attn_part, part_bytes}, {p.attn_o, attn_o_bytes}, {p.router, router_bytes}};
   rc = hipMemset(e->ws, 0, total);
   if (rc == hipSuccess) {
     std::vector<double> inv(cfg->head_dim / 2);
@@ -333,7 +339,18 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
   p.cu_offsets = dp->d_offsets;
   p.trace = e->trace;
   p.trace_cap = e->trace_cap;
+  // A fresh epoch per step (tagged words carry (epoch << 8) | layer).  Epoch 0 is never
+  // used, so zeroed words never read as ready; when the 24-bit epoch wraps, the tagged
+  // buffers are cleared first, so no word from 2^24 steps ago can pass for a new one.
   hipStream_t s = (hipStream_t)stream;
+  if (++e->epoch >= (1u << 24)) {
+    e->epoch = 1;
+    for (const auto& t : e->tagged) {
+      rc = launch_clear((uint32_t*)t.first, (int32_t)(t.second / 4), s);
+      if (rc != hipSuccess) return hip_fail(e, rc, "tag clear");
+    }
+  }
+  p.epoch = e->epoch;
   rc = launch_clear(p.counters, e->ctr.total, s);
   if (rc != hipSuccess) return hip_fail(e, rc, "counter clear");
   if (e->mode == MKD_MODE_MEGAKERNEL) {
@@ -394,22 +411,37 @@ int mkd_debug_read(mkd_engine* e, int32_t what, void* dst, size_t bytes) {
   if (e->device < 0) return fail(e, MKD_ERR_STATE, "host-only engine");
   const int64_t B = e->last_batch, L = e->cfg.n_layers, mb = e->max_batch;
   if (B < 1) return fail(e, MKD_ERR_STATE, "no step has run");
-  int64_t inner = 0, outer = 0;
+  int64_t inner = 0, outer = 0;  // inner: 4-byte values per (layer, token) row
   const char* src = nullptr;
+  bool tagged = false;  // the buffer holds tagged words: the value is each word's low half
   switch (what) {
-    case MKD_DEBUG_HIDDEN: inner = e->cfg.hidden * 4; outer = L + 1; src = (const char*)e->base.h; break;
-    case MKD_DEBUG_TOPK_IDS: inner = e->cfg.top_k * 4; outer = L; src = (const char*)e->base.topk_ids; break;
-    case MKD_DEBUG_TOPK_W: inner = e->cfg.top_k * 4; outer = L; src = (const char*)e->base.topk_w; break;
-    case MKD_DEBUG_ROUTER: inner = e->cfg.n_experts * 4; outer = L; src = (const char*)e->base.router; break;
+    case MKD_DEBUG_HIDDEN: inner = e->cfg.hidden; outer = L + 1; src = (const char*)e->base.h; break;
+    case MKD_DEBUG_TOPK_IDS: inner = e->cfg.top_k; outer = L; src = (const char*)e->base.topk_ids; break;
+    case MKD_DEBUG_TOPK_W: inner = e->cfg.top_k; outer = L; src = (const char*)e->base.topk_w; break;
+    case MKD_DEBUG_ROUTER:
+      inner = e->cfg.n_experts; outer = L; src = (const char*)e->base.router; tagged = true; break;
     default: return fail(e, MKD_ERR_ARG, "unknown debug buffer");
   }
-  if (bytes < (size_t)(outer * B * inner)) return fail(e, MKD_ERR_ARG, "debug buffer too small");
+  if (bytes < (size_t)(outer * B * inner * 4)) return fail(e, MKD_ERR_ARG, "debug buffer too small");
   hipError_t rc = hipSetDevice(e->device);
   if (rc == hipSuccess) rc = hipStreamSynchronize(e->last_stream);
   // one copy per layer row (a strided 2-D copy was seen to leave the destination
   // untouched under a profiler's interception)
-  for (int64_t o = 0; o < outer && rc == hipSuccess; ++o)
-    rc = hipMemcpy((char*)dst + o * B * inner, src + o * mb * inner, (size_t)(B * inner), hipMemcpyDeviceToHost);
+  const int64_t wb = tagged ? 8 : 4;  // bytes per stored word
+  std::vector<uint64_t> row(tagged ? (size_t)(B * inner) : 0);
+  for (int64_t o = 0; o < outer && rc == hipSuccess; ++o) {
+    char* d = (char*)dst + o * B * inner * 4;
+    const char* sp = src + o * mb * inner * wb;
+    if (!tagged) {
+      rc = hipMemcpy(d, sp, (size_t)(B * inner * 4), hipMemcpyDeviceToHost);
+    } else {
+      rc = hipMemcpy(row.data(), sp, (size_t)(B * inner * 8), hipMemcpyDeviceToHost);
+      for (int64_t i = 0; i < B * inner; ++i) {
+        const uint32_t v = (uint32_t)row[i];
+        std::memcpy(d + i * 4, &v, 4);
+      }
+    }
+  }
   if (rc != hipSuccess) return hip_fail(e, rc, "debug read");
   return MKD_OK;
 }

@@ -43,13 +43,14 @@ namespace mkd {
 
 // ------------------------------------------------------------------ LDS layout
 // One workgroup per CU is forced by the LDS footprint (> half of the 160 KB).  Each team
-// owns a region: activation staging / attention merge (xs), per-row results of a tile
-// (rowsum), routing tables (route) and controller state (misc).  One team of 8 waves has
-// 128 KB of xs (16 tokens x 2048 fp32); each of two teams of 4 waves has 44 KB (4 tokens).
+// owns a region: activation staging / attention pages and merge (xs), per-row results of a
+// tile (rowsum), routing tables (route) and controller state (misc).  One team of 8 waves
+// has 144 KB of xs (16 tokens x 2048 fp32 plus room for the attention pages held in LDS);
+// each of two teams of 4 waves has 44 KB (4 tokens).
 constexpr int kLdsRowsumBytes = 8192;
 constexpr int kLdsRouteBytes = 6144;
 constexpr int kLdsMiscBytes = 1024;
-constexpr int kXsBytes1 = 131072;
+constexpr int kXsBytes1 = 147456;
 constexpr int kXsBytes2 = 45056;
 constexpr int kTeamBytes1 = kXsBytes1 + kLdsRowsumBytes + kLdsRouteBytes + kLdsMiscBytes;
 constexpr int kTeamBytes2 = kXsBytes2 + kLdsRowsumBytes + kLdsRouteBytes + kLdsMiscBytes;
@@ -60,6 +61,7 @@ static_assert(2 * kTeamBytes2 <= kLdsBar, "two team regions must fit");
 #define MKD_MAXP 1
 #endif
 constexpr int kMaxPagesPerWave = MKD_MAXP;  // attention pages each worker holds in registers
+constexpr int kMaxLdsPages = 4;       // attention pages each worker prefetches into LDS
 constexpr int kMaccOffset = 640;      // MoE-down accumulator, floats after rowsum
 #ifndef MKD_RING
 #define MKD_RING 6
@@ -93,8 +95,8 @@ constexpr int MI_READY_LO = 6;   // trace: when the current task's first wait co
 constexpr int MI_READY_HI = 7;
 constexpr int MI_XS_LAYER = 8;   // layer whose normed input xs holds (-1: none)
 constexpr int MI_ROUTE_LAYER = 9;  // layer whose routing tables the route area holds (-1: none)
+constexpr int MI_WFAIL = 10;     // a worker's wait on tagged data gave up (the step is aborted)
 constexpr int MI_NEXT = 16;      // [2][2] claimed items (ping-pong): (item, task index) pairs
-constexpr int MI_OLD = 12;       // previous counter value of the last arrive
 constexpr int MI_T_STAGED = 14;  // trace: low 32 bits of the clock when inputs were staged
 constexpr int MI_T_DONE = 15;    // trace: low 32 bits of the clock when the workers finished
 constexpr int MI_TOK = 32;       // [16] token list of the current GEMV
@@ -264,7 +266,60 @@ __device__ __forceinline__ void ctl_set_ok(Ctx& c, bool ok) {
   if (c.lane == 0) c.s.mi[MI_OK] = ok ? 1 : 0;
 }
 __device__ __forceinline__ int32_t read_mi(Ctx& c, int slot) { return __builtin_amdgcn_readfirstlane(c.s.mi[slot]); }
-__device__ __forceinline__ bool read_ok(Ctx& c) { return read_mi(c, MI_OK) != 0; }
+__device__ __forceinline__ bool read_ok(Ctx& c) { return read_mi(c, MI_OK) != 0 && read_mi(c, MI_WFAIL) == 0; }
+
+// ------------------------------------------------------------------ tagged-data waits
+// Copy n tagged words into LDS, each thread of the team taking words tid, tid + tthreads,
+// ... in passes of W words: src(i) is the address of word i, dst(i) where its payload
+// goes.  A word whose tag is not this step's epoch is read again (after a short sleep)
+// until it is; the watchdog and the abort flag bound the wait.  No barrier inside: every
+// wave may call it with its share, and the caller synchronises the team.  On failure a
+// worker marks MI_WFAIL, so that the team leaves the task after its next barrier.
+template <int W, class Src, class Dst>
+__device__ __forceinline__ bool team_poll(const Ctx& c, uint32_t ep, int n, Src src, Dst dst) {
+  const DParams p = device_view(*c.kp);
+  bool ok = true;
+  for (int base = 0; base < n && ok; base += W * c.tthreads) {
+    uint64_t w[W];
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      const int i = base + c.tid + u * c.tthreads;
+      w[u] = i < n ? ld_tag(src(i)) : tag_word(0.0f, ep);
+    }
+    int32_t spins = 0;
+    while (true) {
+      bool ready = true;
+#pragma unroll
+      for (int u = 0; u < W; ++u) ready = ready && tag_is(w[u], ep);
+      if (ready) break;
+      if ((++spins & 63) == 0 && aborted(p)) { ok = false; break; }
+      if (spins > p.spin_limit) {
+        uint32_t seen = 0;
+#pragma unroll
+        for (int u = 0; u < W; ++u)
+          if (!tag_is(w[u], ep)) seen = (uint32_t)(w[u] >> 32);
+        report_error(p, 1u, c.task, G_TAGGED, seen, ep);
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        const int i = base + c.tid + u * c.tthreads;
+        if (!tag_is(w[u], ep)) w[u] = ld_tag(src(i));
+      }
+    }
+    if (ok) {
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        const int i = base + c.tid + u * c.tthreads;
+        if (i < n) dst(i) = tag_val(w[u]);
+      }
+    }
+  }
+  if (!ok && !c.ctl) c.s.mi[MI_WFAIL] = 1;
+  return ok;
+}
 
 // ------------------------------------------------------------------ GEMV tile (workers)
 // Weight rows of a tile: up to four segments of n1 rows each (the last may be shorter)
@@ -336,9 +391,14 @@ __device__ __forceinline__ uint32_t gemv_chunk_off(const Ctx& c, const RowSrc& s
 // addresses are a wave-uniform base plus a 32-bit lane offset), so the loop body is
 // straight-line and the wait-counter pass keeps kRing loads in flight.
 // rowsum[row * nb + j] = W[row] . x_j, x_j = xs + xo(row) + tok[j] * xld, rows < R.  NB bounds nb.
-template <int K, int NB, bool XSEG>
+// `stage` runs between the prefetch and the first barrier: the worker's share of a
+// team-wide wait on tagged inputs (a no-op when the controller stages alone).
+struct NoStage {
+  __device__ bool operator()() const { return true; }
+};
+template <int K, int NB, bool XSEG, class Stage>
 __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R, const LAS float* xs,
-                                          const LAS int32_t* tok, int nb, LAS float* rowsum) {
+                                          const LAS int32_t* tok, int nb, LAS float* rowsum, Stage stage) {
   using G = Gemv<K>;
   const int S = (R + G::RPS - 1) / G::RPS;
   const int ns = c.wi < S ? (S - c.wi + c.nw - 1) / c.nw : 0;
@@ -347,6 +407,7 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
   u32x4 ring[kRing];
 #pragma unroll
   for (int r = 0; r < kRing; ++r) ring[r] = ld_stream16(r < F ? (const GAS void*)(src.base + gemv_chunk_off<K>(c, src, r)) : (const GAS void*)dum);
+  stage();
   bar(c);
   if (!read_ok(const_cast<Ctx&>(c))) return false;
   float acc[NB];
@@ -395,11 +456,12 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
 }
 
 // XSEG: the segments of the tile read different activation blocks (output tasks).
-template <int K, bool XSEG = false>
+template <int K, bool XSEG = false, class Stage = NoStage>
 __device__ __forceinline__ bool worker_gemv(const Ctx& c, const RowSrc& src, int R, const LAS float* xs,
-                                            const LAS int32_t* tok, int nb, LAS float* rowsum) {
-  if (nb == 1) return gemv_tile<K, 1, XSEG>(c, src, R, xs, tok, nb, rowsum);
-  return gemv_tile<K, kMaxBatch, XSEG>(c, src, R, xs, tok, nb, rowsum);
+                                            const LAS int32_t* tok, int nb, LAS float* rowsum,
+                                            Stage stage = Stage()) {
+  if (nb == 1) return gemv_tile<K, 1, XSEG>(c, src, R, xs, tok, nb, rowsum, stage);
+  return gemv_tile<K, kMaxBatch, XSEG>(c, src, R, xs, tok, nb, rowsum, stage);
 }
 
 // Controller side of the same two barriers.  While the workers compute, a pending claim
@@ -597,7 +659,7 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
       const int r = i / B, b = i % B;
       const float v = c.s.rowsum[i] * c.s.mf[b];
       if (lm_head) st_pub(p.logits + (int64_t)b * p.vocab + r0 + r, v);
-      else st_pub(p.router + ((int64_t)l * p.max_batch + b) * p.n_experts + r0 + r, v);
+      else st_tag(p.router + ((int64_t)l * p.max_batch + b) * p.n_experts + r0 + r, v, layer_tag(p.epoch, l));
     }
     if (c.d[D_SIGNAL] >= 0) ctl_signal(c, p.counters + c.d[D_SIGNAL]);
   }
@@ -614,20 +676,52 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
 // Top-k of token b by one wave: k rounds of a wave argmax, each a DPP maximum of the
 // lanes' best remaining logits and a DPP minimum of the expert indices that reach it
 // (ties go to the lower index); lane 0 writes the ids and the softmax weights.
-__device__ __forceinline__ void route_load(const Ctx& c, const DParams& p, int l, int b, float (&v)[4]) {
+// Router logits of token b (lane e holds experts e, e + 64, ...), waited for on their tags.
+// With `once`, a single read: returns false unless every logit is already there.
+// Otherwise the read repeats until they are (false on abort or watchdog).
+__device__ __forceinline__ bool route_load(const Ctx& c, const DParams& p, int l, int b, float (&v)[4],
+                                           bool once = false) {
   const int E = p.n_experts;  // E <= 256
-  const GAS float* r = p.router + ((int64_t)l * p.max_batch + b) * E;
+  const uint32_t ep = layer_tag(p.epoch, l);
+  const GAS uint64_t* r = p.router + ((int64_t)l * p.max_batch + b) * E;
+  uint64_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = c.lane + 64 * i;
-    v[i] = e < E ? r[e] : -INFINITY;
+    w[i] = e < E ? ld_tag(r + e) : tag_word(-INFINITY, ep);
   }
+  int32_t spins = 0;
+  while (true) {
+    bool ready = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ready = ready && tag_is(w[i], ep);
+    const uint64_t pending = __ballot(!ready);
+    if (pending == 0) break;
+    if (once) return false;
+    if ((++spins & 63) == 0 && aborted(p)) return false;
+    if (spins > p.spin_limit) {
+      if (c.lane == __builtin_ctzll(pending)) report_error(p, 1u, c.task, G_TAGGED, (uint32_t)(w[0] >> 32), ep);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = c.lane + 64 * i;
+      if (!tag_is(w[i], ep)) w[i] = ld_tag(r + e);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = tag_val(w[i]);
+  return true;
 }
 __device__ __forceinline__ void route_select(const Ctx& c, const DParams& p, int b, float (&v)[4]) {
-  const int E = p.n_experts, k = p.top_k;
+  const int E = p.n_experts, k = p.top_k;  // k <= 16
   LAS int32_t* rt = c.s.route;
   LAS float* rw = reinterpret_cast<LAS float*>(rt + RT_W);
   const int lane = c.lane;
+  // round j leaves the j-th choice (logit, expert) in lane j's registers
+  float myv = -INFINITY;
+  int myid = 0;
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
@@ -641,35 +735,43 @@ __device__ __forceinline__ void route_select(const Ctx& c, const DParams& p, int
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (lane + 64 * i == BI) v[i] = -INFINITY;
-    if (lane == 0) {
-      rt[RT_IDS + b * 16 + j] = BI;
-      rw[b * 16 + j] = M;  // logit for now
+    if (lane == j) {
+      myv = M;
+      myid = BI;
     }
   }
-  if (lane == 0) {
-    const float sel_v0 = rw[b * 16];
-    float sum = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const float ex = expf(rw[b * 16 + j] - sel_v0);
-      rw[b * 16 + j] = ex;
-      sum += ex;
-    }
-    for (int j = 0; j < k; ++j) rw[b * 16 + j] /= sum;
+  // softmax over the k selected logits (lane j: choice j), the first choice being the max
+  const float v0 = lane_f(myv, 0);
+  const float ex = lane < k ? expf(myv - v0) : 0.0f;
+  const float sum = group_sum<16>(ex);  // lanes 0..15 hold the k choices
+  if (lane < k) {
+    rt[RT_IDS + b * 16 + lane] = myid;
+    rw[b * 16 + lane] = ex / sum;
   }
 }
 
 // Active experts (ascending) with their CSR offsets into the flat (token, slot) list, by
-// one wave: lane = expert of a 64-expert block; ballots give each active expert its rank
-// and the exclusive prefix of the entry counts (counts <= 16: five bit planes).
+// one wave: lane = expert of a 64-expert block; each lane counts its entries from the
+// entries' expert ids held in registers (read once, broadcast with readlane), and ballots
+// give each active expert its rank and the exclusive prefix of the entry counts (counts
+// <= 16: five bit planes).
 __device__ __forceinline__ void route_csr(const Ctx& c, const DParams& p) {
-  const int B = p.batch, E = p.n_experts, k = p.top_k;
+  const int B = p.batch, E = p.n_experts, k = p.top_k, n = B * k;  // n <= 256
   LAS int32_t* rt = c.s.route;
   const int lane = c.lane;
+  int ev[4];  // expert of entry lane + 64 q (entry t = b * k + j)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = lane + 64 * q;
+    ev[q] = t < n ? rt[RT_IDS + (t / k) * 16 + t % k] : -1;
+  }
   int n_act = 0, n_ent = 0;
   for (int blk = 0; blk < E; blk += 64) {
     const int e = blk + lane;
     int m = 0;
-    for (int t = 0; t < B * k; ++t) m += rt[RT_IDS + (t / k) * 16 + t % k] == e ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      for (int s = 0; s < min(64, n - 64 * q); ++s) m += __builtin_amdgcn_readlane(ev[q], s) == e ? 1 : 0;
     if (e >= E) m = 0;
     const uint64_t act = __ballot(m > 0);
     int pre = 0, tot = 0;
@@ -684,8 +786,10 @@ __device__ __forceinline__ void route_csr(const Ctx& c, const DParams& p) {
       int at = n_ent + pre;
       rt[RT_ACT + rank] = e;
       rt[RT_OFF + rank] = at;
-      for (int t = 0; t < B * k; ++t)
-        if (rt[RT_IDS + (t / k) * 16 + t % k] == e) rt[RT_FLAT + at++] = t;  // t = b * k + j
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        for (int s = 0; s < min(64, n - 64 * q); ++s)
+          if (__builtin_amdgcn_readlane(ev[q], s) == e) rt[RT_FLAT + at++] = 64 * q + s;  // t = b * k + j
     }
     n_act += __builtin_popcountll(act);
     n_ent += tot;
@@ -700,16 +804,25 @@ __device__ __forceinline__ void route_csr(const Ctx& c, const DParams& p) {
 // CSR by the first wave.  Called after a barrier that follows the controller's acquire of
 // the router counter; no wave has weight loads in flight here.  Tables already built for
 // layer l are kept; `write_debug` also stores the routing of every token for inspection.
-__device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
+__device__ __forceinline__ bool route_layer(Ctx& c, int l, bool write_debug) {
   const DParams p = device_view(*c.kp);
   const int B = p.batch, k = p.top_k;
   if (read_mi(c, MI_ROUTE_LAYER) != l) {
-    for (int b = c.tw; b < B; b += c.nw + 1) {
+    bool ok = true;
+    for (int b = c.tw; b < B && ok; b += c.nw + 1) {
       float v[4];
-      route_load(c, p, l, b, v);
-      route_select(c, p, b, v);
+      ok = route_load(c, p, l, b, v);
+#ifdef MKD_DIAG_RA
+      if (c.ctl && c.lane == 0 && c.s.mi[MI_T_STAGED] == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
+#endif
+      if (ok) route_select(c, p, b, v);
+#ifdef MKD_DIAG_RB
+      if (c.ctl && c.lane == 0 && c.s.mi[MI_T_STAGED] == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
+#endif
     }
+    if (!ok) c.s.mi[MI_WFAIL] = 1;
     bar(c);
+    if (read_mi(c, MI_WFAIL) != 0) return false;
     if (c.tw == 0) route_csr(c, p);
     // published before the barrier, so that every wave of the team sees the same value at
     // the next check (a task may start right after this one without another barrier)
@@ -723,6 +836,7 @@ __device__ __forceinline__ void route_layer(Ctx& c, int l, bool write_debug) {
     st_pub(p.topk_ids + ((int64_t)l * p.max_batch + b) * k + j, rt[RT_IDS + b * 16 + j]);
     st_pub(p.topk_w + ((int64_t)l * p.max_batch + b) * k + j, rw[b * 16 + j]);
   }
+  return true;
 }
 
 // The controller builds the tables of layer l alone, without barriers, when the router
@@ -734,15 +848,12 @@ constexpr int kRouteAhead = 8;
 __device__ __forceinline__ void ctl_route_ahead(Ctx& c, int l) {
   const DParams p = device_view(*c.kp);
   if (p.batch > kRouteAhead || read_mi(c, MI_ROUTE_LAYER) == l) return;
-  const int n_router_tiles = (p.n_experts + p.shape.router_rows - 1) / p.shape.router_rows;
-  uint32_t seen = 0;
-  if (c.lane == 0) seen = ctr_load(layer_ctr(p, l, p.ctr.router_done));
-  if (__shfl((int)seen, 0, 64) < n_router_tiles) return;
-  fence_acquire_agent();
   float v[kRouteAhead][4];
+  bool all = true;
 #pragma unroll
   for (int b = 0; b < kRouteAhead; ++b)
-    if (b < p.batch) route_load(c, p, l, b, v[b]);
+    if (b < p.batch && all) all = route_load(c, p, l, b, v[b], true);
+  if (!all) return;
 #pragma unroll
   for (int b = 0; b < kRouteAhead; ++b)
     if (b < p.batch) route_select(c, p, b, v[b]);
@@ -759,36 +870,186 @@ __device__ __forceinline__ int attn_item_count(const DParams& p) {
 }
 
 // ------------------------------------------------------------------ OP_MOE_UP (claimer)
-// Claims (active expert, tile of up_rows activation rows); weights = up_rows gate rows and
-// the matching up rows; epilogue silu(gate) * up for every token routed to the expert;
-// arrives on the expert's up counter.
+// Items are (active expert, tile of up_rows activation rows); weights = up_rows gate rows
+// and the matching up rows; epilogue silu(gate) * up for every token routed to the expert;
+// each item arrives on the expert's up counter.
+//
+// Static streaming (when at least kMinFreeClaimers claimers have no attention item): the
+// free claimers take the items round robin (free claimer f: items f, f + n_free, ...) and
+// stream all of them through one ring of weight loads that runs on from one item into the
+// next, so no item waits for its first loads; after each item the workers meet the
+// controller at a barrier, and the controller finishes that item (SiLU, stores, arrive)
+// while the workers compute the next one (rows sums double-buffered).  Claimers with an
+// attention item take no MoE-up item then.  Otherwise the shared queue of the pages'
+// design is drained (below).
+constexpr int kMinFreeClaimers = 64;
+constexpr int kRowsumHalf = 1024;  // floats: the two row-sum buffers of static streaming
+
+template <int K, int NB>
+__device__ __forceinline__ bool moe_up_static(Ctx& c, const DParams& p, int l, int fi, int n_free, int n_items) {
+  using G = Gemv<K>;
+  const int UR = p.shape.up_rows, NT = p.shape.n_up_tiles, I = p.inter, k = p.top_k;
+  const LAS int32_t* rt = c.s.route;
+  const int M = fi < n_items ? (n_items - fi + n_free - 1) / n_free : 0;
+  auto item_expert = [&](int m) { return __builtin_amdgcn_readfirstlane(rt[RT_ACT + (fi + m * n_free) / NT]); };
+  auto item_src = [&](int m) -> RowSrc {
+    const int tile = (fi + m * n_free) % NT;
+    const GAS uint16_t* base =
+        p.w_gate_up + (((int64_t)l * p.n_experts + item_expert(m)) * 2 * I + (int64_t)tile * UR) * p.hidden;
+    return row_src(base, base + (int64_t)I * p.hidden, p.hidden, UR);
+  };
+  if (!c.ctl) {
+    const int R = 2 * UR;
+    const int S = (R + G::RPS - 1) / G::RPS;
+    const int ns = c.wi < S ? (S - c.wi + c.nw - 1) / c.nw : 0;
+    const int F = ns * G::CPL;  // this worker's chunks per item
+    if (F == 0) {
+      for (int m = 0; m < M; ++m) bar(c);
+      return true;
+    }
+    const int FT = M * F;
+    const GAS u32x4* dum = reinterpret_cast<const GAS u32x4*>(gas(c.kp->dummy)) + c.lane;
+    // next load: chunk la_f of item la_m (a dummy line past the last item)
+    int la_m = 0, la_f = 0;
+    RowSrc sla = item_src(0);
+    auto next_addr = [&]() -> const GAS void* {
+      if (la_m >= M) return (const GAS void*)dum;
+      const GAS void* a = (const GAS void*)(sla.base + gemv_chunk_off<K>(c, sla, la_f));
+      if (++la_f == F) {
+        la_f = 0;
+        if (++la_m < M) sla = item_src(la_m);
+      }
+      return a;
+    };
+    u32x4 ring[kRing];
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) ring[r] = ld_stream16(next_addr());
+    // item being computed: m, its chunk f, tokens
+    int m = 0, f = 0, nb = 1;
+    float acc[NB];
+    int toff[NB];
+    auto setup_item = [&](int mm) {
+      const int a = (fi + mm * n_free) / NT;
+      const int o0 = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a]);
+      nb = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a + 1]) - o0;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        toff[j] = (NB == 1 || j < nb) ? __builtin_amdgcn_readfirstlane(rt[RT_FLAT + o0 + j] / k) * K : 0;
+        acc[j] = 0.0f;
+      }
+    };
+    setup_item(0);
+    for (int gb = 0; gb < FT; gb += kRing) {
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) {
+        const int g = gb + r;
+        const u32x4 w = ring[r];
+        ring[r] = ld_stream16(next_addr());
+        if (g < FT) {
+          const int cc = f % G::CPL;
+          const int kc = c.lane % G::LPR + G::LPR * cc;
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            if (NB == 1 || j < nb) {
+              const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(c.s.xs + toff[j] + kc * 8);
+              acc[j] += dot8(w, xp[0], xp[1]);
+            }
+            if (NB > 1 && (j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+          }
+          if (cc == G::CPL - 1) {
+            const int row = (c.wi + c.nw * (f / G::CPL)) * G::RPS + c.lane / G::LPR;
+            LAS float* rs = c.s.rowsum + (m & 1) * kRowsumHalf;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              if (NB == 1 || j < nb) {
+                const float t = group_sum<G::LPR>(acc[j]);
+                if (c.lane % G::LPR == 0 && row < R) rs[row * nb + j] = t;
+                acc[j] = 0.0f;
+              }
+            }
+          }
+          if (++f == F) {
+            // item m done on this worker: meet the controller, go on with the next item
+            // (its first loads are already in flight)
+            f = 0;
+            bar(c);
+            if (++m < M) setup_item(m);
+          }
+        }
+      }
+    }
+    return true;
+  } else {
+    if (c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
+    GAS uint32_t* pending = nullptr;
+    for (int m = 0; m < M; ++m) {
+      bar(c);
+      if (m == 0 && c.lane == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
+      if (pending) ctl_signal(c, pending);
+      const int idx = fi + m * n_free, a = idx / NT, tile = idx % NT;
+      const int o0 = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a]);
+      const int n_e = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a + 1]) - o0;
+      const LAS float* rs = c.s.rowsum + (m & 1) * kRowsumHalf;
+      for (int i = c.lane; i < UR * n_e; i += 64) {
+        const int r = i / n_e, jj = i % n_e;
+        const int slot = rt[RT_FLAT + o0 + jj];  // b * k + j
+        const float sc = c.s.mf[slot / k];
+        const float gt = rs[r * n_e + jj] * sc, u = rs[(UR + r) * n_e + jj] * sc;
+        const float act = gt / (1.0f + expf(-gt)) * u;
+        st_pub(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * I + (int64_t)tile * UR + r, act);
+      }
+      pending = layer_ctr(p, l, p.ctr.up_done + item_expert(m));
+      if (c.lane == 0) c.s.mi[MI_ITEMS] += 1;
+    }
+    if (pending) ctl_signal(c, pending);
+    return true;
+  }
+}
+
+// Shared-queue draining (the pages' MOE_UPGATE_ACT_DRAIN): claimer i of n takes item i
+// first when it had no attention item, then items from the queue.
 template <int K>
 __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   const DParams p = device_view(*c.kp);
   const int l = c.d[D_LAYER];
   const int UR = p.shape.up_rows, NT = p.shape.n_up_tiles, H = p.hidden, I = p.inter, k = p.top_k;
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.up_claim);
-  // Static first items go to the claimers that had no attention item in this step
-  // (claimer i of both queues runs on the same CU, attention first): claimer i >= n_attn
-  // takes item i - n_attn.  The others reach this task only after their attention item
-  // (or its combine) and start from the queue, whose items follow the static ones, so no
-  // late CU holds an item back.
+  const int n_attn = attn_item_count(p), ci = c.d[D_ARG0], n_cl = c.d[D_ARG1];
+  const bool stat = n_cl - n_attn >= kMinFreeClaimers;
+  if (stat && ci < n_attn) return true;  // busy with attention: no MoE-up item
+  // Queue mode: static first items go to the claimers that had no attention item in this
+  // step (claimer i of both queues runs on the same CU, attention first): claimer
+  // i >= n_attn takes item i - n_attn.  The others reach this task only after their
+  // attention item (or its combine) and start from the queue, whose items follow the
+  // static ones, so no late CU holds an item back.
   int n_static = 0;
+#ifdef MKD_DIAG_R0
+  if (c.ctl && c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
+#endif
   if (c.ctl) {
-    const int n_attn = attn_item_count(p), ci = c.d[D_ARG0];
-    n_static = max(0, c.d[D_ARG1] - n_attn);
-    // routing tables of layer l built ahead mean that the router wait is satisfied
-    const bool ok =
-        read_mi(c, MI_ROUTE_LAYER) == l || ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
-    if (ok) ctl_stage_x_normed(c, l);
-    ctl_claim_put(c, 0, ci >= n_attn ? (uint32_t)(ci - n_attn) : ctl_claim_issue(c, head, n_static));
+    n_static = max(0, n_cl - n_attn);
+    // the layer's normed input (normally still staged by this CU's QKV or router task)
+    bool ok = true;
+    if (read_mi(c, MI_XS_LAYER) != l) {
+      ok = ctl_wait(c, layer_ctr(p, l, p.ctr.x_ready), (uint32_t)p.shape.n_rt);
+      if (ok) ctl_stage_x_normed(c, l);
+    }
+    if (!stat) ctl_claim_put(c, 0, ci >= n_attn ? (uint32_t)(ci - n_attn) : ctl_claim_issue(c, head, n_static));
     ctl_set_ok(c, ok);
   }
   bar(c);
   if (!read_ok(c)) return false;
-  route_layer(c, l, c.d[D_ARG0] == 0);
+  // the first claimer that routes also stores the layer's routing for inspection
+  if (!route_layer(c, l, ci == (stat ? n_attn : 0))) return false;
+#ifdef MKD_DIAG_MOE
+  if (c.ctl && c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
+#endif
   const LAS int32_t* rt = c.s.route;
   const int n_items = __builtin_amdgcn_readfirstlane(rt[RT_NACT]) * NT;
+  if (stat) {
+    if (p.batch == 1) return moe_up_static<K, 1>(c, p, l, ci - n_attn, n_cl - n_attn, n_items);
+    return moe_up_static<K, kMaxBatch>(c, p, l, ci - n_attn, n_cl - n_attn, n_items);
+  }
   // the arrive of item j is completed while the workers compute item j + 1, so the
   // store round trip of its activations is off the workers' path
   GAS uint32_t* pending = nullptr;
@@ -857,13 +1118,7 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
   }
   // routing tables of layer l (normally left in LDS by this CU's MoE-up claimer)
   if (read_mi(c, MI_ROUTE_LAYER) != l) {
-    if (c.ctl) {
-      const int n_router_tiles = (E + p.shape.router_rows - 1) / p.shape.router_rows;
-      ctl_set_ok(c, ctl_wait(c, layer_ctr(p, l, p.ctr.router_done), (uint32_t)n_router_tiles));
-    }
-    bar(c);
-    if (!read_ok(c)) return false;
-    route_layer(c, l, false);
+    if (!route_layer(c, l, false)) return false;
   }
   // (1) O-proj: NSO * R rows of length KH; token groups that fit in LDS
   {
@@ -877,15 +1132,18 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
     const int TG = min(kMaxBatch, xs_floats / QD);
     for (int t0 = 0; t0 < B; t0 += TG) {
       const int nb = min(TG, B - t0);
+      // the combined attention of the group's tokens, waited for on its tags by every wave
+      const GAS uint64_t* asrc = p.attn_o + ((int64_t)l * p.max_batch + t0) * QD;
+      LAS float* xs = c.s.xs;
+      auto stage = [&]() {
+        return team_poll<8>(c, layer_tag(p.epoch, l), nb * QD, [&](int i) { return asrc + i; },
+                            [&](int i) -> LAS float& { return xs[i]; });
+      };
       if (!c.ctl) {
-        if (!worker_gemv<KH, true>(c, so, NSO * R, c.s.xs, c.s.mi + MI_TOK, nb, c.s.rowsum)) return false;
+        if (!worker_gemv<KH, true>(c, so, NSO * R, c.s.xs, c.s.mi + MI_TOK, nb, c.s.rowsum, stage)) return false;
       } else {
-        bool ok = true;
-        if (t0 == 0) ok = ctl_wait_lanes(c, layer_ctr(p, l, p.ctr.comb) + c.lane, p.n_kv, (uint32_t)B);
+        const bool ok = stage();
         if (ok) {
-          const GAS float* src = p.attn_o + ((int64_t)l * p.max_batch + t0) * QD;
-          for (int i = c.lane; i < nb * (QD / 4); i += 64)
-            *reinterpret_cast<LAS f32x4*>(c.s.xs + i * 4) = *reinterpret_cast<const GAS f32x4*>(src + i * 4);
           if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
           if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
         }
@@ -1042,16 +1300,22 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.attn_claim);
   const int nw = c.nw;
   // The attention buffers go after this layer's staged normed input when both fit, so
-  // the MoE-up claimer that follows on this CU finds the input still staged.
-  const int attn_floats = 16 * HD + 2 * nw * 16 + nw * 16 * HD + 16 * (HD + 2);
+  // the MoE-up claimer that follows on this CU finds the input still staged.  Each worker
+  // then owns a region for the pages it prefetches into LDS (as many as fit, up to
+  // kMaxLdsPages); its unnormalised outputs reuse the start of that region once its pages
+  // are consumed.
+  const int attn_fixed = 16 * HD + 2 * nw * 16 + 16 * (HD + 2);
   const int xs_floats = (nw == kWaves - 1 ? kXsBytes1 : kXsBytes2) / 4;
-  const int keep = p.batch * p.hidden + attn_floats <= xs_floats ? p.batch * p.hidden : 0;
+  const int keep = p.batch * p.hidden + attn_fixed + nw * hpg * HD <= xs_floats ? p.batch * p.hidden : 0;
+  const int page_floats = p.page * HD;  // K and V of one page, bf16
+  const int n_lds = min(kMaxLdsPages, (xs_floats - keep - attn_fixed) / nw / page_floats);
+  const int wstride = max(n_lds * page_floats, hpg * HD);
   LAS float* ab = c.s.xs + keep;
   LAS float* qs = ab;                                  // [hpg][HD] fp32 queries
   LAS float* mw = ab + 16 * HD;                        // [nw][16] running max per worker
   LAS float* lw = mw + nw * 16;                        // [nw][16] running sum
-  LAS float* ow = lw + nw * 16;                        // [nw][hpg][HD] unnormalised outputs
-  LAS float* part = ow + nw * 16 * HD;                 // [hpg][HD + 2] merged partial
+  LAS float* part = lw + nw * 16;                      // [hpg][HD + 2] merged partial
+  LAS float* wreg = part + 16 * (HD + 2);              // [nw][wstride] pages, then [hpg][HD] outputs
   bool waited = false;
   if (c.ctl) {
     ctl_claim_put(c, 0, (uint32_t)c.d[D_ARG0]);
@@ -1093,6 +1357,18 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
       for (int dt = 0; dt < NV; ++dt)
         vq[dt] = ld_stream8(p.kv_pool + vb + (dt * 16 + (c.lane & 15)) * 16 + (c.lane >> 4) * 4);
     };
+    // LDS copy of a page for slot s of this worker: K in the K operand's lane layout (1 KB
+    // per 32 dims, read back conflict-free), V verbatim (dim-major, as in the pool)
+    LAS char* wslot = reinterpret_cast<LAS char*>(wreg + (c.wi < 0 ? 0 : c.wi) * wstride);
+    auto dma_page = [&](int s, int64_t kb, int64_t vb) {
+      LAS char* dst = wslot + s * page_floats * 4;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        dma16(p.kv_pool + kb + (c.lane & 15) * HD + kk * 32 + (c.lane >> 4) * 8, dst + kk * 1024);
+#pragma unroll
+      for (int j = 0; j < NK; ++j) dma16(p.kv_pool + vb + j * 512 + c.lane * 8, dst + NK * 1024 + j * 1024);
+    };
+    int lpl[kMaxLdsPages];  // pages in this worker's LDS slots (c1: none)
     if (!c.ctl) {
 #pragma unroll
       for (int i = 0; i < MAXP; ++i) {
@@ -1101,6 +1377,20 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
         vbase[i] = 0;
         if (lp[i] < c1 && !page_base(lp[i], kbase[i], vbase[i])) lp[i] = c1;  // skip
         if (lp[i] < c1 && lp[i] != last) load_page(kr[i], vr[i], kbase[i], vbase[i]);
+      }
+      // the worker's next pages go to its LDS slots; the page holding the new token is
+      // copied after the wait
+#pragma unroll
+      for (int s = 0; s < kMaxLdsPages; ++s) {
+        lpl[s] = c1;
+        if (s < n_lds) {
+          const int lpg = c0 + c.wi + nw * (MAXP + s);
+          int64_t kb = 0, vb = 0;
+          if (lpg < c1 && page_base(lpg, kb, vb)) {
+            lpl[s] = lpg;
+            if (lpg != last) dma_page(s, kb, vb);
+          }
+        }
       }
     } else {
       bool ok = true;
@@ -1134,12 +1424,25 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     if (!read_ok(c)) return false;
     // the controller is idle until the merge: it builds this layer's routing tables for
     // the MoE-up claimer that follows on this CU
+#ifndef MKD_DIAG_NORA
     if (c.ctl) ctl_route_ahead(c, l);
+#endif
+#ifdef MKD_DIAG_A0
+    if (c.ctl && c.lane == 0 && j == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
+#endif
     if (!c.ctl) {
       // the page holding the new token is read after the wait (the acquire made it visible)
 #pragma unroll
       for (int i = 0; i < MAXP; ++i)
         if (lp[i] < c1 && lp[i] == last) load_page(kr[i], vr[i], kbase[i], vbase[i]);
+#pragma unroll
+      for (int s = 0; s < kMaxLdsPages; ++s) {
+        if (s < n_lds && lpl[s] == last) {
+          int64_t kb = 0, vb = 0;
+          page_base(last, kb, vb);
+          dma_page(s, kb, vb);
+        }
+      }
       // Q^T operand: lane holds head (lane & 15), dims kk*32 + (lane>>4)*8 + [0, 8)
       const int hq = c.lane & 15;
       const float qscale = 1.4426950408889634f / sqrtf((float)HD);
@@ -1195,8 +1498,23 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
 #pragma unroll
       for (int i = 0; i < MAXP; ++i)
         if (lp[i] < c1) do_page(kr[i], vr[i], lp[i]);
+      // pages in LDS: every copy this wave issued has landed after its own wait
+      if (n_lds > 0) wait_vm_all();
+#pragma unroll
+      for (int s = 0; s < kMaxLdsPages; ++s) {
+        if (s < n_lds && lpl[s] < c1) {
+          const LAS char* src = wslot + s * page_floats * 4;
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk) kr[0][kk] = *reinterpret_cast<const LAS u32x4*>(src + kk * 1024 + c.lane * 16);
+#pragma unroll
+          for (int dt = 0; dt < NV; ++dt)
+            vr[0][dt] = *reinterpret_cast<const LAS u32x2*>(src + NK * 1024 +
+                                                           ((dt * 16 + (c.lane & 15)) * 16 + (c.lane >> 4) * 4) * 2);
+          do_page(kr[0], vr[0], lpl[s]);
+        }
+      }
       // further pages of this worker stream through the first page's registers
-      for (int lpg = c0 + c.wi + nw * MAXP; lpg < c1; lpg += nw) {
+      for (int lpg = c0 + c.wi + nw * (MAXP + n_lds); lpg < c1; lpg += nw) {
         int64_t kb = 0, vb = 0;
         if (!page_base(lpg, kb, vb)) continue;
         load_page(kr[0], vr[0], kb, vb);
@@ -1207,13 +1525,17 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
         lw[c.wi * 16 + c.lane] = lsum;
       }
       if (hq < hpg) {
+        LAS float* ow = reinterpret_cast<LAS float*>(wslot);
 #pragma unroll
         for (int dt = 0; dt < NV; ++dt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ow[(c.wi * hpg + hq) * HD + dt * 16 + (c.lane >> 4) * 4 + r] = o[dt][r];
+          for (int r = 0; r < 4; ++r) ow[hq * HD + dt * 16 + (c.lane >> 4) * 4 + r] = o[dt][r];
       }
     }
     bar(c);
+#ifdef MKD_DIAG_A1
+    if (c.ctl && c.lane == 0 && j == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
+#endif
     // merge the workers: unnormalised o, running max M and sum L per head (all waves)
     for (int t = c.tid; t < hpg * HD; t += c.tthreads) {
       const int h = t / HD, dd = t % HD;
@@ -1222,7 +1544,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
       float acc = 0.0f, L = 0.0f;
       for (int ww = 0; ww < nw; ++ww) {
         const float sc = exp2f(mw[ww * 16 + h] - M);
-        acc += sc * ow[(ww * hpg + h) * HD + dd];
+        acc += sc * wreg[ww * wstride + h * HD + dd];
         L += sc * lw[ww * 16 + h];
       }
       part[h * (HD + 2) + dd] = acc;
@@ -1235,65 +1557,63 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     // the merge give it time to arrive (the next item's index is read after the next barriers)
     if (c.ctl) ctl_claim_put(c, (j + 1) & 1, nxt);
     bar(c);
+    // the item's partial (o, m, l per head) leaves as tagged words: no counter, no wait
     if (c.ctl) {
-      GAS float* dst = p.attn_part + (int64_t)idx * hpg * (HD + 2);
-      for (int i = c.lane; i < hpg * (HD + 2); i += 64) st_pub(dst + i, part[i]);
-      const uint32_t old = ctl_arrive(c, layer_ctr(p, l, p.ctr.attn_items + b * nkv + g));
-      if (c.lane == 0) c.s.mi[MI_OLD] = (int32_t)old;
-      // trace: "done" = the last item's partial published (a combine follows it or not)
-      if (c.lane == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
+      GAS uint64_t* dst = p.attn_part + (int64_t)idx * hpg * (HD + 2);
+      for (int i = c.lane; i < hpg * (HD + 2); i += 64) st_tag(dst + i, part[i], layer_tag(p.epoch, l));
+      // trace: "done" = the first item's partial stored
+      if (c.lane == 0 && c.s.mi[MI_T_DONE] == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
     }
-    bar(c);
-    if ((uint32_t)read_mi(c, MI_OLD) + 1 == (uint32_t)nchunks) {
-      // last item of (b, g): combine all chunks (log-sum-exp merge, chunk order fixed):
-      // per head the global max M and 1 / sum_c 2^(m_c - M) l_c, then the weighted sum
-      // of the chunks' unnormalised outputs.
-      fence_acquire_agent();
-      const GAS float* pb = p.attn_part + (int64_t)base_bg * hpg * (HD + 2);
-      LAS float* mrow = ab;       // [hpg] inverse denominators
-      LAS float* mmax = ab + 16;  // [hpg] maxima
-      for (int h = c.tw; h < hpg; h += nw + 1) {
-        float M = -INFINITY;
-        for (int ci = c.lane; ci < nchunks; ci += 64) M = fmaxf(M, pb[((int64_t)ci * hpg + h) * (HD + 2) + HD]);
-        M = wave_max(M);
-        float den = 0.0f;
-        for (int ci = c.lane; ci < nchunks; ci += 64) {
-          const GAS float* pc = pb + ((int64_t)ci * hpg + h) * (HD + 2);
-          den += exp2f(pc[HD] - M) * pc[HD + 1];
-        }
-        den = group_sum<64>(den);
-        if (c.lane == 0) {
-          mrow[h] = 1.0f / den;
-          mmax[h] = M;
+  }
+  // Combine (ATTN_COMBINE): query head qh of sequence b is merged by claimer
+  // (b * n_q + qh) mod n_claimers once it has left the queue.  Every item is claimed by
+  // then, so the partials it waits for are being computed or stored.  The chunks of
+  // (b, kv group) are staged in LDS in batches (their tags waited for by every wave), then
+  // thread d merges dimension d over the chunks in order (online log-sum-exp, base 2);
+  // the result leaves as tagged words for the output tasks.
+  {
+    const int n_cl = c.d[D_ARG1], ci = c.d[D_ARG0];
+    const int n_duty = p.batch * p.n_q;
+    LAS float* stg = wreg;
+    const int CB = max(1, min(64, nw * wstride / (HD + 2)));  // chunks per staged batch
+    for (int dj = ci; dj < n_duty; dj += n_cl) {
+      const int b = dj / p.n_q, qh = dj % p.n_q, g = qh / hpg, h = qh % hpg;
+      int base_bg = 0, nch = 0;
+      for (int bb = 0; bb <= b; ++bb) {
+        const int nit = (p.seq_lens[bb] / p.page + 1 + ppi - 1) / ppi;
+        if (bb == b) {
+          base_bg += g * nit;
+          nch = nit;
+        } else {
+          base_bg += nit * nkv;
         }
       }
-      bar(c);
-      for (int t = c.tid; t < hpg * (HD / 4); t += c.tthreads) {
-        const int h = t / (HD / 4), d4 = (t % (HD / 4)) * 4;
-        const float M = mmax[h];
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int cb = 0; cb < nchunks; cb += 8) {
-          f32x4 v[8];
-          float mc[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            v[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-            mc[jj] = -INFINITY;
-            if (cb + jj < nchunks) {
-              const GAS float* pc = pb + ((int64_t)(cb + jj) * hpg + h) * (HD + 2);
-              v[jj] = *reinterpret_cast<const GAS f32x4*>(pc + d4);
-              mc[jj] = pc[HD];
-            }
+      float M = -INFINITY, den = 0.0f, acc = 0.0f;
+      for (int cb0 = 0; cb0 < nch; cb0 += CB) {
+        const int ncb = min(CB, nch - cb0);
+        const GAS uint64_t* src = p.attn_part + ((int64_t)(base_bg + cb0) * hpg + h) * (HD + 2);
+        const int64_t cstride = (int64_t)hpg * (HD + 2);
+        const bool ok = team_poll<8>(
+            c, layer_tag(p.epoch, l), ncb * (HD + 2), [&](int i) { return src + (i / (HD + 2)) * cstride + i % (HD + 2); },
+            [&](int i) -> LAS float& { return stg[i]; });
+        if (c.ctl) ctl_set_ok(c, ok);
+        bar(c);
+        if (!read_ok(c)) return false;
+        if (c.tid < HD) {
+          for (int k = 0; k < ncb; ++k) {
+            const float mk = stg[k * (HD + 2) + HD], lk = stg[k * (HD + 2) + HD + 1];
+            const float mn = fmaxf(M, mk);
+            const float sa = exp2f(M - mn), sb = exp2f(mk - mn);
+            den = den * sa + lk * sb;
+            acc = acc * sa + stg[k * (HD + 2) + c.tid] * sb;
+            M = mn;
           }
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) acc += exp2f(mc[jj] - M) * v[jj];
         }
-        GAS float* dst = p.attn_o + ((int64_t)l * p.max_batch + b) * p.n_q * HD + (int64_t)(g * hpg + h) * HD + d4;
-        st_pub4(dst, acc * mrow[h]);
+        bar(c);
       }
-      wait_vm_all();
-      bar(c);
-      if (c.ctl) ctl_signal(c, layer_ctr(p, l, p.ctr.comb + g));
+      if (c.tid < HD)
+        st_tag(p.attn_o + ((int64_t)l * p.max_batch + b) * p.n_q * HD + (int64_t)qh * HD + c.tid, acc / den,
+               layer_tag(p.epoch, l));
     }
   }
   return true;
@@ -1341,12 +1661,22 @@ MKD_EXEC(exec_embed, return op_embed(c);)
 MKD_EXEC(exec_qkv, return op_qkv<G::kHidden>(c);)
 MKD_EXEC(exec_router, return op_rows_on_x<G::kHidden>(c, false);)
 MKD_EXEC(exec_lm_head, return op_rows_on_x<G::kHidden>(c, true);)
+#ifdef MKD_DIAG_R1
+MKD_EXEC(exec_moe_up, if (c.ctl && c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64(); return op_moe_up<G::kHidden>(c);)
+#else
 MKD_EXEC(exec_moe_up, return op_moe_up<G::kHidden>(c);)
+#endif
 MKD_EXEC(exec_out, return (op_out<G::kHidden, G::kInter>(c));)
 MKD_EXEC(exec_attn, return op_attn<G::kHd>(c);)
 
 template <class G>
 __device__ __forceinline__ bool run_task(KParams* kp, LAS char* lds, const CAS int32_t* d, int32_t task, int32_t team) {
+#ifdef MKD_DIAG_R2
+  if (d[D_OPCODE] == OP_MOE_UP && (int)threadIdx.x == 0) {
+    Smem sm(lds, 0, 1);
+    sm.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
+  }
+#endif
   switch (d[D_OPCODE]) {
     case OP_EMBED: return exec_embed<G>(kp, lds, d, task, team);
     case OP_QKV: return exec_qkv<G>(kp, lds, d, task, team);
@@ -1392,6 +1722,7 @@ __device__ __forceinline__ void init_team_state(LAS int32_t* mi, bool leader) {
     mi[MI_WAIT_TGT] = 0;
     mi[MI_XS_LAYER] = -1;
     mi[MI_ROUTE_LAYER] = -1;
+    mi[MI_WFAIL] = 0;
     for (int k = 0; k < 4; ++k) mi[MI_NEXT + k] = -1;
   }
 }
@@ -1433,10 +1764,22 @@ __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params prm) {
     asm volatile("" : "+s"(kpv));
     KParams* kpt = (KParams*)kpv;
     const CAS int32_t* d = cas(kpt->tasks) + (int64_t)t * D_WORDS;
+    // The next task's descriptor is touched now with a vector load, so that its scalar
+    // loads at the next task's start find it in L2: a scalar miss that goes to HBM queues
+    // behind the weight streams for microseconds.  The value is only consumed (waited
+    // for) after this task.
+#ifndef MKD_NO_DESC_PREFETCH
+    int32_t dpre = 0;
+    if (t + 1 < end && (threadIdx.x & 63) < 2)
+      dpre = gas(kpt->tasks)[(int64_t)(t + 1) * D_WORDS + 16 * (threadIdx.x & 1)];
+#endif
     reset_task_state(mi, leader);
     const uint64_t t0 = kpt->trace ? wall_clock64() : 0;
     const bool ok = run_task<G>(kpt, lds, d, t, team);
     trace_task(kpt, mi, d, t0, leader, list);
+#ifndef MKD_NO_DESC_PREFETCH
+    asm volatile("" ::"v"(dpre));
+#endif
     if (!ok) break;
   }
 }

@@ -144,8 +144,9 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
           break;
         case W_ROUTER:
           for (int r0 = 0; r0 < g.n_experts; r0 += o.router_rows)
+            // logits leave as tagged words (no counter): consumers wait on the data itself
             em.emit(OP_ROUTER, l, r0, std::min(o.router_rows, g.n_experts - r0), 0, 0, L(l, c.x_ready), s.n_rt,
-                    L(l, c.router_done));
+                    -1);
           break;
         case W_ATTN:
           for (int i = 0; i < n_attn; ++i)
@@ -153,7 +154,7 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
           break;
         case W_MOE_UP:
           for (int i = 0; i < n_up; ++i)
-            em.emit(OP_MOE_UP, l, i, n_up, 0, 0, L(l, c.router_done), n_router_tiles, -1);
+            em.emit(OP_MOE_UP, l, i, n_up, 0, 0, -1, 0, -1);
           break;
         case W_OUT:
           // waits inside the task: the combined attention of every KV group, then the up
@@ -244,16 +245,24 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
              ") waits for " + std::to_string(d[D_TARGET]) + " arrivals on counter " + std::to_string(d[D_WAIT]) +
              " but only " + std::to_string(avail) + " producers precede it";
   }
-  // Output tasks wait inside the task on the combine counters (attention claimers) and
-  // the experts' up counters (MoE-up claimers): both waves precede the output wave.
+  // Edges carried by tagged data (no counter): the router logits (MoE-up claimers and
+  // output tasks read them), the attention partials and combined output (output tasks),
+  // and the experts' activations (output tasks).  Their producers' waves precede their
+  // consumers' waves in the global order.
   for (int l = 0; l < g.n_layers; ++l) {
-    int attn_end = -1, up_end = -1, out_first = -1;
+    int router_end = -1, up_first = -1, attn_end = -1, up_end = -1, out_first = -1;
     for (const Wave& w : P.waves)
       if (w.layer == l) {
+        if (w.kind == W_ROUTER) router_end = w.first + w.count;
         if (w.kind == W_ATTN) attn_end = w.first + w.count;
-        if (w.kind == W_MOE_UP) up_end = w.first + w.count;
+        if (w.kind == W_MOE_UP) {
+          up_first = w.first;
+          up_end = w.first + w.count;
+        }
         if (w.kind == W_OUT) out_first = w.first;
       }
+    if (router_end < 0 || up_first < router_end)
+      return "layer " + std::to_string(l) + ": the MoE-up wave must follow the router wave";
     if (attn_end < 0 || up_end < 0 || out_first < 0 || out_first < attn_end || out_first < up_end)
       return "layer " + std::to_string(l) + ": the output wave must follow the attention and MoE-up waves";
   }
