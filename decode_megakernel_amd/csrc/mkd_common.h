@@ -121,17 +121,17 @@ struct Params {
   uint16_t* kv_pool;
   float* logits;
   // workspace (fp32 unless noted)
-  float* h;           // [L+1][maxB][H]
-  float* ss;          // [L+1][maxB][n_rt] per-row-tile sum of squares
+  uint64_t* h;        // [L+1][maxB][H] tagged
+  uint64_t* ss;       // [L+1][maxB][n_rt] tagged per-row-tile sums of squares
   float* q;           // [L][maxB][nq*hd] post-RoPE queries
   uint64_t* attn_part;  // [max_items][hpg][hd + 2] tagged: unnormalised o, then m, l
   uint64_t* attn_o;     // [L][maxB][nq*hd] tagged
   uint64_t* router;   // [L][maxB][E] tagged
   int32_t* topk_ids;  // [L][maxB][k]
   float* topk_w;      // [L][maxB][k]
-  float* moe_act;     // [L][maxB*k][I]
+  uint64_t* moe_act;  // [L][maxB*k][I] tagged
   const double* inv_freq;  // [hd/2] RoPE frequencies base^(-2i/hd), fp64
-  float* rope;             // [maxB][hd/2][2] cos, sin of this step's positions
+  uint64_t* rope;          // [maxB][hd/2][2] tagged cos, sin of this step's positions
   const void* dummy;       // 1 KB of zeros: target of the GEMV ring's idle slots
   uint32_t* counters;
   // task lists

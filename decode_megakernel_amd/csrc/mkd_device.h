@@ -240,17 +240,17 @@ struct DParams {
   const CAS int32_t* page_table;
   GAS uint16_t* kv_pool;
   GAS float* logits;
-  GAS float* h;
-  GAS float* ss;
+  GAS uint64_t* h;
+  GAS uint64_t* ss;
   GAS float* q;
   GAS uint64_t* attn_part;
   GAS uint64_t* attn_o;
   GAS uint64_t* router;
   GAS int32_t* topk_ids;
   GAS float* topk_w;
-  GAS float* moe_act;
+  GAS uint64_t* moe_act;
   const CAS double* inv_freq;
-  GAS float* rope;
+  GAS uint64_t* rope;
   GAS uint32_t* counters;
   const CAS int32_t* tasks;
   const CAS int32_t* cu_offsets;

@@ -95,6 +95,7 @@ std::string check_config(const mkd_config& c, int32_t max_batch, int32_t max_pag
   if (c.n_layers < 1 || c.hidden < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 ||
       c.n_experts < 1 || c.top_k < 1 || c.moe_inter < 1 || c.vocab < 1 || c.page_size < 1)
     return "all dimensions must be positive";
+  if (c.n_layers > 254) return "at most 254 layers (tagged words carry the layer in 8 bits)";
   if (c.n_q_heads % c.n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
   if (c.n_q_heads / c.n_kv_heads > 16) return "at most 16 query heads per KV group";
   if (geometry_index(c.hidden, c.moe_inter, c.head_dim) < 0)
@@ -173,18 +174,22 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
   const size_t part_bytes = sizeof(uint64_t) * (size_t)e->max_attn_items * hpg * (cfg->head_dim + 2);
   const size_t attn_o_bytes = sizeof(uint64_t) * L * B * QD;
   const size_t router_bytes = sizeof(uint64_t) * L * B * E;
+  const size_t act_bytes = sizeof(uint64_t) * L * B * K * cfg->moe_inter;
+  const size_t h_bytes = sizeof(uint64_t) * (L + 1) * B * H;
+  const size_t ss_bytes = sizeof(uint64_t) * (L + 1) * B * e->shape.n_rt;
+  const size_t rope_bytes = sizeof(uint64_t) * B * cfg->head_dim;
   std::vector<std::pair<size_t, void**>> slots = {
-      {sizeof(float) * (L + 1) * B * H, (void**)&p.h},
-      {sizeof(float) * (L + 1) * B * e->shape.n_rt, (void**)&p.ss},
+      {h_bytes, (void**)&p.h},
+      {ss_bytes, (void**)&p.ss},
       {sizeof(float) * L * B * QD, (void**)&p.q},
       {part_bytes, (void**)&p.attn_part},
       {attn_o_bytes, (void**)&p.attn_o},
       {router_bytes, (void**)&p.router},
       {sizeof(int32_t) * L * B * K, (void**)&p.topk_ids},
       {sizeof(float) * L * B * K, (void**)&p.topk_w},
-      {sizeof(float) * L * B * K * cfg->moe_inter, (void**)&p.moe_act},
+      {act_bytes, (void**)&p.moe_act},
       {sizeof(double) * cfg->head_dim / 2, (void**)&p.inv_freq},
-      {sizeof(float) * B * cfg->head_dim, (void**)&p.rope},
+      {rope_bytes, (void**)&p.rope},
       {1024, (void**)&p.dummy},
       {sizeof(uint32_t) * (size_t)e->ctr.total, (void**)&p.counters},
   };
@@ -201,7 +206,8 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
     *s.second = (char*)e->ws + at;
     at += align256(s.first);
   }
-  e->tagged = {{p.attn_part, part_bytes}, {p.attn_o, attn_o_bytes}, {p.router, router_bytes}};
+  e->tagged = {{p.attn_part, part_bytes}, {p.attn_o, attn_o_bytes}, {p.router, router_bytes},
+               {p.moe_act, act_bytes}, {p.h, h_bytes}, {p.ss, ss_bytes}, {p.rope, rope_bytes}};
   rc = hipMemset(e->ws, 0, total);
   if (rc == hipSuccess) {
     std::vector<double> inv(cfg->head_dim / 2);
@@ -415,7 +421,8 @@ int mkd_debug_read(mkd_engine* e, int32_t what, void* dst, size_t bytes) {
   const char* src = nullptr;
   bool tagged = false;  // the buffer holds tagged words: the value is each word's low half
   switch (what) {
-    case MKD_DEBUG_HIDDEN: inner = e->cfg.hidden; outer = L + 1; src = (const char*)e->base.h; break;
+    case MKD_DEBUG_HIDDEN:
+      inner = e->cfg.hidden; outer = L + 1; src = (const char*)e->base.h; tagged = true; break;
     case MKD_DEBUG_TOPK_IDS: inner = e->cfg.top_k; outer = L; src = (const char*)e->base.topk_ids; break;
     case MKD_DEBUG_TOPK_W: inner = e->cfg.top_k; outer = L; src = (const char*)e->base.topk_w; break;
     case MKD_DEBUG_ROUTER:

@@ -275,16 +275,21 @@ __device__ __forceinline__ bool read_ok(Ctx& c) { return read_mi(c, MI_OK) != 0 
 // until it is; the watchdog and the abort flag bound the wait.  No barrier inside: every
 // wave may call it with its share, and the caller synchronises the team.  On failure a
 // worker marks MI_WFAIL, so that the team leaves the task after its next barrier.
-template <int W, class Src, class Dst>
-__device__ __forceinline__ bool team_poll(const Ctx& c, uint32_t ep, int n, Src src, Dst dst) {
+struct NoScale {
+  __device__ float operator()(int) const { return 1.0f; }
+};
+template <int W, class Src, class Dst, class Scale = NoScale>
+__device__ __forceinline__ bool team_poll(const Ctx& c, uint32_t ep, int n, Src src, Dst dst, Scale scale = Scale()) {
   const DParams p = device_view(*c.kp);
   bool ok = true;
   for (int base = 0; base < n && ok; base += W * c.tthreads) {
     uint64_t w[W];
+    float sc[W];  // plain (read-only) factors, loaded together with the tagged words
 #pragma unroll
     for (int u = 0; u < W; ++u) {
       const int i = base + c.tid + u * c.tthreads;
       w[u] = i < n ? ld_tag(src(i)) : tag_word(0.0f, ep);
+      sc[u] = i < n ? scale(i) : 0.0f;
     }
     int32_t spins = 0;
     while (true) {
@@ -313,7 +318,7 @@ __device__ __forceinline__ bool team_poll(const Ctx& c, uint32_t ep, int n, Src 
 #pragma unroll
       for (int u = 0; u < W; ++u) {
         const int i = base + c.tid + u * c.tthreads;
-        if (i < n) dst(i) = tag_val(w[u]);
+        if (i < n) dst(i) = tag_val(w[u]) * sc[u];
       }
     }
   }
@@ -467,12 +472,17 @@ __device__ __forceinline__ bool worker_gemv(const Ctx& c, const RowSrc& src, int
 // Controller side of the same two barriers.  While the workers compute, a pending claim
 // reply (next_entry >= 0) is stored to its claim entry and a deferred arrive (the
 // previous item's results, already stored) is completed on `flush`.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+template <class Hook = NoHook>
 __device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_entry = -1, uint32_t claim = 0,
-                                                  GAS uint32_t* flush = nullptr) {
+                                                  GAS uint32_t* flush = nullptr, Hook after_first = Hook()) {
   ctl_set_ok(c, ok);
   if (c.lane == 0 && c.s.mi[MI_T_STAGED] == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
   bar(c);
-  if (!ok) return false;
+  if (!read_ok(c)) return false;
+  after_first();
   if (next_entry >= 0) ctl_claim_put(c, next_entry, claim);
   if (flush) ctl_signal(c, flush);
   bar(c);
@@ -480,59 +490,41 @@ __device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_entr
   return true;
 }
 
-// ------------------------------------------------------------------ activation staging (controller)
-// xs[b][k] = h_l[b][k] * gamma_l[k] and mf[b] = inv_rms_b for every token of the batch:
+// ------------------------------------------------------------------ activation staging (team)
+// xs[b][k] = h_l[b][k] * gamma_l[k] for every token of the batch, and mf[b] = inv_rms_b:
 // the RMSNorm that every consumer of layer l's input applies, with the per-token scale
-// moved to the consumer's epilogue (row sums times mf[token]) so that staging is one
-// round trip: the per-row-tile sums of squares (written when the residual rows were
-// finalised) are loaded together with h and gamma.  The staged vector is kept while the
-// next tasks on this CU read the same layer's input.
-__device__ __forceinline__ void ctl_stage_x_normed(Ctx& c, int l) {
-  if (read_mi(c, MI_XS_LAYER) == l) return;
+// moved to the consumer's epilogue (row sums times mf[token]).  Every wave of the team
+// waits for its share of the tagged residual rows and of the per-row-tile sums of squares
+// (staged behind x, at xs + B * H) and writes x; after the task's first barrier the
+// controller reduces the sums of squares into mf (stage_x_finish).  The staged vector is
+// kept while the next tasks on this CU read the same layer's input (MI_XS_LAYER, set by
+// the controller after that barrier, so that every wave of this task saw the old value).
+// Returns false on abort / watchdog; `fresh` tells whether this call staged.
+__device__ __forceinline__ bool team_stage_x(const Ctx& c, int l, bool& fresh) {
+  fresh = read_mi(const_cast<Ctx&>(c), MI_XS_LAYER) != l;
+  if (!fresh) return true;
   const DParams p = device_view(*c.kp);
-  const int B = p.batch, H = p.hidden, NRT = p.shape.n_rt;  // NRT <= 256
-  // per token, its NRT partial sums: lane r < NRT holds tile r (four per lane); the load
-  // addresses are clamped into the token's row so the loads need no branch
-  float part[16];
-#pragma unroll
-  for (int b = 0; b < 16; ++b) {
-    float t = 0.0f;
-    if (b < B) {
-      const GAS float* row = p.ss + ((int64_t)l * p.max_batch + b) * NRT;
-      float v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = row[min(c.lane + 64 * q, NRT - 1)];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) t += c.lane + 64 * q < NRT ? v[q] : 0.0f;
-    }
-    part[b] = t;
-  }
+  const int B = p.batch, H = p.hidden, NRT = p.shape.n_rt, nh = B * H;  // NRT <= 256
+  const GAS uint64_t* hb = p.h + (int64_t)l * p.max_batch * H;
+  const GAS uint64_t* sb = p.ss + (int64_t)l * p.max_batch * NRT;
   const GAS uint16_t* gamma = p.norm + (int64_t)l * H;
-  const int n8 = B * (H / 8);
-#pragma unroll 4
-  for (int i = c.lane; i < n8; i += 64) {
-    const int b = i / (H / 8), k8 = (i % (H / 8)) * 8;
-    const GAS float* hp = p.h + ((int64_t)l * p.max_batch + b) * H + k8;
-    const f32x4 h0 = *reinterpret_cast<const GAS f32x4*>(hp);
-    const f32x4 h1 = *reinterpret_cast<const GAS f32x4*>(hp + 4);
-    const u32x4 gw = *reinterpret_cast<const GAS u32x4*>(gamma + k8);
-    f32x4 o0, o1;
-    o0.x = h0.x * bf_lo(gw.x); o0.y = h0.y * bf_hi(gw.x);
-    o0.z = h0.z * bf_lo(gw.y); o0.w = h0.w * bf_hi(gw.y);
-    o1.x = h1.x * bf_lo(gw.z); o1.y = h1.y * bf_hi(gw.z);
-    o1.z = h1.z * bf_lo(gw.w); o1.w = h1.w * bf_hi(gw.w);
-    LAS float* xo = c.s.xs + b * H + k8;
-    *reinterpret_cast<LAS f32x4*>(xo) = o0;
-    *reinterpret_cast<LAS f32x4*>(xo + 4) = o1;
+  LAS float* xs = c.s.xs;
+  return team_poll<5>(
+      c, layer_tag(p.epoch, l), nh + B * NRT, [&](int i) { return i < nh ? hb + i : sb + (i - nh); },
+      [&](int i) -> LAS float& { return xs[i]; },
+      [&](int i) { return i < nh ? bf16_to_f32(gamma[i % H]) : 1.0f; });
+}
+__device__ __forceinline__ void stage_x_finish(Ctx& c, int l, bool fresh) {
+  if (!fresh) return;
+  const DParams p = device_view(*c.kp);
+  const int B = p.batch, H = p.hidden, NRT = p.shape.n_rt;
+  const LAS float* ssx = c.s.xs + B * H;
+  for (int b = 0; b < B; ++b) {
+    float t = 0.0f;
+    for (int r = c.lane; r < NRT; r += 64) t += ssx[b * NRT + r];
+    t = group_sum<64>(t);
+    if (c.lane == 0) c.s.mf[b] = 1.0f / sqrtf(t / (float)H + p.rms_eps);
   }
-#pragma unroll
-  for (int b = 0; b < 16; ++b) {
-    if (b < B) {
-      const float t = group_sum<64>(part[b]);
-      if (c.lane == 0) c.s.mf[b] = 1.0f / sqrtf(t / (float)H + p.rms_eps);
-    }
-  }
-  if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
   if (c.lane == 0) c.s.mi[MI_XS_LAYER] = l;
 }
 
@@ -554,25 +546,24 @@ __device__ __forceinline__ bool op_embed(Ctx& c) {
       tok = 0;
     }
     const float v = bf16_to_f32(p.embed[(int64_t)tok * H + r]);
-    st_pub(p.h + (int64_t)b * H + r, v);
+    st_tag(p.h + (int64_t)b * H + r, v, layer_tag(p.epoch, 0));
     red[i] = v * v;
   }
   for (int b = 0; b < B; ++b) {
     float t = 0.0f;
     for (int r = c.lane; r < R; r += 64) t += red[b * R + r];
     t = group_sum<64>(t);
-    if (c.lane == 0) st_pub(p.ss + (int64_t)b * p.shape.n_rt + rt, t);
+    if (c.lane == 0) st_tag(p.ss + (int64_t)b * p.shape.n_rt + rt, t, layer_tag(p.epoch, 0));
   }
   if (rt == 0) {
     const int half = p.head_dim / 2;
     for (int i = c.lane; i < B * half; i += 64) {
       const int b = i / half, k = i % half;
       const double ang = (double)p.seq_lens[b] * p.inv_freq[k];
-      st_pub(p.rope + 2 * i, (float)cos(ang));
-      st_pub(p.rope + 2 * i + 1, (float)sin(ang));
+      st_tag(p.rope + 2 * i, (float)cos(ang), layer_tag(p.epoch, 0));
+      st_tag(p.rope + 2 * i + 1, (float)sin(ang), layer_tag(p.epoch, 0));
     }
   }
-  ctl_signal(c, layer_ctr(p, 0, p.ctr.x_ready));
   return true;
 }
 
@@ -588,25 +579,38 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
   const int hd = p.head_dim, half = hd / 2, H = p.hidden, B = p.batch;
   const GAS uint16_t* wl = p.w_qkv + (int64_t)l * (p.n_q + 2 * p.n_kv) * hd * H;
   const RowSrc src = row_src(wl + ((int64_t)hh * hd + j0) * H, wl + ((int64_t)hh * hd + half + j0) * H, H, PB);
+  bool fresh = false;
+  auto stage = [&]() { return team_stage_x(c, l, fresh); };
   if (!c.ctl) {
-    return worker_gemv<K>(c, src, 2 * PB, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum);
+    return worker_gemv<K>(c, src, 2 * PB, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum, stage);
   } else {
-    const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
-    if (ok) ctl_stage_x_normed(c, l);
-    // the epilogue's first (cos, sin) pair per lane is loaded while the workers compute
     const bool rope_head = hh < p.n_q + p.n_kv;
-    f32x2 cs0 = f32x2{1.0f, 0.0f};
-    if (ok && rope_head && c.lane < PB * B)
-      cs0 = *reinterpret_cast<const GAS f32x2*>(p.rope + ((int64_t)(c.lane % B) * half + j0 + c.lane / B) * 2);
-    if (!ctl_gemv_barriers(c, ok)) return false;
+    // the epilogue's first (cos, sin) pair per lane (tagged by the embedding task) is read
+    // before the staging, so that it arrives while the workers compute
+    uint64_t cw0 = 0, sw0 = 0;
+    const GAS uint64_t* rope0 = p.rope + ((int64_t)(c.lane % B) * half + j0 + c.lane / B) * 2;
+    if (rope_head && c.lane < PB * B) {
+      cw0 = ld_tag(rope0);
+      sw0 = ld_tag(rope0 + 1);
+    }
+    const bool ok = stage();
+    if (ok && c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
+    if (!ctl_gemv_barriers(c, ok, -1, 0, nullptr, [&]() { stage_x_finish(c, l, fresh); })) return false;
+    const uint32_t ep0 = layer_tag(p.epoch, 0);
     for (int i = c.lane; i < PB * B; i += 64) {
       const int r = i / B, b = i % B, dim = j0 + r;
       const float a = c.s.rowsum[r * B + b] * c.s.mf[b], bb = c.s.rowsum[(PB + r) * B + b] * c.s.mf[b];
       const int pos = p.seq_lens[b];
       float o1 = a, o2 = bb;
       if (rope_head) {
-        const f32x2 csn = i == c.lane ? cs0 : *reinterpret_cast<const GAS f32x2*>(p.rope + ((int64_t)b * half + dim) * 2);
-        const float cs = csn.x, sn = csn.y;
+        const GAS uint64_t* rp = p.rope + ((int64_t)b * half + dim) * 2;
+        uint64_t cw = i == c.lane ? cw0 : ld_tag(rp), sw = i == c.lane ? sw0 : ld_tag(rp + 1);
+        while (!tag_is(cw, ep0) || !tag_is(sw, ep0)) {  // written long before (embedding task)
+          __builtin_amdgcn_s_sleep(1);
+          cw = ld_tag(rp);
+          sw = ld_tag(rp + 1);
+        }
+        const float cs = tag_val(cw), sn = tag_val(sw);
         o1 = a * cs - bb * sn;
         o2 = bb * cs + a * sn;
       }
@@ -649,12 +653,14 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
   const int H = p.hidden, B = p.batch;
   const GAS uint16_t* base = lm_head ? p.embed + (int64_t)r0 * H : p.w_router + ((int64_t)l * p.n_experts + r0) * H;
   const RowSrc src = row_src(base, base, H, R);
+  bool fresh = false;
+  auto stage = [&]() { return team_stage_x(c, l, fresh); };
   if (!c.ctl) {
-    return worker_gemv<K>(c, src, R, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum);
+    return worker_gemv<K>(c, src, R, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum, stage);
   } else {
-    const bool ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
-    if (ok) ctl_stage_x_normed(c, l);
-    if (!ctl_gemv_barriers(c, ok)) return false;
+    const bool ok = stage();
+    if (ok && c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
+    if (!ctl_gemv_barriers(c, ok, -1, 0, nullptr, [&]() { stage_x_finish(c, l, fresh); })) return false;
     for (int i = c.lane; i < R * B; i += 64) {
       const int r = i / B, b = i % B;
       const float v = c.s.rowsum[i] * c.s.mf[b];
@@ -981,11 +987,9 @@ __device__ __forceinline__ bool moe_up_static(Ctx& c, const DParams& p, int l, i
     return true;
   } else {
     if (c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
-    GAS uint32_t* pending = nullptr;
     for (int m = 0; m < M; ++m) {
       bar(c);
       if (m == 0 && c.lane == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
-      if (pending) ctl_signal(c, pending);
       const int idx = fi + m * n_free, a = idx / NT, tile = idx % NT;
       const int o0 = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a]);
       const int n_e = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a + 1]) - o0;
@@ -996,12 +1000,11 @@ __device__ __forceinline__ bool moe_up_static(Ctx& c, const DParams& p, int l, i
         const float sc = c.s.mf[slot / k];
         const float gt = rs[r * n_e + jj] * sc, u = rs[(UR + r) * n_e + jj] * sc;
         const float act = gt / (1.0f + expf(-gt)) * u;
-        st_pub(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * I + (int64_t)tile * UR + r, act);
+        st_tag(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * I + (int64_t)tile * UR + r, act,
+               layer_tag(p.epoch, l));
       }
-      pending = layer_ctr(p, l, p.ctr.up_done + item_expert(m));
       if (c.lane == 0) c.s.mi[MI_ITEMS] += 1;
     }
-    if (pending) ctl_signal(c, pending);
     return true;
   }
 }
@@ -1026,19 +1029,18 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
 #ifdef MKD_DIAG_R0
   if (c.ctl && c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
 #endif
+  // the layer's normed input (normally still staged by this CU's QKV or router task)
+  bool fresh = false;
+  const bool staged = team_stage_x(c, l, fresh);
+  if (!staged && !c.ctl) c.s.mi[MI_WFAIL] = 1;
   if (c.ctl) {
     n_static = max(0, n_cl - n_attn);
-    // the layer's normed input (normally still staged by this CU's QKV or router task)
-    bool ok = true;
-    if (read_mi(c, MI_XS_LAYER) != l) {
-      ok = ctl_wait(c, layer_ctr(p, l, p.ctr.x_ready), (uint32_t)p.shape.n_rt);
-      if (ok) ctl_stage_x_normed(c, l);
-    }
     if (!stat) ctl_claim_put(c, 0, ci >= n_attn ? (uint32_t)(ci - n_attn) : ctl_claim_issue(c, head, n_static));
-    ctl_set_ok(c, ok);
+    ctl_set_ok(c, staged);
   }
   bar(c);
   if (!read_ok(c)) return false;
+  if (c.ctl) stage_x_finish(c, l, fresh);
   // the first claimer that routes also stores the layer's routing for inspection
   if (!route_layer(c, l, ci == (stat ? n_attn : 0))) return false;
 #ifdef MKD_DIAG_MOE
@@ -1050,9 +1052,6 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
     if (p.batch == 1) return moe_up_static<K, 1>(c, p, l, ci - n_attn, n_cl - n_attn, n_items);
     return moe_up_static<K, kMaxBatch>(c, p, l, ci - n_attn, n_cl - n_attn, n_items);
   }
-  // the arrive of item j is completed while the workers compute item j + 1, so the
-  // store round trip of its activations is off the workers' path
-  GAS uint32_t* pending = nullptr;
   for (int j = 0;; ++j) {
     const int idx = read_claim(c, j & 1);
     if (idx >= n_items) break;
@@ -1067,20 +1066,19 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
     } else {
       if (c.lane < n_e) c.s.mi[MI_TOK + c.lane] = rt[RT_FLAT + o0 + c.lane] / k;
       const uint32_t nxt = ctl_claim_issue(c, head, n_static);
-      if (!ctl_gemv_barriers(c, true, (j + 1) & 1, nxt, pending)) return false;
+      if (!ctl_gemv_barriers(c, true, (j + 1) & 1, nxt)) return false;
       for (int i = c.lane; i < UR * n_e; i += 64) {
         const int r = i / n_e, jj = i % n_e;
         const int slot = rt[RT_FLAT + o0 + jj];  // b * k + j
         const float sc = c.s.mf[slot / k];
         const float gt = c.s.rowsum[r * n_e + jj] * sc, u = c.s.rowsum[(UR + r) * n_e + jj] * sc;
         const float act = gt / (1.0f + expf(-gt)) * u;
-        st_pub(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * I + (int64_t)tile * UR + r, act);
+        st_tag(p.moe_act + ((int64_t)l * p.max_batch * k + slot) * I + (int64_t)tile * UR + r, act,
+               layer_tag(p.epoch, l));
       }
-      pending = layer_ctr(p, l, p.ctr.up_done + e);
       if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
     }
   }
-  if (c.ctl && pending) ctl_signal(c, pending);
   return true;
 }
 
@@ -1106,13 +1104,15 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
   LAS float* acc_a = c.s.rowsum + kMaccOffset;  // [R][B] O-proj rows
   LAS float* acc_m = acc_a + R * kMaxBatch;     // [R][B] expert rows
   const int64_t hstride = (int64_t)p.max_batch * H;
-  // this tile's residual rows of layer l, loaded now and used at the end
-  float hold[2];
+  // this tile's residual rows of layer l (tagged), read now and checked at the end
+  const uint32_t ep = layer_tag(p.epoch, l);
+  uint64_t hold[2];
+  auto hold_src = [&](int i) { return p.h + (int64_t)l * hstride + (int64_t)(i % B) * H + r0 + i / B; };
   if (c.ctl) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = c.lane + 64 * u;
-      hold[u] = i < R * B ? p.h[(int64_t)l * hstride + (int64_t)(i % B) * H + r0 + i / B] : 0.0f;
+      hold[u] = i < R * B ? ld_tag(hold_src(i)) : tag_word(0.0f, ep);
     }
     for (int i = c.lane; i < 2 * R * kMaxBatch; i += 64) acc_a[i] = 0.0f;
   }
@@ -1178,42 +1178,25 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
       sd.xstep = KI; sd.xsh = 31 - __builtin_clz(R);
       sd.eids = rtab + RT_ACT + a0; sd.escale = (uint32_t)(H * KI);
       sd.xtab = rtab + RT_OFF + a0; sd.xbase = ob0;
+      // activation rows of the group's (expert, token) entries in CSR order, waited for on
+      // their tags by every wave: row r (entry ob0 + r) goes to xs + r * KI
+      const int n_rows = __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a0 + na]) - ob0;
+      const GAS uint64_t* abase = p.moe_act + (int64_t)l * p.max_batch * k * KI;
+      LAS float* xs = c.s.xs;
+      auto stage = [&]() {
+        return team_poll<12>(
+            c, layer_tag(p.epoch, l), n_rows * KI,
+            [&](int i) { return abase + (int64_t)rtab[RT_FLAT + ob0 + i / KI] * KI + i % KI; },
+            [&](int i) -> LAS float& { return xs[i]; });
+      };
       if (!c.ctl) {
-        if (!worker_gemv<KI, true>(c, sd, na * R, c.s.xs, c.s.mi + MI_TOK, nb, c.s.rowsum)) return false;
+        if (!worker_gemv<KI, true>(c, sd, na * R, c.s.xs, c.s.mi + MI_TOK, nb, c.s.rowsum, stage)) return false;
       } else {
-        GAS uint32_t* up = layer_ctr(p, l, p.ctr.up_done);
-        const int my_e = c.lane < na ? rtab[RT_ACT + a0 + c.lane] : 0;
-        const bool ok = ctl_wait_lanes(c, up + my_e, na, (uint32_t)p.shape.n_up_tiles);
-        // trace: an output task's "staged" time is when its first expert group's up tiles
-        // were all done, its "done" time when its last GEMV finished
+        const bool ok = stage();
+        // trace: an output task's "staged" time is when its first expert group's
+        // activations were in LDS, its "done" time when its last GEMV finished
         if (c.lane == 0 && a0 == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
         if (ok) {
-          // activation rows of the group's (expert, token) entries, in CSR order; the
-          // loads of eight rows are all issued before their LDS stores
-          const int n_rows = __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a0 + na]) - ob0;
-          constexpr int QL = (KI / 4 + 63) / 64;  // 16-byte pieces per lane per row
-          for (int r0 = 0; r0 < n_rows; r0 += 8) {
-            f32x4 buf[8][QL];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int r = r0 + u;
-              const int slot = r < n_rows ? rtab[RT_FLAT + ob0 + r] : 0;
-              const GAS float* src = p.moe_act + ((int64_t)l * p.max_batch * k + slot) * KI;
-#pragma unroll
-              for (int q = 0; q < QL; ++q) {
-                const int k4 = (c.lane + 64 * q) * 4;
-                if (r < n_rows && k4 < KI) buf[u][q] = *reinterpret_cast<const GAS f32x4*>(src + k4);
-              }
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-#pragma unroll
-              for (int q = 0; q < QL; ++q) {
-                const int k4 = (c.lane + 64 * q) * 4;
-                if (r0 + u < n_rows && k4 < KI) *reinterpret_cast<LAS f32x4*>(c.s.xs + (r0 + u) * KI + k4) = buf[u][q];
-              }
-            }
-          }
           if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
           if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
         }
@@ -1233,25 +1216,39 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
       }
     }
   }
-  // (3) h_{l+1}[rows] = h_l + a + m and the tile's sums of squares
+  // (3) h_{l+1}[rows] = h_l + a + m and the tile's sums of squares, as tagged words (the
+  // next layer's consumers wait on them)
   if (c.ctl) {
+    // the residual rows read at the start were written long before (previous layer's
+    // output tasks, before any task of this layer could start); re-read any not yet seen
+    int32_t spins = 0;
+    while (__ballot(!tag_is(hold[0], ep) || !tag_is(hold[1], ep)) != 0) {
+      if (++spins > p.spin_limit) {
+        report_error(p, 1u, c.task, G_TAGGED, (uint32_t)(hold[0] >> 32), ep);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (!tag_is(hold[u], ep)) hold[u] = ld_tag(hold_src(c.lane + 64 * u));
+    }
+    const uint32_t ep1 = layer_tag(p.epoch, l + 1);
     LAS float* red = c.s.rowsum;  // [B][R] squares
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = c.lane + 64 * u;
       if (i < R * B) {
         const int r = i / B, b = i % B;
-        const float v = hold[u] + acc_a[r * kMaxBatch + b] + acc_m[r * kMaxBatch + b];
-        st_pub(p.h + (int64_t)(l + 1) * hstride + (int64_t)b * H + r0 + r, v);
+        const float v = tag_val(hold[u]) + acc_a[r * kMaxBatch + b] + acc_m[r * kMaxBatch + b];
+        st_tag(p.h + (int64_t)(l + 1) * hstride + (int64_t)b * H + r0 + r, v, ep1);
         red[b * R + r] = v * v;
       }
     }
     if (c.lane < B) {
       float t = 0.0f;
       for (int r = 0; r < R; ++r) t += red[c.lane * R + r];
-      st_pub(p.ss + ((int64_t)(l + 1) * p.max_batch + c.lane) * p.shape.n_rt + rt, t);
+      st_tag(p.ss + ((int64_t)(l + 1) * p.max_batch + c.lane) * p.shape.n_rt + rt, t, ep1);
     }
-    ctl_signal(c, p.counters + c.d[D_SIGNAL]);
   }
   return true;
 }

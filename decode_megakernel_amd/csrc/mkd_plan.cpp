@@ -128,7 +128,8 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   const int n_up = o.n_up_claimers > 0 ? o.n_up_claimers : n_cu;
 
   begin_wave(-1, 0);
-  for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_EMBED, 0, rt, 0, 0, 0, -1, 0, L(0, c.x_ready));
+  // residual rows, their sums of squares and the RoPE table leave as tagged words
+  for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_EMBED, 0, rt, 0, 0, 0, -1, 0, -1);
   end_wave();
   for (int l = 0; l < g.n_layers; ++l) {
     for (int wi = 0; wi < W_KINDS; ++wi) {
@@ -139,14 +140,13 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
           for (int hh = 0; hh < n_qkv_heads; ++hh)
             for (int t = 0; t < qkv_tph; ++t) {
               const int j0 = t * half / qkv_tph, j1 = (t + 1) * half / qkv_tph;
-              em.emit(OP_QKV, l, hh, j0, j1 - j0, 0, L(l, c.x_ready), s.n_rt, L(l, c.qkv_done));
+              em.emit(OP_QKV, l, hh, j0, j1 - j0, 0, -1, 0, L(l, c.qkv_done));
             }
           break;
         case W_ROUTER:
           for (int r0 = 0; r0 < g.n_experts; r0 += o.router_rows)
             // logits leave as tagged words (no counter): consumers wait on the data itself
-            em.emit(OP_ROUTER, l, r0, std::min(o.router_rows, g.n_experts - r0), 0, 0, L(l, c.x_ready), s.n_rt,
-                    -1);
+            em.emit(OP_ROUTER, l, r0, std::min(o.router_rows, g.n_experts - r0), 0, 0, -1, 0, -1);
           break;
         case W_ATTN:
           for (int i = 0; i < n_attn; ++i)
@@ -159,7 +159,7 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
         case W_OUT:
           // waits inside the task: the combined attention of every KV group, then the up
           // tiles of every active expert (dynamic: routing decides the experts)
-          for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_OUT, l, rt, 0, 0, 0, -1, 0, L(l + 1, c.x_ready));
+          for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_OUT, l, rt, 0, 0, 0, -1, 0, -1);
           break;
         default:
           return "bad wave order";
@@ -169,8 +169,7 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   }
   begin_wave(-2, g.n_layers);
   for (int r0 = 0; r0 < g.vocab; r0 += o.lm_rows)
-    em.emit(OP_LM_HEAD, g.n_layers, r0, std::min(o.lm_rows, g.vocab - r0), 0, 0, L(g.n_layers, c.x_ready), s.n_rt,
-            -1);
+    em.emit(OP_LM_HEAD, g.n_layers, r0, std::min(o.lm_rows, g.vocab - r0), 0, 0, -1, 0, -1);
   end_wave();
 
   // Deal the tasks round robin, keeping global order within each list.  One team: task k
@@ -263,8 +262,25 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
       }
     if (router_end < 0 || up_first < router_end)
       return "layer " + std::to_string(l) + ": the MoE-up wave must follow the router wave";
+    // the layer's input: the previous layer's output wave (the embedding wave for layer 0)
+    // precedes every task of the layer
+    int prev_end = -1, first = -1;
+    for (const Wave& w : P.waves) {
+      if ((l == 0 && w.kind == -1) || (l > 0 && w.layer == l - 1 && w.kind == W_OUT)) prev_end = w.first + w.count;
+      if (w.layer == l && w.kind >= 0 && (first < 0 || w.first < first)) first = w.first;
+    }
+    if (prev_end < 0 || first < prev_end)
+      return "layer " + std::to_string(l) + ": its tasks must follow the previous layer's output wave";
     if (attn_end < 0 || up_end < 0 || out_first < 0 || out_first < attn_end || out_first < up_end)
       return "layer " + std::to_string(l) + ": the output wave must follow the attention and MoE-up waves";
+  }
+  {
+    int last_out_end = -1, lm_first = -1;
+    for (const Wave& w : P.waves) {
+      if (w.layer == g.n_layers - 1 && w.kind == W_OUT) last_out_end = w.first + w.count;
+      if (w.kind == -2 && w.count > 0) lm_first = w.first;
+    }
+    if (lm_first >= 0 && lm_first < last_out_end) return "the LM-head wave must follow the last output wave";
   }
   // every list in increasing global order, every task in exactly one list
   if ((int)P.cu_offsets.size() != P.n_cu * P.n_teams + 1) return "wrong number of task lists";
