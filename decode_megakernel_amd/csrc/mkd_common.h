@@ -85,6 +85,9 @@ enum GlobalCounter : int32_t {
   G_COUNT = 8,
 };
 
+// Words of one layer's published routing table (the LDS routing area's layout).
+constexpr int32_t kRouteTableWords = 1548;
+
 // ---------------------------------------------------------------- plan constants
 struct PlanShape {
   int32_t n_rt;            // residual row tiles (hidden / rt_rows)
@@ -127,6 +130,7 @@ struct Params {
   uint64_t* attn_part;  // [max_items][hpg][hd + 2] tagged: unnormalised o, then m, l
   uint64_t* attn_o;     // [L][maxB][nq*hd] tagged
   uint64_t* router;   // [L][maxB][E] tagged
+  uint64_t* route_tbl;  // [L][route words] tagged routing tables (built once per layer)
   int32_t* topk_ids;  // [L][maxB][k]
   float* topk_w;      // [L][maxB][k]
   uint64_t* moe_act;  // [L][maxB*k][I] tagged

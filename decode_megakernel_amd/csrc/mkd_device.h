@@ -246,6 +246,7 @@ struct DParams {
   GAS uint64_t* attn_part;
   GAS uint64_t* attn_o;
   GAS uint64_t* router;
+  GAS uint64_t* route_tbl;
   GAS int32_t* topk_ids;
   GAS float* topk_w;
   GAS uint64_t* moe_act;
@@ -294,7 +295,7 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.tokens = cas(p.tokens); d.seq_lens = cas(p.seq_lens); d.page_table = cas(p.page_table);
   d.kv_pool = gas(p.kv_pool); d.logits = gas(p.logits);
   d.h = gas(p.h); d.ss = gas(p.ss); d.q = gas(p.q); d.attn_part = gas(p.attn_part); d.attn_o = gas(p.attn_o);
-  d.router = gas(p.router); d.topk_ids = gas(p.topk_ids); d.topk_w = gas(p.topk_w);
+  d.router = gas(p.router); d.route_tbl = gas(p.route_tbl); d.topk_ids = gas(p.topk_ids); d.topk_w = gas(p.topk_w);
   d.moe_act = gas(p.moe_act); d.inv_freq = cas(p.inv_freq);
   d.rope = gas(p.rope);
   d.counters = gas(p.counters); d.tasks = cas(p.tasks); d.cu_offsets = cas(p.cu_offsets);

@@ -174,6 +174,7 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
   const size_t part_bytes = sizeof(uint64_t) * (size_t)e->max_attn_items * hpg * (cfg->head_dim + 2);
   const size_t attn_o_bytes = sizeof(uint64_t) * L * B * QD;
   const size_t router_bytes = sizeof(uint64_t) * L * B * E;
+  const size_t tbl_bytes = sizeof(uint64_t) * L * kRouteTableWords;
   const size_t act_bytes = sizeof(uint64_t) * L * B * K * cfg->moe_inter;
   const size_t h_bytes = sizeof(uint64_t) * (L + 1) * B * H;
   const size_t ss_bytes = sizeof(uint64_t) * (L + 1) * B * e->shape.n_rt;
@@ -185,6 +186,7 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
       {part_bytes, (void**)&p.attn_part},
       {attn_o_bytes, (void**)&p.attn_o},
       {router_bytes, (void**)&p.router},
+      {tbl_bytes, (void**)&p.route_tbl},
       {sizeof(int32_t) * L * B * K, (void**)&p.topk_ids},
       {sizeof(float) * L * B * K, (void**)&p.topk_w},
       {act_bytes, (void**)&p.moe_act},
@@ -206,7 +208,7 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
     *s.second = (char*)e->ws + at;
     at += align256(s.first);
   }
-  e->tagged = {{p.attn_part, part_bytes}, {p.attn_o, attn_o_bytes}, {p.router, router_bytes},
+  e->tagged = {{p.attn_part, part_bytes}, {p.attn_o, attn_o_bytes}, {p.router, router_bytes}, {p.route_tbl, tbl_bytes},
                {p.moe_act, act_bytes}, {p.h, h_bytes}, {p.ss, ss_bytes}, {p.rope, rope_bytes}};
   rc = hipMemset(e->ws, 0, total);
   if (rc == hipSuccess) {

@@ -48,7 +48,7 @@ namespace mkd {
 // has 144 KB of xs (16 tokens x 2048 fp32 plus room for the attention pages held in LDS);
 // each of two teams of 4 waves has 44 KB (4 tokens).
 constexpr int kLdsRowsumBytes = 8192;
-constexpr int kLdsRouteBytes = 6144;
+constexpr int kLdsRouteBytes = 6400;
 constexpr int kLdsMiscBytes = 1024;
 constexpr int kXsBytes1 = 147456;
 constexpr int kXsBytes2 = 45056;
@@ -61,7 +61,10 @@ static_assert(2 * kTeamBytes2 <= kLdsBar, "two team regions must fit");
 #define MKD_MAXP 1
 #endif
 constexpr int kMaxPagesPerWave = MKD_MAXP;  // attention pages each worker holds in registers
-constexpr int kMaxLdsPages = 4;       // attention pages each worker prefetches into LDS
+#ifndef MKD_LDS_PAGES
+#define MKD_LDS_PAGES 4
+#endif
+constexpr int kMaxLdsPages = MKD_LDS_PAGES;  // attention pages each worker prefetches into LDS
 constexpr int kMaccOffset = 640;      // MoE-down accumulator, floats after rowsum
 #ifndef MKD_RING
 #define MKD_RING 6
@@ -109,6 +112,10 @@ constexpr int RT_NACT = 512;    // number of active experts
 constexpr int RT_ACT = 520;     // [256] active experts, ascending
 constexpr int RT_OFF = 776;     // [257] CSR offsets of each active expert's (token, slot) list
 constexpr int RT_FLAT = 1036;   // [256] b*k + j entries, experts ascending, tokens ascending
+constexpr int RT_EPOS = 1292;   // [256] entry b*k + j: (active expert index << 16) | position in its list
+constexpr int kRouteWords = kRouteTableWords;  // the whole table, as published (tagged) by the route builder
+static_assert(RT_EPOS + 256 == kRouteWords, "published table covers the routing area");
+static_assert(kRouteWords * 4 <= kLdsRouteBytes, "routing tables must fit the route area");
 
 // ------------------------------------------------------------------ task context
 struct Ctx {
@@ -275,6 +282,9 @@ __device__ __forceinline__ bool read_ok(Ctx& c) { return read_mi(c, MI_OK) != 0 
 // until it is; the watchdog and the abort flag bound the wait.  No barrier inside: every
 // wave may call it with its share, and the caller synchronises the team.  On failure a
 // worker marks MI_WFAIL, so that the team leaves the task after its next barrier.
+#ifndef MKD_POLL_SLEEP
+#define MKD_POLL_SLEEP 1
+#endif
 struct NoScale {
   __device__ float operator()(int) const { return 1.0f; }
 };
@@ -307,7 +317,7 @@ __device__ __forceinline__ bool team_poll(const Ctx& c, uint32_t ep, int n, Src 
         ok = false;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(MKD_POLL_SLEEP);
 #pragma unroll
       for (int u = 0; u < W; ++u) {
         const int i = base + c.tid + u * c.tthreads;
@@ -318,7 +328,10 @@ __device__ __forceinline__ bool team_poll(const Ctx& c, uint32_t ep, int n, Src 
 #pragma unroll
       for (int u = 0; u < W; ++u) {
         const int i = base + c.tid + u * c.tthreads;
-        if (i < n) dst(i) = tag_val(w[u]) * sc[u];
+        if (i < n) {
+          if constexpr (__is_same(Scale, NoScale)) dst(i) = tag_val(w[u]);
+          else dst(i) = tag_val(w[u]) * sc[u];
+        }
       }
     }
   }
@@ -643,6 +656,8 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
   return true;
 }
 
+__device__ __forceinline__ bool route_build(Ctx& c, int l);
+
 // ------------------------------------------------------------------ OP_ROUTER / OP_LM_HEAD
 // Plain GEMV tiles on the normed input: router logits (layer l) or vocabulary logits
 // (final norm, tied embedding).
@@ -656,7 +671,7 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
   bool fresh = false;
   auto stage = [&]() { return team_stage_x(c, l, fresh); };
   if (!c.ctl) {
-    return worker_gemv<K>(c, src, R, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum, stage);
+    if (!worker_gemv<K>(c, src, R, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum, stage)) return false;
   } else {
     const bool ok = stage();
     if (ok && c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
@@ -669,6 +684,8 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
     }
     if (c.d[D_SIGNAL] >= 0) ctl_signal(c, p.counters + c.d[D_SIGNAL]);
   }
+  // the layer's route builder (first router tile): routing tables for everyone
+  if (!lm_head && c.d[D_ARG2] == 1) return route_build(c, l);
   return true;
 }
 
@@ -792,10 +809,14 @@ __device__ __forceinline__ void route_csr(const Ctx& c, const DParams& p) {
       int at = n_ent + pre;
       rt[RT_ACT + rank] = e;
       rt[RT_OFF + rank] = at;
+      int jj = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         for (int s = 0; s < min(64, n - 64 * q); ++s)
-          if (__builtin_amdgcn_readlane(ev[q], s) == e) rt[RT_FLAT + at++] = 64 * q + s;  // t = b * k + j
+          if (__builtin_amdgcn_readlane(ev[q], s) == e) {
+            rt[RT_FLAT + at++] = 64 * q + s;  // t = b * k + j
+            rt[RT_EPOS + 64 * q + s] = (rank << 16) | jj++;
+          }
     }
     n_act += __builtin_popcountll(act);
     n_ent += tot;
@@ -806,37 +827,32 @@ __device__ __forceinline__ void route_csr(const Ctx& c, const DParams& p) {
   }
 }
 
-// The tables of layer l by every wave of the team: tokens spread over the waves, then the
-// CSR by the first wave.  Called after a barrier that follows the controller's acquire of
-// the router counter; no wave has weight loads in flight here.  Tables already built for
-// layer l are kept; `write_debug` also stores the routing of every token for inspection.
-__device__ __forceinline__ bool route_layer(Ctx& c, int l, bool write_debug) {
+// ROUTER_TOPK + ROUTE_FINALIZE + MOE_GATHER, once per layer: the task of the first router
+// tile, after its own logits, waits for every token's logits (tagged), builds the tables
+// in its LDS with every wave (top-k per token, then the CSR by the first wave) and
+// publishes the whole table as tagged words; it also stores the routing for inspection.
+// Every other CU copies the table (route_layer) instead of recomputing it, so the
+// routing is done as soon as the router tiles are, off the MoE-up claimers' path.
+__device__ __forceinline__ bool route_build(Ctx& c, int l) {
   const DParams p = device_view(*c.kp);
   const int B = p.batch, k = p.top_k;
-  if (read_mi(c, MI_ROUTE_LAYER) != l) {
-    bool ok = true;
-    for (int b = c.tw; b < B && ok; b += c.nw + 1) {
-      float v[4];
-      ok = route_load(c, p, l, b, v);
-#ifdef MKD_DIAG_RA
-      if (c.ctl && c.lane == 0 && c.s.mi[MI_T_STAGED] == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
-#endif
-      if (ok) route_select(c, p, b, v);
-#ifdef MKD_DIAG_RB
-      if (c.ctl && c.lane == 0 && c.s.mi[MI_T_STAGED] == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
-#endif
-    }
-    if (!ok) c.s.mi[MI_WFAIL] = 1;
-    bar(c);
-    if (read_mi(c, MI_WFAIL) != 0) return false;
-    if (c.tw == 0) route_csr(c, p);
-    // published before the barrier, so that every wave of the team sees the same value at
-    // the next check (a task may start right after this one without another barrier)
-    if (c.tid == 0) c.s.mi[MI_ROUTE_LAYER] = l;
-    bar(c);
+  bool ok = true;
+  for (int b = c.tw; b < B && ok; b += c.nw + 1) {
+    float v[4];
+    ok = route_load(c, p, l, b, v);
+    if (ok) route_select(c, p, b, v);
   }
-  if (write_debug && c.tid < B * k) {
-    const LAS int32_t* rt = c.s.route;
+  if (!ok) c.s.mi[MI_WFAIL] = 1;
+  bar(c);
+  if (read_mi(c, MI_WFAIL) != 0) return false;
+  if (c.tw == 0) route_csr(c, p);
+  if (c.tid == 0) c.s.mi[MI_ROUTE_LAYER] = l;
+  bar(c);
+  const LAS int32_t* rt = c.s.route;
+  GAS uint64_t* dst = p.route_tbl + (int64_t)l * kRouteWords;
+  const uint32_t ep = layer_tag(p.epoch, l);
+  for (int i = c.tid; i < kRouteWords; i += c.tthreads) st_tag(dst + i, __int_as_float(rt[i]), ep);
+  if (c.tid < B * k) {
     const LAS float* rw = reinterpret_cast<const LAS float*>(rt + RT_W);
     const int b = c.tid / k, j = c.tid % k;
     st_pub(p.topk_ids + ((int64_t)l * p.max_batch + b) * k + j, rt[RT_IDS + b * 16 + j]);
@@ -845,25 +861,54 @@ __device__ __forceinline__ bool route_layer(Ctx& c, int l, bool write_debug) {
   return true;
 }
 
-// The controller builds the tables of layer l alone, without barriers, when the router
-// tiles of layer l are already done (one poll, no wait): used while the workers compute
-// another task (attention), so that the MoE-up claimer that follows on this CU starts
-// with its routing in place.  The workers read the tables only after a later barrier.
-// Batches of at most kRouteAhead tokens: their logits are loaded together (one round trip).
-constexpr int kRouteAhead = 8;
+// The tables of layer l in this CU's LDS: kept when already there, else copied from the
+// published (tagged) table by every wave.
+__device__ __forceinline__ bool route_layer(Ctx& c, int l) {
+  const DParams p = device_view(*c.kp);
+  if (read_mi(c, MI_ROUTE_LAYER) == l) return true;
+  const GAS uint64_t* src = p.route_tbl + (int64_t)l * kRouteWords;
+  LAS float* rt = reinterpret_cast<LAS float*>(c.s.route);
+  const bool ok = team_poll<4>(
+      c, layer_tag(p.epoch, l), kRouteWords, [&](int i) { return src + i; },
+      [&](int i) -> LAS float& { return rt[i]; });
+  if (!ok) c.s.mi[MI_WFAIL] = 1;
+  bar(c);
+  if (read_mi(c, MI_WFAIL) != 0) return false;
+  // published before the barrier, so that every wave of the team sees the same value at
+  // the next check (a task may start right after this one without another barrier)
+  if (c.tid == 0) c.s.mi[MI_ROUTE_LAYER] = l;
+  bar(c);
+  return true;
+}
+
+// The controller copies the published table of layer l alone, without barriers, when it
+// is already complete (one read, no wait): used while the workers compute another task
+// (attention), so that the MoE-up claimer that follows on this CU starts with its routing
+// in place.  The workers read the tables only after a later barrier.
 __device__ __forceinline__ void ctl_route_ahead(Ctx& c, int l) {
   const DParams p = device_view(*c.kp);
-  if (p.batch > kRouteAhead || read_mi(c, MI_ROUTE_LAYER) == l) return;
-  float v[kRouteAhead][4];
-  bool all = true;
+  if (read_mi(c, MI_ROUTE_LAYER) == l) return;
+  const GAS uint64_t* src = p.route_tbl + (int64_t)l * kRouteWords;
+  const uint32_t ep = layer_tag(p.epoch, l);
+  LAS int32_t* rt = c.s.route;
+  constexpr int PER = 8;
+  for (int base = 0; base < kRouteWords; base += 64 * PER) {
+    uint64_t w[PER];
 #pragma unroll
-  for (int b = 0; b < kRouteAhead; ++b)
-    if (b < p.batch && all) all = route_load(c, p, l, b, v[b], true);
-  if (!all) return;
+    for (int u = 0; u < PER; ++u) {
+      const int i = base + c.lane + 64 * u;
+      w[u] = i < kRouteWords ? ld_tag(src + i) : tag_word(0.0f, ep);
+    }
+    bool ready = true;
 #pragma unroll
-  for (int b = 0; b < kRouteAhead; ++b)
-    if (b < p.batch) route_select(c, p, b, v[b]);
-  route_csr(c, p);
+    for (int u = 0; u < PER; ++u) ready = ready && tag_is(w[u], ep);
+    if (__ballot(!ready) != 0) return;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = base + c.lane + 64 * u;
+      if (i < kRouteWords) rt[i] = (int32_t)(uint32_t)w[u];
+    }
+  }
   if (c.lane == 0) c.s.mi[MI_ROUTE_LAYER] = l;
 }
 
@@ -1041,8 +1086,7 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   bar(c);
   if (!read_ok(c)) return false;
   if (c.ctl) stage_x_finish(c, l, fresh);
-  // the first claimer that routes also stores the layer's routing for inspection
-  if (!route_layer(c, l, ci == (stat ? n_attn : 0))) return false;
+  if (!route_layer(c, l)) return false;
 #ifdef MKD_DIAG_MOE
   if (c.ctl && c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
 #endif
@@ -1118,7 +1162,7 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
   }
   // routing tables of layer l (normally left in LDS by this CU's MoE-up claimer)
   if (read_mi(c, MI_ROUTE_LAYER) != l) {
-    if (!route_layer(c, l, false)) return false;
+    if (!route_layer(c, l)) return false;
   }
   // (1) O-proj: NSO * R rows of length KH; token groups that fit in LDS
   {
@@ -1202,22 +1246,26 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
         }
         if (!ctl_gemv_barriers(c, ok)) return false;
         if (c.lane == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
-        // router-weighted sum, experts in ascending order (one expert per pass: a token
-        // appears once per expert, so no two lanes update the same element)
-        for (int sg = 0; sg < na; ++sg) {
-          const int ob = rtab[RT_OFF + a0 + sg], n_e = rtab[RT_OFF + a0 + sg + 1] - ob;
-          for (int i = c.lane; i < R * n_e; i += 64) {
-            const int r = i / n_e, j = i % n_e;
-            const int slot = rtab[RT_FLAT + ob + j];
-            const int b = slot / k, sj = slot % k;
-            acc_m[r * kMaxBatch + b] += rw[b * 16 + sj] * c.s.rowsum[(sg * R + r) * nb + j];
+        // router-weighted sum: lane (row, token) adds the token's choices in selection
+        // order, each found through its entry record (active expert, position in the
+        // expert's list), so the loads of one lane are independent of each other
+        for (int i = c.lane; i < R * B; i += 64) {
+          const int r = i / B, b = i % B;
+          float a = acc_m[r * kMaxBatch + b];
+          for (int j = 0; j < k; ++j) {
+            const int ep = rtab[RT_EPOS + b * k + j], ai = (ep >> 16) - a0;
+            if (ai >= 0 && ai < na) a += rw[b * 16 + j] * c.s.rowsum[(ai * R + r) * nb + (ep & 0xFFFF)];
           }
+          acc_m[r * kMaxBatch + b] = a;
         }
       }
     }
   }
   // (3) h_{l+1}[rows] = h_l + a + m and the tile's sums of squares, as tagged words (the
   // next layer's consumers wait on them)
+#ifdef MKD_DIAG_O1
+  if (c.ctl && c.lane == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
+#endif
   if (c.ctl) {
     // the residual rows read at the start were written long before (previous layer's
     // output tasks, before any task of this layer could start); re-read any not yet seen
@@ -1250,6 +1298,9 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
       st_tag(p.ss + ((int64_t)(l + 1) * p.max_batch + c.lane) * p.shape.n_rt + rt, t, ep1);
     }
   }
+  // the workers wait for the controller's stores to be issued before they start polling for
+  // the next layer's input (measured: their polls slowed this tail by about a microsecond)
+  bar(c);
   return true;
 }
 
@@ -1365,7 +1416,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
 #pragma unroll
       for (int j = 0; j < NK; ++j) dma16(p.kv_pool + vb + j * 512 + c.lane * 8, dst + NK * 1024 + j * 1024);
     };
-    int lpl[kMaxLdsPages];  // pages in this worker's LDS slots (c1: none)
+    int lpl[kMaxLdsPages > 0 ? kMaxLdsPages : 1];  // pages in this worker's LDS slots (c1: none)
     if (!c.ctl) {
 #pragma unroll
       for (int i = 0; i < MAXP; ++i) {

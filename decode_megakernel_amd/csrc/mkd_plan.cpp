@@ -146,7 +146,8 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
         case W_ROUTER:
           for (int r0 = 0; r0 < g.n_experts; r0 += o.router_rows)
             // logits leave as tagged words (no counter): consumers wait on the data itself
-            em.emit(OP_ROUTER, l, r0, std::min(o.router_rows, g.n_experts - r0), 0, 0, -1, 0, -1);
+            // ARG2 = 1: the first tile also builds and publishes the layer's routing tables
+            em.emit(OP_ROUTER, l, r0, std::min(o.router_rows, g.n_experts - r0), r0 == 0 ? 1 : 0, 0, -1, 0, -1);
           break;
         case W_ATTN:
           for (int i = 0; i < n_attn; ++i)

@@ -24,7 +24,7 @@
 #define MKD_UP_ROWS 12  // batch 1, 8K context: 4 -> 268, 8 -> 289, 12 -> 293, 16 -> 291 tok/s
 #endif
 #ifndef MKD_PPI
-#define MKD_PPI 28  // measured at batch 1, 8K context: 14 -> 270, 21 -> 284, 28 -> 290, 42 -> 285, 56 -> 274 tok/s
+#define MKD_PPI 21  // batch 1, 8K context (tagged edges, static MoE-up): 14 -> 344, 21 -> 368, 28 -> 360, 35 -> 356, 42 -> 346 tok/s
 #endif
 
 namespace mkd {
