@@ -96,6 +96,7 @@ struct PlanShape {
   int32_t n_up_tiles;      // moe_inter / up_rows
   int32_t pages_per_item;  // attention pages per claimed item
   int32_t qkv_rows;        // weight rows per QKV tile (RoPE pairs kept together)
+  int32_t qkv_tph;         // QKV tiles per head
   int32_t router_rows;     // rows per router tile
   int32_t lm_rows;         // rows per LM-head tile
 };
@@ -126,7 +127,8 @@ struct Params {
   // workspace (fp32 unless noted)
   uint64_t* h;        // [L+1][maxB][H] tagged
   uint64_t* ss;       // [L+1][maxB][n_rt] tagged per-row-tile sums of squares
-  float* q;           // [L][maxB][nq*hd] post-RoPE queries
+  uint64_t* q;        // [L][maxB][nq*hd] tagged post-RoPE queries
+  uint64_t* kvflag;   // [L][2*nkv][64] tagged: K/V tile t of a head has stored its new slots
   uint64_t* attn_part;  // [max_items][hpg][hd + 2] tagged: unnormalised o, then m, l
   uint64_t* attn_o;     // [L][maxB][nq*hd] tagged
   uint64_t* router;   // [L][maxB][E] tagged

@@ -242,7 +242,8 @@ struct DParams {
   GAS float* logits;
   GAS uint64_t* h;
   GAS uint64_t* ss;
-  GAS float* q;
+  GAS uint64_t* q;
+  GAS uint64_t* kvflag;
   GAS uint64_t* attn_part;
   GAS uint64_t* attn_o;
   GAS uint64_t* router;
@@ -283,7 +284,7 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.n_teams = p.n_teams;
   d.shape.n_rt = p.shape.n_rt; d.shape.rt_rows = p.shape.rt_rows;
   d.shape.up_rows = p.shape.up_rows; d.shape.n_up_tiles = p.shape.n_up_tiles;
-  d.shape.pages_per_item = p.shape.pages_per_item; d.shape.qkv_rows = p.shape.qkv_rows;
+  d.shape.pages_per_item = p.shape.pages_per_item; d.shape.qkv_rows = p.shape.qkv_rows; d.shape.qkv_tph = p.shape.qkv_tph;
   d.shape.router_rows = p.shape.router_rows; d.shape.lm_rows = p.shape.lm_rows;
   d.ctr.per_layer = p.ctr.per_layer; d.ctr.x_ready = p.ctr.x_ready; d.ctr.qkv_done = p.ctr.qkv_done;
   d.ctr.router_done = p.ctr.router_done; d.ctr.attn_claim = p.ctr.attn_claim; d.ctr.up_claim = p.ctr.up_claim;
@@ -294,7 +295,7 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.w_router = gas(p.w_router); d.w_gate_up = gas(p.w_gate_up); d.w_down = gas(p.w_down);
   d.tokens = cas(p.tokens); d.seq_lens = cas(p.seq_lens); d.page_table = cas(p.page_table);
   d.kv_pool = gas(p.kv_pool); d.logits = gas(p.logits);
-  d.h = gas(p.h); d.ss = gas(p.ss); d.q = gas(p.q); d.attn_part = gas(p.attn_part); d.attn_o = gas(p.attn_o);
+  d.h = gas(p.h); d.ss = gas(p.ss); d.q = gas(p.q); d.kvflag = gas(p.kvflag); d.attn_part = gas(p.attn_part); d.attn_o = gas(p.attn_o);
   d.router = gas(p.router); d.route_tbl = gas(p.route_tbl); d.topk_ids = gas(p.topk_ids); d.topk_w = gas(p.topk_w);
   d.moe_act = gas(p.moe_act); d.inv_freq = cas(p.inv_freq);
   d.rope = gas(p.rope);

@@ -177,12 +177,15 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
   const size_t tbl_bytes = sizeof(uint64_t) * L * kRouteTableWords;
   const size_t act_bytes = sizeof(uint64_t) * L * B * K * cfg->moe_inter;
   const size_t h_bytes = sizeof(uint64_t) * (L + 1) * B * H;
+  const size_t q_bytes = sizeof(uint64_t) * L * B * QD;
+  const size_t flag_bytes = sizeof(uint64_t) * L * 2 * cfg->n_kv_heads * 64;
   const size_t ss_bytes = sizeof(uint64_t) * (L + 1) * B * e->shape.n_rt;
   const size_t rope_bytes = sizeof(uint64_t) * B * cfg->head_dim;
   std::vector<std::pair<size_t, void**>> slots = {
       {h_bytes, (void**)&p.h},
       {ss_bytes, (void**)&p.ss},
-      {sizeof(float) * L * B * QD, (void**)&p.q},
+      {q_bytes, (void**)&p.q},
+      {flag_bytes, (void**)&p.kvflag},
       {part_bytes, (void**)&p.attn_part},
       {attn_o_bytes, (void**)&p.attn_o},
       {router_bytes, (void**)&p.router},
@@ -209,7 +212,8 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
     at += align256(s.first);
   }
   e->tagged = {{p.attn_part, part_bytes}, {p.attn_o, attn_o_bytes}, {p.router, router_bytes}, {p.route_tbl, tbl_bytes},
-               {p.moe_act, act_bytes}, {p.h, h_bytes}, {p.ss, ss_bytes}, {p.rope, rope_bytes}};
+               {p.moe_act, act_bytes}, {p.h, h_bytes}, {p.ss, ss_bytes}, {p.rope, rope_bytes},
+               {p.q, q_bytes}, {p.kvflag, flag_bytes}};
   rc = hipMemset(e->ws, 0, total);
   if (rc == hipSuccess) {
     std::vector<double> inv(cfg->head_dim / 2);

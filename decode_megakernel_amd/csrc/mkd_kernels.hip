@@ -628,9 +628,9 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
         o2 = bb * cs + a * sn;
       }
       if (hh < p.n_q) {
-        GAS float* q = p.q + ((int64_t)l * p.max_batch + b) * p.n_q * hd + (int64_t)hh * hd;
-        st_pub(q + dim, o1);
-        st_pub(q + dim + half, o2);
+        GAS uint64_t* q = p.q + ((int64_t)l * p.max_batch + b) * p.n_q * hd + (int64_t)hh * hd;
+        st_tag(q + dim, o1, layer_tag(p.epoch, l));
+        st_tag(q + dim + half, o2, layer_tag(p.epoch, l));
       } else {
         const int lp = pos / p.page, t = pos % p.page;
         const int phys = (lp < p.max_pages) ? p.page_table[(int64_t)b * p.max_pages + lp] : -1;
@@ -651,7 +651,12 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
         }
       }
     }
-    ctl_signal(c, p.counters + c.d[D_SIGNAL]);
+    // queries leave as tagged words; a K or V tile raises its flag once its pool stores
+    // have completed, so that the attention item holding the new token's page may read it
+    if (hh >= p.n_q && c.lane == 0) {
+      wait_vm_all();
+      st_tag(p.kvflag + ((int64_t)l * 2 * p.n_kv + (hh - p.n_q)) * 64 + c.d[D_ARG3], 1.0f, layer_tag(p.epoch, l));
+    }
   }
   return true;
 }
@@ -1364,7 +1369,6 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
   LAS float* lw = mw + nw * 16;                        // [nw][16] running sum
   LAS float* part = lw + nw * 16;                      // [hpg][HD + 2] merged partial
   LAS float* wreg = part + 16 * (HD + 2);              // [nw][wstride] pages, then [hpg][HD] outputs
-  bool waited = false;
   if (c.ctl) {
     ctl_claim_put(c, 0, (uint32_t)c.d[D_ARG0]);
     if (c.lane == 0 && keep == 0) c.s.mi[MI_XS_LAYER] = -1;
@@ -1416,6 +1420,29 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
 #pragma unroll
       for (int j = 0; j < NK; ++j) dma16(p.kv_pool + vb + j * 512 + c.lane * 8, dst + NK * 1024 + j * 1024);
     };
+    // K and V tiles of group g for layer l have stored the new token's slot (their flags,
+    // one per tile, are tagged); then an acquire makes the pool's new slot visible
+    auto wait_kv_new = [&]() -> bool {
+      const int tph = p.shape.qkv_tph;  // <= 64
+      const uint32_t ep = layer_tag(p.epoch, l);
+      const GAS uint64_t* fk = p.kvflag + ((int64_t)l * 2 * nkv + g) * 64;
+      const GAS uint64_t* fv = p.kvflag + ((int64_t)l * 2 * nkv + nkv + g) * 64;
+      uint64_t wk = c.lane < tph ? ld_tag(fk + c.lane) : tag_word(0.0f, ep);
+      uint64_t wv = c.lane < tph ? ld_tag(fv + c.lane) : tag_word(0.0f, ep);
+      int32_t spins = 0;
+      while (__ballot(!tag_is(wk, ep) || !tag_is(wv, ep)) != 0) {
+        if ((++spins & 63) == 0 && aborted(p)) return false;
+        if (spins > p.spin_limit) {
+          if (c.lane == 0) report_error(p, 1u, c.task, G_TAGGED, (uint32_t)(wk >> 32), ep);
+          return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        if (!tag_is(wk, ep)) wk = ld_tag(fk + c.lane);
+        if (!tag_is(wv, ep)) wv = ld_tag(fv + c.lane);
+      }
+      fence_acquire_agent();
+      return true;
+    };
     int lpl[kMaxLdsPages > 0 ? kMaxLdsPages : 1];  // pages in this worker's LDS slots (c1: none)
     if (!c.ctl) {
 #pragma unroll
@@ -1441,27 +1468,46 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
         }
       }
     } else {
+      // the group's queries (tagged, from the QKV tiles of its heads) go first, the claim
+      // after them: the claim reply arrives during the compute
+      const GAS uint64_t* qsrc = p.q + ((int64_t)l * p.max_batch + b) * p.n_q * HD + (int64_t)g * hpg * HD;
+      constexpr int QPL = 16 * HD / 64;  // words per lane for up to 16 heads
+      const uint32_t ep = layer_tag(p.epoch, l);
+      uint64_t qw[QPL];
+#pragma unroll
+      for (int u = 0; u < QPL; ++u) {
+        const int i = c.lane + 64 * u;
+        qw[u] = i < hpg * HD ? ld_tag(qsrc + i) : tag_word(0.0f, ep);
+      }
+      nxt = ctl_claim_issue(c, head, c.d[D_ARG1]);
       bool ok = true;
-      if (!waited) {
-        ok = ctl_wait(c, p.counters + c.d[D_WAIT], (uint32_t)c.d[D_TARGET]);
-        waited = true;
+      int32_t spins = 0;
+      while (true) {
+        bool ready = true;
+#pragma unroll
+        for (int u = 0; u < QPL; ++u) ready = ready && tag_is(qw[u], ep);
+        if (__ballot(!ready) == 0) break;
+        if ((++spins & 63) == 0 && aborted(p)) { ok = false; break; }
+        if (spins > p.spin_limit) {
+          if (c.lane == 0) report_error(p, 1u, c.task, G_TAGGED, (uint32_t)(qw[0] >> 32), ep);
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int u = 0; u < QPL; ++u)
+          if (!tag_is(qw[u], ep)) qw[u] = ld_tag(qsrc + c.lane + 64 * u);
       }
       if (ok) {
-        // the query loads go first, the claim after them: writing the queries to LDS then
-        // waits for the loads only, and the claim reply arrives during the compute
-        const GAS float* qsrc = p.q + ((int64_t)l * p.max_batch + b) * p.n_q * HD + (int64_t)g * hpg * HD;
-        constexpr int QPL = 16 * HD / 4 / 64;  // f32x4 per lane for up to 16 heads
-        f32x4 qv[QPL];
 #pragma unroll
         for (int u = 0; u < QPL; ++u) {
           const int i = c.lane + 64 * u;
-          if (i < hpg * HD / 4) qv[u] = *reinterpret_cast<const GAS f32x4*>(qsrc + i * 4);
+          if (i < hpg * HD) qs[i] = tag_val(qw[u]);
         }
-        nxt = ctl_claim_issue(c, head, c.d[D_ARG1]);
-#pragma unroll
-        for (int u = 0; u < QPL; ++u) {
-          const int i = c.lane + 64 * u;
-          if (i < hpg * HD / 4) *reinterpret_cast<LAS f32x4*>(qs + i * 4) = qv[u];
+        if (c.lane == 0 && c.s.mi[MI_READY_LO] == 0 && c.s.mi[MI_READY_HI] == 0) {
+          const uint64_t t = wall_clock64();
+          c.s.mi[MI_READY_LO] = (int32_t)(uint32_t)t;
+          c.s.mi[MI_READY_HI] = (int32_t)(uint32_t)(t >> 32);
         }
       }
       ctl_set_ok(c, ok);
@@ -1479,7 +1525,14 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     if (c.ctl && c.lane == 0 && j == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
 #endif
     if (!c.ctl) {
-      // the page holding the new token is read after the wait (the acquire made it visible)
+      // the page holding the new token is read once the K and V tiles of the group have
+      // flagged their stores (then an acquire, for the plain page loads)
+      bool holds_last = false;
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) holds_last = holds_last || (lp[i] < c1 && lp[i] == last);
+#pragma unroll
+      for (int s = 0; s < kMaxLdsPages; ++s) holds_last = holds_last || (s < n_lds && lpl[s] == last);
+      if (holds_last && !wait_kv_new()) return false;
 #pragma unroll
       for (int i = 0; i < MAXP; ++i)
         if (lp[i] < c1 && lp[i] == last) load_page(kr[i], vr[i], kbase[i], vbase[i]);
@@ -1565,6 +1618,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
       for (int lpg = c0 + c.wi + nw * (MAXP + n_lds); lpg < c1; lpg += nw) {
         int64_t kb = 0, vb = 0;
         if (!page_base(lpg, kb, vb)) continue;
+        if (lpg == last && !wait_kv_new()) return false;
         load_page(kr[0], vr[0], kb, vb);
         do_page(kr[0], vr[0], lpg);
       }

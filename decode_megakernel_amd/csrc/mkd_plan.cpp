@@ -122,7 +122,8 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   // tiles per head: about n_cu / heads, within [ceil(half / max_pairs), half]; the pairs of
   // a head are split as evenly as possible
   const int qkv_tph = std::min(half, std::max((half + o.qkv_max_pairs - 1) / o.qkv_max_pairs, n_cu / n_qkv_heads));
-  const int n_qkv_tiles = n_qkv_heads * qkv_tph;
+  if (qkv_tph > 64) return "at most 64 QKV tiles per head";
+  P.shape.qkv_tph = qkv_tph;
   const int n_router_tiles = (g.n_experts + o.router_rows - 1) / o.router_rows;
   const int n_attn = o.n_attn_claimers > 0 ? o.n_attn_claimers : n_cu;
   const int n_up = o.n_up_claimers > 0 ? o.n_up_claimers : n_cu;
@@ -140,7 +141,8 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
           for (int hh = 0; hh < n_qkv_heads; ++hh)
             for (int t = 0; t < qkv_tph; ++t) {
               const int j0 = t * half / qkv_tph, j1 = (t + 1) * half / qkv_tph;
-              em.emit(OP_QKV, l, hh, j0, j1 - j0, 0, -1, 0, L(l, c.qkv_done));
+              // queries leave tagged; K / V tiles raise a tagged flag (ARG3: tile of the head)
+              em.emit(OP_QKV, l, hh, j0, j1 - j0, t, -1, 0, -1);
             }
           break;
         case W_ROUTER:
@@ -151,7 +153,7 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
           break;
         case W_ATTN:
           for (int i = 0; i < n_attn; ++i)
-            em.emit(OP_ATTN, l, i, n_attn, 0, 0, L(l, c.qkv_done), n_qkv_tiles, -1);
+            em.emit(OP_ATTN, l, i, n_attn, 0, 0, -1, 0, -1);
           break;
         case W_MOE_UP:
           for (int i = 0; i < n_up; ++i)
@@ -250,10 +252,12 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
   // and the experts' activations (output tasks).  Their producers' waves precede their
   // consumers' waves in the global order.
   for (int l = 0; l < g.n_layers; ++l) {
-    int router_end = -1, up_first = -1, attn_end = -1, up_end = -1, out_first = -1;
+    int router_end = -1, up_first = -1, attn_end = -1, up_end = -1, out_first = -1, qkv_end = -1, attn_first = -1;
     for (const Wave& w : P.waves)
       if (w.layer == l) {
         if (w.kind == W_ROUTER) router_end = w.first + w.count;
+        if (w.kind == W_QKV) qkv_end = w.first + w.count;
+        if (w.kind == W_ATTN) attn_first = w.first;
         if (w.kind == W_ATTN) attn_end = w.first + w.count;
         if (w.kind == W_MOE_UP) {
           up_first = w.first;
@@ -261,6 +265,8 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
         }
         if (w.kind == W_OUT) out_first = w.first;
       }
+    if (qkv_end < 0 || attn_first < qkv_end)
+      return "layer " + std::to_string(l) + ": the attention wave must follow the QKV wave";
     if (router_end < 0 || up_first < router_end)
       return "layer " + std::to_string(l) + ": the MoE-up wave must follow the router wave";
     // the layer's input: the previous layer's output wave (the embedding wave for layer 0)

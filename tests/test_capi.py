@@ -80,13 +80,17 @@ def test_plan_structure(geom, batch, n_cu):
         t = qkv[qkv[:, 1] == layer]
         covered = sorted((h, j0 + i) for h, j0, pb in t[:, 2:5] for i in range(pb))
         assert covered == [(h, i) for h in range(gq) for i in range(geom.head_dim // 2)]
-    # barrier accounting: every QKV tile signals the counter the attention claimers
-    # wait on, with the target equal to the number of tiles
+    # queries and the K / V flags are tagged words: no counter between QKV tiles and the
+    # attention claimers, which come after the layer's QKV wave; ARG3 numbers the tiles of
+    # a head
     attn = desc[ops == OP_ATTN]
     for layer in range(geom.n_layers):
         a = attn[attn[:, 1] == layer]
         t = qkv[qkv[:, 1] == layer]
-        assert (a[:, 6] == t[0, 8]).all() and (a[:, 7] == len(t)).all()
+        assert (a[:, 6] == -1).all() and (t[:, 8] == -1).all()
+        assert a[:, 10].min() > t[:, 10].max()
+        for h in range(gq):
+            assert sorted(t[t[:, 2] == h][:, 5].tolist()) == list(range((t[:, 2] == h).sum()))
     # one output task per residual row tile and layer; the residual rows travel as tagged
     # words, so neither the output tasks nor the next layer's consumers use a counter, and
     # the next layer's tasks come after the output wave in the global order
