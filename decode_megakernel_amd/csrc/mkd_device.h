@@ -1,14 +1,15 @@
 // mkd_device.h - device primitives for the decode megakernel on gfx950 (CDNA4).
 //
-// Counter protocol ("Inside the megakernel serving engine for North Mini Code",
-// section "Barriers": a waiter spins until the counter reaches its target and then
-// fences; an arriver fences its results and then atomically adds one).  On MI355X
-// the eight XCDs have private L2 caches that are not coherent with each other, so
-// both sides use agent-scope ordering: the arriver makes every wave's stores
-// complete, then one lane issues an agent-scope release fence (L2 write-back) and
-// a relaxed agent-scope atomic add; the waiter polls with relaxed agent-scope loads
-// (which bypass the non-coherent cache levels), then issues an agent-scope acquire
-// fence (cache invalidate) before the workgroup reads the producer's data.
+// Dependency protocol ("Inside the megakernel serving engine for North Mini Code",
+// section "Barriers": a waiter spins until its dependency is met and then reads the
+// producer's data).  On MI355X the eight XCDs have private L2 caches that are not
+// coherent with each other.  Data that crosses workgroups travels as tagged 64-bit words
+// (value and a step/layer tag, one agent-scope store, written through to the coherent
+// level): the consumer polls the words themselves with agent-scope loads, which bypass
+// the non-coherent levels, so no fence or atomic sits on the critical path.  Counters
+// (relaxed agent-scope atomics) remain for the claim queues and the abort / error block;
+// the one plain-load consumer of data written during the step (the new K/V slot of the
+// paged pool) waits on tagged flags and then issues an agent-scope acquire.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

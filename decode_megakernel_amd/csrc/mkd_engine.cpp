@@ -394,7 +394,11 @@ int mkd_sync_status(mkd_engine* e) {
   if (rc != hipSuccess) return hip_fail(e, rc, "status read");
   if (st[G_ERR_CODE] == 0) return MKD_OK;
   char buf[256];
-  if (st[G_ERR_CODE] == 1) {
+  if (st[G_ERR_CODE] == 1 && (int32_t)st[G_ERR_CTR] == G_TAGGED) {
+    snprintf(buf, sizeof(buf), "watchdog: task %u waited on tagged data (saw tag %u, wanted %u)", st[G_ERR_TASK],
+             st[G_ERR_SEEN], st[G_ERR_WANT]);
+    fail(e, MKD_ERR_DEADLOCK, buf);
+  } else if (st[G_ERR_CODE] == 1) {
     snprintf(buf, sizeof(buf), "watchdog: task %u waited on counter %u (saw %u, wanted %u)", st[G_ERR_TASK],
              st[G_ERR_CTR], st[G_ERR_SEEN], st[G_ERR_WANT]);
     fail(e, MKD_ERR_DEADLOCK, buf);

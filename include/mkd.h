@@ -4,8 +4,10 @@
  * One call runs one whole autoregressive decode step of a parallel-transformer MoE
  * model as a single persistent kernel: one workgroup per compute unit, resident for
  * the step, walking a host-built per-CU task list (one task = one tile of one op),
- * with dependencies carried by global-memory counters and the variable-size
- * attention and MoE work balanced through shared claim queues.
+ * with dependencies carried through global memory (tagged 64-bit data words whose
+ * tag names the step and layer, polled by their consumers; atomic counters for the
+ * shared claim queues) and the variable-size attention and MoE work balanced over
+ * the compute units.
  *
  * Source of the method: "Inside the megakernel serving engine for North Mini Code"
  * (Cohere), sections "What is a Megakernel?" (persistent kernel, per-SM task lists,
@@ -131,9 +133,9 @@ int mkd_decode_step(mkd_engine* eng, void* stream, int32_t batch, const int32_t*
                     int32_t n_pages, float* d_logits);
 
 /* Wait for the engine's last step on its stream and report device-side errors:
-   MKD_ERR_DEADLOCK if the wait watchdog fired (a counter never reached its
-   target), MKD_ERR_ARG if a page-table entry was out of range, else MKD_OK.  The
-   error record is cleared. */
+   MKD_ERR_DEADLOCK if the wait watchdog fired (a dependency's data or counter
+   never arrived), MKD_ERR_ARG if a page-table entry was out of range, else MKD_OK.
+   The error record is cleared. */
 int mkd_sync_status(mkd_engine* eng);
 
 /* Text of the engine's last error ("" if none).  The pointer stays valid until the
