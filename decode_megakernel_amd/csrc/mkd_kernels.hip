@@ -1516,11 +1516,9 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     }
     bar(c);
     if (!read_ok(c)) return false;
-    // the controller is idle until the merge: it builds this layer's routing tables for
-    // the MoE-up claimer that follows on this CU
-#ifndef MKD_DIAG_NORA
+    // the controller is idle until the merge: it copies this layer's routing tables (when
+    // already published) for the tasks that follow on this CU
     if (c.ctl) ctl_route_ahead(c, l);
-#endif
 #ifdef MKD_DIAG_A0
     if (c.ctl && c.lane == 0 && j == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
 #endif

@@ -121,7 +121,10 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   const int half = g.head_dim / 2;
   // tiles per head: about n_cu / heads, within [ceil(half / max_pairs), half]; the pairs of
   // a head are split as evenly as possible
-  const int qkv_tph = std::min(half, std::max((half + o.qkv_max_pairs - 1) / o.qkv_max_pairs, n_cu / n_qkv_heads));
+  const int qkv_tph = o.qkv_tph > 0 ? std::min(half, std::max(o.qkv_tph, (half + 23) / 24))
+                                    : std::min(half, std::max((half + o.qkv_max_pairs - 1) / o.qkv_max_pairs,
+                                                              n_cu / n_qkv_heads));
+  if (2 * ((half + qkv_tph - 1) / qkv_tph) * max_batch > 2048) return "QKV tile rows x batch exceed the row-sum area";
   if (qkv_tph > 64) return "at most 64 QKV tiles per head";
   P.shape.qkv_tph = qkv_tph;
   const int n_router_tiles = (g.n_experts + o.router_rows - 1) / o.router_rows;

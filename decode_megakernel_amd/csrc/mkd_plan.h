@@ -23,8 +23,11 @@
 #ifndef MKD_UP_ROWS
 #define MKD_UP_ROWS 12  // batch 1, 8K context: 4 -> 268, 8 -> 289, 12 -> 293, 16 -> 291 tok/s
 #endif
+#ifndef MKD_QKV_TPH
+#define MKD_QKV_TPH 4  // batch 1, 8K (21-page items): 3 -> 377, 4 -> 381, auto (6) -> 381; with 28-page items 3 -> 396, 4 -> 405, 5 -> 366 tok/s
+#endif
 #ifndef MKD_PPI
-#define MKD_PPI 21  // batch 1, 8K context (tagged edges, static MoE-up): 14 -> 344, 21 -> 368, 28 -> 360, 35 -> 356, 42 -> 346 tok/s
+#define MKD_PPI 28  // batch 1, 8K context, 4 QKV tiles per head: 24 -> 388, 28 -> 405, 32 -> 400 tok/s
 #endif
 
 namespace mkd {
@@ -47,6 +50,8 @@ struct PlanOptions {
   int32_t qkv_max_pairs = 17;  // RoPE pairs per QKV tile at most (tile = 2x rows); a head is
                                // split into about n_cu / heads tiles so that one pass of QKV
                                // tiles covers the compute units once
+  int32_t qkv_tph = MKD_QKV_TPH;  // QKV tiles per head when > 0 (tiles of up to 24 pairs): fewer,
+                                  // larger tiles leave the CUs after them free for attention
   int32_t router_rows = 16;
   int32_t lm_rows = 32;
   int32_t n_attn_claimers = 0; // 0: automatic
