@@ -1467,6 +1467,28 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
           }
         }
       }
+      // The page holding the new token: the worker that has it waits for the group's K and
+      // V flags (raised by the same QKV wave that stores the queries the controller is
+      // waiting for), acquires and requests it, all before the first barrier.
+      bool holds_last = false;
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) holds_last = holds_last || (lp[i] < c1 && lp[i] == last);
+#pragma unroll
+      for (int s = 0; s < kMaxLdsPages; ++s) holds_last = holds_last || (s < n_lds && lpl[s] == last);
+      if (holds_last) {
+        if (!wait_kv_new()) c.s.mi[MI_WFAIL] = 1;
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i)
+          if (lp[i] < c1 && lp[i] == last) load_page(kr[i], vr[i], kbase[i], vbase[i]);
+#pragma unroll
+        for (int s = 0; s < kMaxLdsPages; ++s) {
+          if (s < n_lds && lpl[s] == last) {
+            int64_t kb = 0, vb = 0;
+            page_base(last, kb, vb);
+            dma_page(s, kb, vb);
+          }
+        }
+      }
     } else {
       // the group's queries (tagged, from the QKV tiles of its heads) go first, the claim
       // after them: the claim reply arrives during the compute
@@ -1523,25 +1545,6 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     if (c.ctl && c.lane == 0 && j == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
 #endif
     if (!c.ctl) {
-      // the page holding the new token is read once the K and V tiles of the group have
-      // flagged their stores (then an acquire, for the plain page loads)
-      bool holds_last = false;
-#pragma unroll
-      for (int i = 0; i < MAXP; ++i) holds_last = holds_last || (lp[i] < c1 && lp[i] == last);
-#pragma unroll
-      for (int s = 0; s < kMaxLdsPages; ++s) holds_last = holds_last || (s < n_lds && lpl[s] == last);
-      if (holds_last && !wait_kv_new()) return false;
-#pragma unroll
-      for (int i = 0; i < MAXP; ++i)
-        if (lp[i] < c1 && lp[i] == last) load_page(kr[i], vr[i], kbase[i], vbase[i]);
-#pragma unroll
-      for (int s = 0; s < kMaxLdsPages; ++s) {
-        if (s < n_lds && lpl[s] == last) {
-          int64_t kb = 0, vb = 0;
-          page_base(last, kb, vb);
-          dma_page(s, kb, vb);
-        }
-      }
       // Q^T operand: lane holds head (lane & 15), dims kk*32 + (lane>>4)*8 + [0, 8)
       const int hq = c.lane & 15;
       const float qscale = 1.4426950408889634f / sqrtf((float)HD);
@@ -1616,7 +1619,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
       for (int lpg = c0 + c.wi + nw * (MAXP + n_lds); lpg < c1; lpg += nw) {
         int64_t kb = 0, vb = 0;
         if (!page_base(lpg, kb, vb)) continue;
-        if (lpg == last && !wait_kv_new()) return false;
+        if (lpg == last && !wait_kv_new()) c.s.mi[MI_WFAIL] = 1;
         load_page(kr[0], vr[0], kb, vb);
         do_page(kr[0], vr[0], lpg);
       }
