@@ -473,6 +473,58 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
   return true;
 }
 
+// Worker side of a GEMV tile whose weights fit in LDS beside the staged input (QKV tiles at
+// small batch): every chunk of the worker's share is copied into its LDS region before the
+// input is waited for (the copies complete before the first barrier), then the tile is
+// computed from LDS.  The region of worker w starts after the chunks of workers 0 .. w-1.
+template <int K, int NB, class Stage>
+__device__ __forceinline__ bool gemv_tile_lds(const Ctx& c, const RowSrc& src, int R, const LAS float* xs,
+                                              const LAS int32_t* tok, int nb, LAS float* rowsum, Stage stage,
+                                              LAS char* region) {
+  using G = Gemv<K>;
+  const int S = (R + G::RPS - 1) / G::RPS;
+  const int ns = c.wi < S ? (S - c.wi + c.nw - 1) / c.nw : 0;
+  const int F = ns * G::CPL;
+  const int before = c.wi * (S / c.nw) + min(c.wi, S % c.nw);  // row steps of workers 0 .. wi-1
+  LAS char* mine = region + before * G::CPL * 1024;
+  for (int f = 0; f < F; ++f) dma16(src.base + gemv_chunk_off<K>(c, src, f), mine + f * 1024);
+  stage();
+  bar(c);
+  if (!read_ok(const_cast<Ctx&>(c))) return false;
+  float acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = 0.0f;
+  int toff[NB];
+  const int xld = src.xld ? src.xld : K;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) toff[j] = (NB == 1 || j < nb) ? __builtin_amdgcn_readfirstlane(tok[j]) * xld : 0;
+  for (int f = 0; f < F; ++f) {
+    const u32x4 w = *reinterpret_cast<const LAS u32x4*>(mine + f * 1024 + c.lane * 16);
+    const int cc = f % G::CPL;
+    const int kc = c.lane % G::LPR + G::LPR * cc;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (NB == 1 || j < nb) {
+        const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(xs + toff[j] + kc * 8);
+        acc[j] += dot8(w, xp[0], xp[1]);
+      }
+    }
+    if (cc == G::CPL - 1) {
+      const int row = (c.wi + c.nw * (f / G::CPL)) * G::RPS + c.lane / G::LPR;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (NB == 1 || j < nb) {
+          const float t = group_sum<G::LPR>(acc[j]);
+          if (c.lane % G::LPR == 0 && row < R) rowsum[row * nb + j] = t;
+          acc[j] = 0.0f;
+        }
+      }
+    }
+  }
+  bar(c);
+  return true;
+}
+
 // XSEG: the segments of the tile read different activation blocks (output tasks).
 template <int K, bool XSEG = false, class Stage = NoStage>
 __device__ __forceinline__ bool worker_gemv(const Ctx& c, const RowSrc& src, int R, const LAS float* xs,
@@ -595,6 +647,12 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
   bool fresh = false;
   auto stage = [&]() { return team_stage_x(c, l, fresh); };
   if (!c.ctl) {
+    // the whole tile in LDS after the staged input and its sums of squares, when it fits
+    const int xs_floats = (c.nw == kWaves - 1 ? kXsBytes1 : kXsBytes2) / 4;
+    const int used = B * H + B * p.shape.n_rt;
+    if (B == 1 && used + 2 * PB * K / 2 <= xs_floats)
+      return gemv_tile_lds<K, 1>(c, src, 2 * PB, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum, stage,
+                                 reinterpret_cast<LAS char*>(c.s.xs + used));
     return worker_gemv<K>(c, src, 2 * PB, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum, stage);
   } else {
     const bool rope_head = hh < p.n_q + p.n_kv;
@@ -1076,9 +1134,6 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   // attention item (or its combine) and start from the queue, whose items follow the
   // static ones, so no late CU holds an item back.
   int n_static = 0;
-#ifdef MKD_DIAG_R0
-  if (c.ctl && c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
-#endif
   // the layer's normed input (normally still staged by this CU's QKV or router task)
   bool fresh = false;
   const bool staged = team_stage_x(c, l, fresh);
@@ -1092,9 +1147,6 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   if (!read_ok(c)) return false;
   if (c.ctl) stage_x_finish(c, l, fresh);
   if (!route_layer(c, l)) return false;
-#ifdef MKD_DIAG_MOE
-  if (c.ctl && c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
-#endif
   const LAS int32_t* rt = c.s.route;
   const int n_items = __builtin_amdgcn_readfirstlane(rt[RT_NACT]) * NT;
   if (stat) {
@@ -1268,9 +1320,6 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
   }
   // (3) h_{l+1}[rows] = h_l + a + m and the tile's sums of squares, as tagged words (the
   // next layer's consumers wait on them)
-#ifdef MKD_DIAG_O1
-  if (c.ctl && c.lane == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
-#endif
   if (c.ctl) {
     // the residual rows read at the start were written long before (previous layer's
     // output tasks, before any task of this layer could start); re-read any not yet seen
@@ -1541,9 +1590,6 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     // the controller is idle until the merge: it copies this layer's routing tables (when
     // already published) for the tasks that follow on this CU
     if (c.ctl) ctl_route_ahead(c, l);
-#ifdef MKD_DIAG_A0
-    if (c.ctl && c.lane == 0 && j == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
-#endif
     if (!c.ctl) {
       // Q^T operand: lane holds head (lane & 15), dims kk*32 + (lane>>4)*8 + [0, 8)
       const int hq = c.lane & 15;
@@ -1636,9 +1682,6 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
       }
     }
     bar(c);
-#ifdef MKD_DIAG_A1
-    if (c.ctl && c.lane == 0 && j == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
-#endif
     // merge the workers: unnormalised o, running max M and sum L per head (all waves)
     for (int t = c.tid; t < hpg * HD; t += c.tthreads) {
       const int h = t / HD, dd = t % HD;
@@ -1764,22 +1807,12 @@ MKD_EXEC(exec_embed, return op_embed(c);)
 MKD_EXEC(exec_qkv, return op_qkv<G::kHidden>(c);)
 MKD_EXEC(exec_router, return op_rows_on_x<G::kHidden>(c, false);)
 MKD_EXEC(exec_lm_head, return op_rows_on_x<G::kHidden>(c, true);)
-#ifdef MKD_DIAG_R1
-MKD_EXEC(exec_moe_up, if (c.ctl && c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64(); return op_moe_up<G::kHidden>(c);)
-#else
 MKD_EXEC(exec_moe_up, return op_moe_up<G::kHidden>(c);)
-#endif
 MKD_EXEC(exec_out, return (op_out<G::kHidden, G::kInter>(c));)
 MKD_EXEC(exec_attn, return op_attn<G::kHd>(c);)
 
 template <class G>
 __device__ __forceinline__ bool run_task(KParams* kp, LAS char* lds, const CAS int32_t* d, int32_t task, int32_t team) {
-#ifdef MKD_DIAG_R2
-  if (d[D_OPCODE] == OP_MOE_UP && (int)threadIdx.x == 0) {
-    Smem sm(lds, 0, 1);
-    sm.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
-  }
-#endif
   switch (d[D_OPCODE]) {
     case OP_EMBED: return exec_embed<G>(kp, lds, d, task, team);
     case OP_QKV: return exec_qkv<G>(kp, lds, d, task, team);
