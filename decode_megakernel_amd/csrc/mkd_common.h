@@ -57,17 +57,12 @@ enum DescField : int32_t {
 };
 
 // ---------------------------------------------------------------- counters
-// Per-layer block of counters; all zeroed before each step.
+// Per-layer block of counters; all zeroed before each step.  Data edges travel as tagged
+// words (no counter); the counters left are the heads of the two claim queues.
 struct CounterLayout {
   int32_t per_layer;   // counters per layer block
-  int32_t x_ready;     // residual rows finalised for this layer's input (target n_rt)
-  int32_t qkv_done;    // QKV tiles done
-  int32_t router_done; // router tiles done
   int32_t attn_claim;  // attention queue head
   int32_t up_claim;    // MoE up queue head
-  int32_t comb;        // [n_kv] combined (seq) count per kv group
-  int32_t attn_items;  // [max_batch][n_kv] items finished per (seq, group)
-  int32_t up_done;     // [n_experts] up tiles finished per expert
   int32_t global_base; // start of the step-global block (after n_layers+1 layer blocks)
   int32_t total;       // total counters
 };

@@ -287,10 +287,8 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.shape.up_rows = p.shape.up_rows; d.shape.n_up_tiles = p.shape.n_up_tiles;
   d.shape.pages_per_item = p.shape.pages_per_item; d.shape.qkv_rows = p.shape.qkv_rows; d.shape.qkv_tph = p.shape.qkv_tph;
   d.shape.router_rows = p.shape.router_rows; d.shape.lm_rows = p.shape.lm_rows;
-  d.ctr.per_layer = p.ctr.per_layer; d.ctr.x_ready = p.ctr.x_ready; d.ctr.qkv_done = p.ctr.qkv_done;
-  d.ctr.router_done = p.ctr.router_done; d.ctr.attn_claim = p.ctr.attn_claim; d.ctr.up_claim = p.ctr.up_claim;
-  d.ctr.comb = p.ctr.comb; d.ctr.attn_items = p.ctr.attn_items;
-  d.ctr.up_done = p.ctr.up_done; d.ctr.global_base = p.ctr.global_base;
+  d.ctr.per_layer = p.ctr.per_layer; d.ctr.attn_claim = p.ctr.attn_claim; d.ctr.up_claim = p.ctr.up_claim;
+  d.ctr.global_base = p.ctr.global_base;
   d.ctr.total = p.ctr.total;
   d.embed = gas(p.embed); d.norm = gas(p.norm); d.w_qkv = gas(p.w_qkv); d.w_o = gas(p.w_o);
   d.w_router = gas(p.w_router); d.w_gate_up = gas(p.w_gate_up); d.w_down = gas(p.w_down);

@@ -91,8 +91,6 @@ struct Smem {
 };
 // misc int slots
 constexpr int MI_OK = 1;         // controller -> workers: inputs ready (0: abort)
-constexpr int MI_WAIT_CTR = 2;   // controller: last satisfied wait (skip repeats)
-constexpr int MI_WAIT_TGT = 3;
 constexpr int MI_ITEMS = 4;      // trace: items claimed by the current task
 constexpr int MI_READY_LO = 6;   // trace: when the current task's first wait completed
 constexpr int MI_READY_HI = 7;
@@ -153,91 +151,6 @@ __device__ __forceinline__ void bar(const Ctx& c) {
 }
 
 // ------------------------------------------------------------------ controller primitives
-// Spin until counter >= target (lane 0 polls, then acquire).  A wait this workgroup
-// already saw satisfied is skipped (counters only grow during a step).  Returns false
-// when the step is aborted.  Controller wave only.
-__device__ __forceinline__ bool ctl_wait(Ctx& c, GAS uint32_t* ctr, uint32_t target) {
-  const DParams p = device_view(*c.kp);
-  const int32_t idx = (int32_t)(ctr - p.counters);
-  int ok = 1;
-  if (c.lane == 0) {
-    if (!(c.s.mi[MI_WAIT_CTR] == idx && target <= (uint32_t)c.s.mi[MI_WAIT_TGT])) {
-      int32_t spins = 0;
-      uint32_t v;
-      while ((v = ctr_load(ctr)) < target) {
-        if ((spins & 63) == 63 && aborted(p)) { ok = 0; break; }
-        if (++spins > p.spin_limit) {
-          report_error(p, 1u, c.task, idx, v, target);
-          ok = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      fence_acquire_agent();
-      if (ok) {
-        c.s.mi[MI_WAIT_CTR] = idx;
-        c.s.mi[MI_WAIT_TGT] = (int32_t)target;
-      }
-    }
-    if (ok && c.s.mi[MI_READY_LO] == 0 && c.s.mi[MI_READY_HI] == 0) {
-      const uint64_t t = wall_clock64();
-      c.s.mi[MI_READY_LO] = (int32_t)(uint32_t)t;
-      c.s.mi[MI_READY_HI] = (int32_t)(uint32_t)(t >> 32);
-    }
-  }
-  return __shfl(ok, 0, 64) != 0;
-}
-
-// Spin until counters[lane] >= target for every lane < n (one poll of all n counters per
-// round), then acquire.  Returns false when the step is aborted.  Controller wave only.
-__device__ __forceinline__ bool ctl_wait_lanes(Ctx& c, GAS uint32_t* ctr, int n, uint32_t target) {
-  const DParams p = device_view(*c.kp);
-  bool ok = true;
-  int32_t spins = 0;
-  while (true) {
-    const uint32_t v = c.lane < n ? ctr_load(ctr) : target;
-    const uint64_t pending = __ballot(v < target);
-    if (pending == 0) break;
-    if ((spins & 63) == 63 && aborted(p)) {
-      ok = false;
-      break;
-    }
-    if (++spins > p.spin_limit) {
-      const int first = __builtin_ctzll(pending);
-      if (c.lane == first) report_error(p, 1u, c.task, (int32_t)(ctr - p.counters), v, target);
-      ok = false;
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  fence_acquire_agent();
-  if (ok && c.lane == 0 && c.s.mi[MI_READY_LO] == 0 && c.s.mi[MI_READY_HI] == 0) {
-    const uint64_t t = wall_clock64();
-    c.s.mi[MI_READY_LO] = (int32_t)(uint32_t)t;
-    c.s.mi[MI_READY_HI] = (int32_t)(uint32_t)(t >> 32);
-  }
-  return ok;
-}
-
-// Publish the controller's stores (written through with st_pub: waiting for their
-// completion suffices) and add one to the counter; returns the old value.
-__device__ __forceinline__ uint32_t ctl_arrive(Ctx& c, GAS uint32_t* ctr) {
-  uint32_t old = 0;
-  if (c.lane == 0) {
-    wait_vm_all();
-    old = ctr_add(ctr, 1u);
-  }
-  return (uint32_t)__shfl((int)old, 0, 64);
-}
-
-// Same, when the old value is not needed (the atomic does not wait for a reply).
-__device__ __forceinline__ void ctl_signal(Ctx& c, GAS uint32_t* ctr) {
-  if (c.lane == 0) {
-    wait_vm_all();
-    ctr_add(ctr, 1u);
-  }
-}
-
 // Claimer queues: claimer i of n takes item i first without touching the queue, then
 // items n + (queue head), so the claimers' first items cost no atomic and the queue
 // only sees the later claims, spread over time.  The claimer index and count are the
@@ -336,6 +249,12 @@ __device__ __forceinline__ bool team_poll(const Ctx& c, uint32_t ep, int n, Src 
     }
   }
   if (!ok && !c.ctl) c.s.mi[MI_WFAIL] = 1;
+  // trace: the task's inputs are ready when its first wait on tagged data completes
+  if (ok && c.ctl && c.lane == 0 && c.s.mi[MI_READY_LO] == 0 && c.s.mi[MI_READY_HI] == 0) {
+    const uint64_t t = wall_clock64();
+    c.s.mi[MI_READY_LO] = (int32_t)(uint32_t)t;
+    c.s.mi[MI_READY_HI] = (int32_t)(uint32_t)(t >> 32);
+  }
   return ok;
 }
 
@@ -542,14 +461,13 @@ struct NoHook {
 };
 template <class Hook = NoHook>
 __device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_entry = -1, uint32_t claim = 0,
-                                                  GAS uint32_t* flush = nullptr, Hook after_first = Hook()) {
+                                                  Hook after_first = Hook()) {
   ctl_set_ok(c, ok);
   if (c.lane == 0 && c.s.mi[MI_T_STAGED] == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
   bar(c);
   if (!read_ok(c)) return false;
   after_first();
   if (next_entry >= 0) ctl_claim_put(c, next_entry, claim);
-  if (flush) ctl_signal(c, flush);
   bar(c);
   if (c.lane == 0 && c.s.mi[MI_T_DONE] == 0) c.s.mi[MI_T_DONE] = (int32_t)(uint32_t)wall_clock64();
   return true;
@@ -666,7 +584,7 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
     }
     const bool ok = stage();
     if (ok && c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
-    if (!ctl_gemv_barriers(c, ok, -1, 0, nullptr, [&]() { stage_x_finish(c, l, fresh); })) return false;
+    if (!ctl_gemv_barriers(c, ok, -1, 0, [&]() { stage_x_finish(c, l, fresh); })) return false;
     const uint32_t ep0 = layer_tag(p.epoch, 0);
     for (int i = c.lane; i < PB * B; i += 64) {
       const int r = i / B, b = i % B, dim = j0 + r;
@@ -738,14 +656,13 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
   } else {
     const bool ok = stage();
     if (ok && c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
-    if (!ctl_gemv_barriers(c, ok, -1, 0, nullptr, [&]() { stage_x_finish(c, l, fresh); })) return false;
+    if (!ctl_gemv_barriers(c, ok, -1, 0, [&]() { stage_x_finish(c, l, fresh); })) return false;
     for (int i = c.lane; i < R * B; i += 64) {
       const int r = i / B, b = i % B;
       const float v = c.s.rowsum[i] * c.s.mf[b];
       if (lm_head) st_pub(p.logits + (int64_t)b * p.vocab + r0 + r, v);
       else st_tag(p.router + ((int64_t)l * p.max_batch + b) * p.n_experts + r0 + r, v, layer_tag(p.epoch, l));
     }
-    if (c.d[D_SIGNAL] >= 0) ctl_signal(c, p.counters + c.d[D_SIGNAL]);
   }
   // the layer's route builder (first router tile): routing tables for everyone
   if (!lm_head && c.d[D_ARG2] == 1) return route_build(c, l);
@@ -1854,8 +1771,6 @@ __device__ __forceinline__ void trace_task(KParams* kp, LAS int32_t* mi, const C
 // must be visible before any task starts (LDS keeps the previous workgroup's contents).
 __device__ __forceinline__ void init_team_state(LAS int32_t* mi, bool leader) {
   if (leader) {
-    mi[MI_WAIT_CTR] = -1;
-    mi[MI_WAIT_TGT] = 0;
     mi[MI_XS_LAYER] = -1;
     mi[MI_ROUTE_LAYER] = -1;
     mi[MI_WFAIL] = 0;

@@ -3,7 +3,6 @@
 
 #include <algorithm>
 #include <cstring>
-#include <map>
 
 namespace mkd {
 
@@ -33,19 +32,12 @@ PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t n_teams) {
 }
 
 CounterLayout make_counters(const Geometry& g, const PlanShape& s, int32_t max_batch) {
+  (void)s;
+  (void)max_batch;
   CounterLayout c{};
   int32_t at = 0;
-  c.x_ready = at++;
-  c.qkv_done = at++;
-  c.router_done = at++;
   c.attn_claim = at++;
   c.up_claim = at++;
-  c.comb = at;
-  at += g.n_kv;
-  c.attn_items = at;
-  at += max_batch * g.n_kv;
-  c.up_done = at;
-  at += g.n_experts;
   c.per_layer = (at + 15) / 16 * 16;
   c.global_base = c.per_layer * (g.n_layers + 1);
   c.total = c.global_base + G_COUNT;
@@ -216,39 +208,16 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
 
 std::string validate_plan(const Geometry& g, const Plan& P) {
   const int n = P.n_tasks();
-  const CounterLayout& c = P.ctr;
-  // static arrivals per counter, by global index
-  std::map<int32_t, std::vector<int32_t>> arrivals;
+  // Every descriptor is well formed.  The interpreter carries every data edge as tagged
+  // words and uses counters only for the claim queues: a descriptor asking for a counter
+  // wait or arrive would be ignored, so it is rejected.
   for (int k = 0; k < n; ++k) {
     const int32_t* d = P.global.data() + (size_t)k * D_WORDS;
     if (d[D_GIDX] != k) return "task " + std::to_string(k) + ": global index mismatch";
-    if (d[D_SIGNAL] >= 0) arrivals[d[D_SIGNAL]].push_back(k);
-  }
-  // static producers cover x_ready (embedding tasks for layer 0, output tasks of layer
-  // l-1 for layer l), qkv_done and router_done; attention combines arrive on comb from
-  // the attention claimers (dynamic: the last item of a (sequence, group)).
-  for (int k = 0; k < n; ++k) {
-    const int32_t* d = P.global.data() + (size_t)k * D_WORDS;
     const int op = d[D_OPCODE];
     if (op < OP_NOP || op >= OP_COUNT) return "task " + std::to_string(k) + ": bad opcode";
-    if (d[D_WAIT] < 0) continue;
-    if (d[D_WAIT] >= c.global_base) return "task " + std::to_string(k) + ": wait on a status counter";
-    const int layer = d[D_WAIT] / c.per_layer, off = d[D_WAIT] % c.per_layer;
-    int64_t avail = 0;
-    if (off >= c.comb && off < c.comb + g.n_kv) {
-      bool attn = false;
-      for (const Wave& w : P.waves)
-        if (w.layer == layer && w.kind == W_ATTN && w.count > 0 && w.first + w.count <= k) attn = true;
-      avail = attn ? P.batch : 0;
-    } else {
-      auto it = arrivals.find(d[D_WAIT]);
-      if (it != arrivals.end())
-        for (int32_t a : it->second) avail += a < k ? 1 : 0;
-    }
-    if (avail < d[D_TARGET])
-      return "task " + std::to_string(k) + " (op " + std::to_string(op) + ", layer " + std::to_string(d[D_LAYER]) +
-             ") waits for " + std::to_string(d[D_TARGET]) + " arrivals on counter " + std::to_string(d[D_WAIT]) +
-             " but only " + std::to_string(avail) + " producers precede it";
+    if (d[D_WAIT] >= 0 || d[D_SIGNAL] >= 0)
+      return "task " + std::to_string(k) + ": counter waits and arrives are not used by this interpreter";
   }
   // Edges carried by tagged data (no counter): the router logits (MoE-up claimers and
   // output tasks read them), the attention partials and combined output (output tasks),
