@@ -320,7 +320,22 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
   DevPlan* dp = nullptr;
   int r = get_plan(e, batch, &dp);
   if (r != MKD_OK) return r;
-  const int ppi = dp->plan.shape.pages_per_item;
+  // attention items per step: one team takes larger items once the step's items at the
+  // plan's size outnumber the CUs (every item costs a claim, a merge and a partial result),
+  // and the largest once they outnumber them four times over at that larger size
+  int ppi = dp->plan.shape.pages_per_item;
+  if (dp->plan.n_teams == 1) {
+    auto n_items = [&](int size) {
+      int64_t n = 0;
+      for (int b = 0; b < batch; ++b)
+        n += (int64_t)e->cfg.n_kv_heads * ((std::max(h_seq_lens[b], 0) / P + 1 + size - 1) / size);
+      return n;
+    };
+    if (n_items(ppi) > e->n_cu) {
+      ppi = e->opts.pages_per_item_long;
+      if (n_items(ppi) > 4 * (int64_t)e->n_cu) ppi = e->opts.pages_per_item_max;
+    }
+  }
   int64_t items = 0;
   for (int b = 0; b < batch; ++b) {
     const int32_t s = h_seq_lens[b];
@@ -341,6 +356,7 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
   Params p = e->base;
   p.n_teams = dp->plan.n_teams;
   p.shape = dp->plan.shape;
+  p.shape.pages_per_item = ppi;
   p.batch = batch;
   p.n_pages = n_pages;
   p.tokens = d_tokens;

@@ -89,6 +89,9 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   if (g.n_experts > 256) return "at most 256 experts";
   if (o.pages_per_item < 1 || o.pages_per_item > 64) return "pages_per_item must be in [1, 64]";
   if (o.pages_per_item_2 < 1 || o.pages_per_item_2 > 64) return "pages_per_item_2 must be in [1, 64]";
+  if (o.pages_per_item_long < o.pages_per_item || o.pages_per_item_max < o.pages_per_item_long ||
+      o.pages_per_item_max > 64)
+    return "pages_per_item <= pages_per_item_long <= pages_per_item_max <= 64 is required";
   // a GEMV tile holds at most 5 row steps per worker wave (7 workers, >= 1 row per step)
   if (o.rt_rows > 35 || 2 * o.up_rows > 35 || 2 * o.qkv_max_pairs > 35 || o.router_rows > 35 || o.lm_rows > 35)
     return "GEMV tiles are limited to 35 rows";

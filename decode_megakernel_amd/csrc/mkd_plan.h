@@ -29,6 +29,9 @@
 #ifndef MKD_PPI
 #define MKD_PPI 28  // batch 1, 8K context, 4 QKV tiles per head: 24 -> 388, 28 -> 405, 32 -> 400 tok/s
 #endif
+#ifndef MKD_PPI_LONG
+#define MKD_PPI_LONG 56  // batch 1, 32K context: 28 -> 257, 42 -> 312, 56 -> 321, 64 -> 311 tok/s
+#endif
 
 namespace mkd {
 
@@ -45,6 +48,12 @@ struct PlanOptions {
                                   // largest divisor of the expert inter size not above it is used
   int32_t pages_per_item = MKD_PPI;  // attention pages per claimed item, one team of 7 workers
   int32_t pages_per_item_2 = 6;  // the same with two teams of 3 workers each
+  // one team, when the step's attention items at pages_per_item outnumber the CUs (long
+  // contexts): larger items, since every item pays a claim, a merge and a partial result;
+  // when they still outnumber the CUs four times over (batch 1 at 256K: 56 -> 97, 64 -> 107
+  // tok/s; batch 4 at 64K: 315 -> 320), the largest, pages_per_item_max
+  int32_t pages_per_item_long = MKD_PPI_LONG;
+  int32_t pages_per_item_max = 64;
   int32_t teams = MKD_TEAMS;    // teams per workgroup: 1, 2, or 0 = 2 when batch <= two_team_max_batch
   int32_t two_team_max_batch = 4;
   int32_t qkv_max_pairs = 17;  // RoPE pairs per QKV tile at most (tile = 2x rows); a head is
