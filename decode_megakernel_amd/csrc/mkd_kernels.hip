@@ -1638,7 +1638,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     const int n_cl = c.d[D_ARG1], ci = c.d[D_ARG0];
     const int n_duty = p.batch * p.n_q;
     LAS float* stg = wreg;
-    const int CB = max(1, min(256, nw * wstride / (HD + 2)));  // chunks per staged batch
+    const int CB = max(1, min(64, nw * wstride / (HD + 2)));  // chunks per staged batch
     for (int dj = ci; dj < n_duty; dj += n_cl) {
       const int b = dj / p.n_q, qh = dj % p.n_q, g = qh / hpg, h = qh % hpg;
       int base_bg = 0, nch = 0;
@@ -1656,7 +1656,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
         const int ncb = min(CB, nch - cb0);
         const GAS uint64_t* src = p.attn_part + ((int64_t)(base_bg + cb0) * hpg + h) * (HD + 2);
         const int64_t cstride = (int64_t)hpg * (HD + 2);
-        const bool ok = team_poll<16>(
+        const bool ok = team_poll<8>(
             c, layer_tag(p.epoch, l), ncb * (HD + 2), [&](int i) { return src + (i / (HD + 2)) * cstride + i % (HD + 2); },
             [&](int i) -> LAS float& { return stg[i]; });
         if (c.ctl) ctl_set_ok(c, ok);
