@@ -335,6 +335,58 @@ def check_kv_append_slot_and_untouched_bytes():
     assert np.max(np.abs(oracle.bf16_to_f32(got) - kvec)) <= 1e-2 * np.max(np.abs(kvec))
 
 
+def _rope_complex(y, base, pos):
+    """Rotate-half RoPE written as complex multiplication: pair (i, i + hd/2) is the
+    complex number y_i + j*y_{i+hd/2}, turned by the angle pos * base^(-2i/hd) (fp64)."""
+    half = y.size // 2
+    z = y[:half].astype(np.complex128) + 1j * y[half:].astype(np.float64)
+    z *= np.exp(1j * pos * base ** (-2.0 * np.arange(half) / y.size))
+    return np.concatenate([z.real, z.imag])
+
+
+def check_qkv_rope_append_every_head():
+    # Every output of the QKV step, against fp64 NumPy: q_j = RoPE(W_q[j] x, pos) for
+    # every query head, and the slot written for every KV group holds bf16(RoPE(W_k[g] x,
+    # pos)) in the K page and bf16(W_v[g] x) (no rotation) in the V page, read back
+    # through the pool layout (K token-major, V dim-major).  Positions: the first slot of
+    # a fresh page and a slot in the middle of a page.
+    g = G
+    rng = np.random.default_rng(14)
+    H, hd, nq, nkv, P = g.hidden, g.head_dim, g.n_q_heads, g.n_kv_heads, g.page_size
+    w = _rand_bf16(rng, (g.qkv_rows, H), 0.2)
+    wf = oracle.bf16_to_f32(w).astype(np.float64)
+    x = rng.standard_normal(H).astype(np.float32)
+    y = wf @ x.astype(np.float64)
+    n_pages = 7
+    page_row = rng.permutation(n_pages)[:4].astype(np.int32)
+    for pos in (8, 9):
+        pool = _rand_bf16(rng, g.kv_layer_numel(n_pages))
+        before = pool.copy()
+        q = oracle.qkv_rope_append(g, pos, page_row, x, w, pool, n_pages)
+        for j in range(nq):
+            ref = _rope_complex(y[j * hd:(j + 1) * hd], g.rope_base, pos)
+            assert _rel(q[j * hd:(j + 1) * hd], ref) < 1e-5, ("q head", j, pos)
+        kview = pool[: n_pages * nkv * P * hd].reshape(n_pages, nkv, P, hd)
+        vview = pool[n_pages * nkv * P * hd:].reshape(n_pages, nkv, hd, P)
+        page, t = int(page_row[pos // P]), pos % P
+        for grp in range(nkv):
+            kref = _rope_complex(y[(nq + grp) * hd:(nq + grp + 1) * hd], g.rope_base, pos)
+            vref = y[(nq + nkv + grp) * hd:(nq + nkv + grp + 1) * hd]
+            kgot = oracle.bf16_to_f32(kview[page, grp, t, :]).astype(np.float64)
+            vgot = oracle.bf16_to_f32(vview[page, grp, :, t]).astype(np.float64)
+            # bf16 rounding: half an ulp, 2^-9 relative
+            assert np.all(np.abs(kgot - kref) <= 2.0 ** -8 * np.abs(kref) + 1e-30), ("k group", grp, pos)
+            assert np.all(np.abs(vgot - vref) <= 2.0 ** -8 * np.abs(vref) + 1e-30), ("v group", grp, pos)
+        # nothing but the slot changed
+        kview0 = before[: n_pages * nkv * P * hd].reshape(n_pages, nkv, P, hd)
+        vview0 = before[n_pages * nkv * P * hd:].reshape(n_pages, nkv, hd, P)
+        km = np.ones(kview.shape, bool)
+        km[page, :, t, :] = False
+        vm = np.ones(vview.shape, bool)
+        vm[page, :, :, t] = False
+        assert np.array_equal(kview[km], kview0[km]) and np.array_equal(vview[vm], vview0[vm])
+
+
 def check_batch_equals_single_runs():
     g = G
     wl, W, pool, pt, toks = _small_inputs(g, [9, 4, 14])

@@ -53,6 +53,13 @@ MUTATIONS = {
     "final_gamma_first": ("orc_lm_head(d, batch, h, norm + (int64_t)d->n_layers * H",
                           "orc_lm_head(d, batch, h, norm"),
     "layer_weights_fixed": ("w_o + l * H * nq * hd,", "w_o,"),
+    "qkv_q_no_rope": ("for (int32_t j = 0; j < nq; ++j) orc_rope(hd, d->rope_base, pos, y + j * hd);", ""),
+    "qkv_q_pos_plus_one": ("orc_rope(hd, d->rope_base, pos, y + j * hd)",
+                           "orc_rope(hd, d->rope_base, pos + 1, y + j * hd)"),
+    "qkv_rope_on_v": ("memcpy(q, y, sizeof(float) * (size_t)nq * hd);",
+                      "for (int32_t g = 0; g < nkv; ++g) orc_rope(hd, d->rope_base, pos, v + g * hd);\n"
+                      "  memcpy(q, y, sizeof(float) * (size_t)nq * hd);"),
+    "qkv_v_from_k_rows": ("float* v = y + (nq + nkv) * hd;", "float* v = y + nq * hd;"),
 }
 
 RUNNER = r"""
