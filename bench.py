@@ -228,7 +228,7 @@ def run(args):
     if args.trace:
         # one more step with the per-task trace on (not part of the timed region)
         from decode_megakernel_amd import trace as mtrace
-        desc, _, _ = eng.plan(batch, torch.cuda.get_device_properties(0).multi_processor_count)
+        desc, _ = eng.plan(torch.cuda.get_device_properties(0).multi_processor_count)
         buf = torch.zeros((desc.shape[0], 4), dtype=torch.int64, device="cuda")
         eng.set_trace(buf)
         step(args.warmup + args.steps)

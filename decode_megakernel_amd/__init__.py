@@ -1,9 +1,10 @@
 """Python binding of libmkd.so, the persistent decode megakernel for MI355X (gfx950).
 
 Argument marshalling only: every step of the decode runs in the HIP kernels behind
-the C-ABI declared in include/mkd.h.  PyTorch is used by callers for device memory
-and streams; tensors are passed as raw device pointers.  There is no fallback: if
-the library is missing or fails to load, importing the engine raises.
+the C-ABI declared in include/mkd.h.  PyTorch provides device memory (the engine's
+workspace is a torch tensor handed to mkd_set_workspace) and streams; tensors are
+passed as raw device pointers.  There is no fallback: if the library is missing or
+fails to load, creating an engine raises.
 """
 from __future__ import annotations
 
@@ -28,11 +29,17 @@ DEBUG_HIDDEN = 0
 DEBUG_TOPK_IDS = 1
 DEBUG_TOPK_W = 2
 DEBUG_ROUTER = 3
+DEBUG_Q = 4
+DEBUG_ATTN = 5
+DEBUG_ROUTE = 6
+ROUTE_WORDS = 1548
 DESC_WORDS = 32
+D_GIDX = 7  # descriptor word holding the task's position in the global order
 
 # every symbol include/mkd.h declares
-EXPORTS = ("mkd_create", "mkd_destroy", "mkd_load_weights", "mkd_set_mode", "mkd_decode_step",
-           "mkd_sync_status", "mkd_last_error", "mkd_debug_read", "mkd_plan_inspect",
+EXPORTS = ("mkd_create", "mkd_destroy", "mkd_workspace_bytes", "mkd_set_workspace",
+           "mkd_load_weights", "mkd_set_mode", "mkd_decode_step", "mkd_sync_status",
+           "mkd_set_watchdog", "mkd_last_error", "mkd_debug_read", "mkd_plan_inspect",
            "mkd_set_trace")
 
 
@@ -70,13 +77,16 @@ def lib():
         sig = {
             "mkd_create": ([P(Config), I32, I32, I32, P(VP)], I32),
             "mkd_destroy": ([VP], None),
+            "mkd_workspace_bytes": ([VP], ctypes.c_size_t),
+            "mkd_set_workspace": ([VP, VP, ctypes.c_size_t], I32),
+            "mkd_set_watchdog": ([VP, I32], I32),
             "mkd_load_weights": ([VP, P(Weights)], I32),
             "mkd_set_mode": ([VP, I32], I32),
             "mkd_decode_step": ([VP, VP, I32, VP, VP, VP, VP, VP, VP, I32, VP], I32),
             "mkd_sync_status": ([VP], I32),
             "mkd_last_error": ([VP], ctypes.c_char_p),
             "mkd_debug_read": ([VP, I32, VP, ctypes.c_size_t], I32),
-            "mkd_plan_inspect": ([VP, I32, I32, VP, I32, VP, P(I32), P(I32)], I32),
+            "mkd_plan_inspect": ([VP, I32, VP, I32, VP, P(I32)], I32),
             "mkd_set_trace": ([VP, VP, ctypes.c_size_t], I32),
         }
         for name, (args, res) in sig.items():
@@ -102,13 +112,16 @@ def _ptr(t) -> Optional[int]:
 
 
 class Engine:
-    """One mkd_engine.  device=-1 gives a host-only engine for plan inspection."""
+    """One mkd_engine.  device=-1 gives a host-only engine for plan inspection.  A device
+    engine gets its workspace from torch (a uint8 tensor of mkd_workspace_bytes bytes on
+    that device) unless `workspace=False`, in which case set_workspace() must be called."""
 
-    def __init__(self, geom, device: int, max_batch: int, max_pages_per_seq: int):
+    def __init__(self, geom, device: int, max_batch: int, max_pages_per_seq: int, workspace=True):
         self.geom = geom
         self.max_batch = max_batch
         self.max_pages = max_pages_per_seq
         self._cfg = config_of(geom)
+        self._ws = None
         h = ctypes.c_void_p()
         rc = lib().mkd_create(ctypes.byref(self._cfg), device, max_batch, max_pages_per_seq,
                               ctypes.byref(h))
@@ -116,11 +129,29 @@ class Engine:
             raise MkdError(rc, lib().mkd_last_error(None).decode())
         self._h = h
         self._weights = None
+        if device >= 0 and workspace:
+            import torch
+
+            self.set_workspace(torch.empty(self.workspace_bytes(), dtype=torch.uint8,
+                                           device=f"cuda:{device}"))
+
+    def workspace_bytes(self) -> int:
+        return int(lib().mkd_workspace_bytes(self._h))
+
+    def set_workspace(self, buf):
+        """buf: a device tensor of at least workspace_bytes() bytes, kept referenced."""
+        self._check(lib().mkd_set_workspace(self._h, _ptr(buf), buf.numel() * buf.element_size()))
+        self._ws = buf
+
+    def set_watchdog(self, polls: int):
+        self._check(lib().mkd_set_watchdog(self._h, int(polls)))
 
     def close(self):
         if getattr(self, "_h", None):
             lib().mkd_destroy(self._h)
             self._h = None
+        self._ws = None
+        self._weights = None
 
     def __del__(self):
         try:
@@ -160,10 +191,14 @@ class Engine:
 
     def debug_read(self, what: int, batch: int) -> np.ndarray:
         g = self.geom
+        qd = g.n_q_heads * g.head_dim
         shapes = {DEBUG_HIDDEN: ((g.n_layers + 1, batch, g.hidden), np.float32),
                   DEBUG_TOPK_IDS: ((g.n_layers, batch, g.top_k), np.int32),
                   DEBUG_TOPK_W: ((g.n_layers, batch, g.top_k), np.float32),
-                  DEBUG_ROUTER: ((g.n_layers, batch, g.n_experts), np.float32)}
+                  DEBUG_ROUTER: ((g.n_layers, batch, g.n_experts), np.float32),
+                  DEBUG_Q: ((g.n_layers, batch, qd), np.float32),
+                  DEBUG_ATTN: ((g.n_layers, batch, qd), np.float32),
+                  DEBUG_ROUTE: ((g.n_layers, ROUTE_WORDS), np.int32)}
         shape, dt = shapes[what]
         out = np.empty(shape, dtype=dt)
         self._check(lib().mkd_debug_read(self._h, what, out.ctypes.data, out.nbytes))
@@ -177,16 +212,15 @@ class Engine:
             self._check(lib().mkd_set_trace(self._h, _ptr(buf), buf.numel() * buf.element_size()))
         self._trace = buf
 
-    def plan(self, batch: int, n_cu: int):
-        """(descriptors [n_tasks][32] int32 grouped by task list, list offsets
-        [n_cu * n_teams + 1], n_teams); list cu * n_teams + t is team t of CU cu."""
+    def plan(self, n_cu: int):
+        """(descriptors [n_tasks][32] int32 grouped by CU, list offsets [n_cu + 1]); the
+        list of CU c is desc[offs[c]:offs[c + 1]], in execution order."""
         n = ctypes.c_int32()
-        teams = ctypes.c_int32()
-        rc = lib().mkd_plan_inspect(self._h, batch, n_cu, None, 0, None, ctypes.byref(n), ctypes.byref(teams))
+        rc = lib().mkd_plan_inspect(self._h, n_cu, None, 0, None, ctypes.byref(n))
         if rc not in (MKD_OK, MKD_ERR_CAPACITY):
             self._check(rc)
         desc = np.empty((n.value, DESC_WORDS), dtype=np.int32)
-        offs = np.empty(2 * n_cu + 1, dtype=np.int32)
-        self._check(lib().mkd_plan_inspect(self._h, batch, n_cu, desc.ctypes.data, n.value,
-                                           offs.ctypes.data, ctypes.byref(n), ctypes.byref(teams)))
-        return desc, offs[: n_cu * teams.value + 1].copy(), teams.value
+        offs = np.empty(n_cu + 1, dtype=np.int32)
+        self._check(lib().mkd_plan_inspect(self._h, n_cu, desc.ctypes.data, n.value,
+                                           offs.ctypes.data, ctypes.byref(n)))
+        return desc, offs

@@ -16,10 +16,13 @@ namespace mkd {
 //   QKV_PROJ            -> OP_QKV (RoPE and the paged-KV append in the epilogue)
 //   ROUTER_GEMM         -> OP_ROUTER
 //   ROUTER_TOPK, ROUTE_FINALIZE, MOE_GATHER
-//                       -> computed in LDS at the start of the OP_MOE_UP claimer of each
-//                          CU and reused by its OP_OUT task (no extra counter hop)
+//                       -> built once per layer by the first OP_ROUTER tile after the
+//                          layer's logits are in, published as one tagged table that
+//                          every MoE-up claimer and output task copies into its LDS
 //   ATTN_DRAIN + ATTN_DECODE -> OP_ATTN (claims (seq, kv group, page chunk) items)
-//   ATTN_COMBINE        -> done by the last attention item of a (seq, kv group)
+//   ATTN_COMBINE        -> the tail of OP_ATTN: after its claim loop, claimer i merges
+//                          the chunks of the query heads (b, h) with (b*nq + h) mod
+//                          n_claimers == i, from the items' tagged partials
 //   MOE_UPGATE_ACT_DRAIN -> OP_MOE_UP
 //   O_PROJ, MOE_DOWN_DRAIN, MOE_COMBINE and the fused residual add + RMSNorm
 //                       -> OP_OUT, one task per residual row tile: the tile's O-proj rows
@@ -40,7 +43,10 @@ enum Opcode : int32_t {
 };
 
 // ---------------------------------------------------------------- descriptor
-// 32 int32 per task, 128 bytes, read with scalar loads.
+// 32 int32 per task, 128 bytes, read with scalar loads.  The pages' descriptor also
+// carries the barrier to wait on, its target and the barrier to signal; here every data
+// edge is a tagged word that the consumer polls, so those fields do not exist and words
+// 7..31 are zero (reserved).
 enum DescField : int32_t {
   D_OPCODE = 0,
   D_LAYER = 1,
@@ -48,11 +54,8 @@ enum DescField : int32_t {
   D_ARG1 = 3,   // row count / kv group / claimer count
   D_ARG2 = 4,
   D_ARG3 = 5,
-  D_WAIT = 6,   // counter index to wait on (-1: none)
-  D_TARGET = 7, // count to wait for
-  D_SIGNAL = 8, // counter index to arrive on (-1: none)
-  D_WAVE = 9,   // wave id in the schedule (for the op-per-kernel ablation)
-  D_GIDX = 10,  // position in the global (flattened) order
+  D_WAVE = 6,   // wave id in the schedule (for the op-per-kernel ablation)
+  D_GIDX = 7,   // position in the global (flattened) order
   D_WORDS = 32,
 };
 
@@ -102,7 +105,6 @@ struct Params {
   int32_t n_layers, hidden, n_q, n_kv, head_dim, n_experts, top_k, inter, vocab, page;
   float rms_eps;
   int32_t batch, max_batch, max_pages, n_pages;
-  int32_t n_teams;  // teams per workgroup (1: 8 waves, 2: 4 waves each)
   PlanShape shape;
   CounterLayout ctr;
   // weights (bf16)
@@ -137,7 +139,7 @@ struct Params {
   uint32_t* counters;
   // task lists
   const int32_t* tasks;      // [n_tasks][32]
-  const int32_t* cu_offsets; // [n_wg * n_teams + 1]: task list of team t of workgroup i is list i * n_teams + t
+  const int32_t* cu_offsets; // [n_wg + 1]: task list of workgroup i
   int32_t max_attn_items;    // capacity of attn_part
   int32_t spin_limit;        // watchdog: polls before a wait gives up
   uint32_t epoch;            // this step's number in [1, 2^24): tagged words carry (epoch << 8) | layer

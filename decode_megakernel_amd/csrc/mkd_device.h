@@ -226,7 +226,6 @@ struct DParams {
   int32_t n_layers, hidden, n_q, n_kv, head_dim, n_experts, top_k, inter, vocab, page;
   float rms_eps;
   int32_t batch, max_batch, max_pages, n_pages;
-  int32_t n_teams;
   PlanShape shape;
   CounterLayout ctr;
   const GAS uint16_t* embed;
@@ -282,7 +281,6 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.n_experts = p.n_experts; d.top_k = p.top_k; d.inter = p.inter; d.vocab = p.vocab; d.page = p.page;
   d.rms_eps = p.rms_eps;
   d.batch = p.batch; d.max_batch = p.max_batch; d.max_pages = p.max_pages; d.n_pages = p.n_pages;
-  d.n_teams = p.n_teams;
   d.shape.n_rt = p.shape.n_rt; d.shape.rt_rows = p.shape.rt_rows;
   d.shape.up_rows = p.shape.up_rows; d.shape.n_up_tiles = p.shape.n_up_tiles;
   d.shape.pages_per_item = p.shape.pages_per_item; d.shape.qkv_rows = p.shape.qkv_rows; d.shape.qkv_tph = p.shape.qkv_tph;

@@ -2,17 +2,18 @@
 //
 // Host side of one step ("Inside the megakernel serving engine for North Mini Code",
 // section "The serving engine around the kernel": clear per-step state, select the
-// schedule, launch the megakernel): validate the arguments, pick the cached plan for
-// the batch size, zero the step's counters with a fill kernel, and make one
-// cooperative launch of the persistent interpreter (or, in the ablation mode, one
-// launch per wave of tasks).
+// schedule, launch the megakernel): validate the arguments, choose the step's attention
+// item size, zero the step's counters with a fill kernel, and make one cooperative launch
+// of the persistent interpreter (or, in the ablation mode, one launch per wave of tasks).
+// The schedule is built once per engine (section "The task scheduler: mapping tasks to
+// SMs") and copied into the caller's workspace when the workspace is handed over, so a
+// step allocates nothing and copies nothing synchronously.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
-#include <map>
 #include <memory>
 #include <string>
 #include <vector>
@@ -22,7 +23,7 @@
 #include "mkd_plan.h"
 
 namespace mkd {
-hipError_t launch_clear(uint32_t* counters, int32_t n, hipStream_t s);
+hipError_t launch_clear(uint32_t* words, int64_t n, hipStream_t s);
 hipError_t launch_persistent(const Params& p, int n_wg, hipStream_t s);
 hipError_t launch_wave(const Params& p, int32_t first, int32_t count, hipStream_t s);
 int geometry_index(int hidden, int inter, int hd);
@@ -34,11 +35,13 @@ namespace {
 
 thread_local std::string g_create_error;
 
-struct DevPlan {
-  Plan plan;
-  int32_t* d_per_cu = nullptr;
-  int32_t* d_offsets = nullptr;
-  int32_t* d_global = nullptr;
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// One region of the workspace: byte offset from the workspace start, size, and whether it
+// holds tagged words (cleared again when the step epoch wraps).
+struct Region {
+  size_t off = 0, bytes = 0;
+  bool tagged = false;
 };
 
 }  // namespace
@@ -49,34 +52,27 @@ struct mkd_engine {
   int32_t device = -1;
   int32_t max_batch = 0, max_pages = 0, n_cu = 0;
   PlanOptions opts;
-  PlanShape shape{};
-  CounterLayout ctr{};
+  Plan plan;  // built in mkd_create (device engines)
   bool have_weights = false;
-  mkd_weights w{};
   int32_t mode = MKD_MODE_MEGAKERNEL;
-  // workspace
-  void* ws = nullptr;
+  // workspace layout (offsets) and the caller's buffer
+  Region r_h, r_ss, r_q, r_kvflag, r_part, r_attn_o, r_router, r_tbl, r_topk_ids, r_topk_w, r_act, r_inv_freq,
+      r_rope, r_dummy, r_counters, r_tasks_cu, r_tasks_global, r_offsets;
   size_t ws_bytes = 0;
+  char* ws = nullptr;
   Params base{};
   int32_t max_attn_items = 0;
-  std::map<int32_t, DevPlan> plans;
   std::string err;
   int32_t last_batch = 0;
   hipStream_t last_stream = nullptr;
   uint64_t* trace = nullptr;
   int32_t trace_cap = 0;
-  uint32_t epoch = 0;  // number of the last step, in [1, 2^24) (0: none yet; the workspace starts zeroed)
-  std::vector<std::pair<void*, size_t>> tagged;  // workspace buffers of tagged words
-  ~mkd_engine() {
-    if (device >= 0) {
-      hipSetDevice(device);
-      for (auto& kv : plans) {
-        hipFree(kv.second.d_per_cu);
-        hipFree(kv.second.d_offsets);
-        hipFree(kv.second.d_global);
-      }
-      hipFree(ws);
-    }
+  int32_t spin_limit = 4000000;
+  uint32_t epoch = 0;  // number of the last step, in [1, 2^24) (0: none since the workspace was cleared)
+  std::vector<const Region*> regions() const {
+    return {&r_h, &r_ss, &r_q, &r_kvflag, &r_part, &r_attn_o, &r_router, &r_tbl, &r_topk_ids,
+            &r_topk_w, &r_act, &r_inv_freq, &r_rope, &r_dummy, &r_counters, &r_tasks_cu,
+            &r_tasks_global, &r_offsets};
   }
 };
 
@@ -114,7 +110,45 @@ std::string check_config(const mkd_config& c, int32_t max_batch, int32_t max_pag
   return "";
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// Workspace layout of an engine (offsets only; the plan must be built).
+void layout(mkd_engine* e) {
+  const mkd_config& c = e->cfg;
+  const int64_t L = c.n_layers, B = e->max_batch, H = c.hidden, E = c.n_experts, K = c.top_k;
+  const int64_t QD = (int64_t)c.n_q_heads * c.head_dim, hpg = c.n_q_heads / c.n_kv_heads;
+  const int64_t n_rt = e->plan.shape.n_rt;
+  size_t at = 0;
+  auto put = [&](Region& r, size_t bytes, bool tagged) {
+    r.off = at;
+    r.bytes = bytes;
+    r.tagged = tagged;
+    at += align256(bytes);
+  };
+  const size_t w8 = sizeof(uint64_t);
+  put(e->r_h, w8 * (L + 1) * B * H, true);
+  put(e->r_ss, w8 * (L + 1) * B * n_rt, true);
+  put(e->r_q, w8 * L * B * QD, true);
+  put(e->r_kvflag, w8 * L * 2 * c.n_kv_heads * 64, true);
+  put(e->r_part, w8 * (size_t)e->max_attn_items * hpg * (c.head_dim + 2), true);
+  put(e->r_attn_o, w8 * L * B * QD, true);
+  put(e->r_router, w8 * L * B * E, true);
+  put(e->r_tbl, w8 * L * kRouteTableWords, true);
+  put(e->r_topk_ids, sizeof(int32_t) * L * B * K, false);
+  put(e->r_topk_w, sizeof(float) * L * B * K, false);
+  put(e->r_act, w8 * L * B * K * c.moe_inter, true);
+  put(e->r_inv_freq, sizeof(double) * c.head_dim / 2, false);
+  put(e->r_rope, w8 * B * c.head_dim, true);
+  put(e->r_dummy, 1024, false);
+  put(e->r_counters, sizeof(uint32_t) * (size_t)e->plan.ctr.total, false);
+  put(e->r_tasks_cu, sizeof(int32_t) * e->plan.per_cu.size(), false);
+  put(e->r_tasks_global, sizeof(int32_t) * e->plan.global.size(), false);
+  put(e->r_offsets, sizeof(int32_t) * e->plan.cu_offsets.size(), false);
+  e->ws_bytes = at;
+}
+
+template <typename T>
+T* at_ws(mkd_engine* e, const Region& r) {
+  return reinterpret_cast<T*>(e->ws + r.off);
+}
 
 }  // namespace
 
@@ -139,25 +173,14 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
                      cfg->n_experts, cfg->top_k, cfg->moe_inter, cfg->vocab, cfg->page_size};
   e->max_batch = max_batch;
   e->max_pages = max_pages_per_seq;
-  e->shape = make_shape(e->geom, e->opts, 1);
-  e->ctr = make_counters(e->geom, e->shape, max_batch);
-  {
-    const int ppi = std::min(e->opts.pages_per_item, e->opts.pages_per_item_2);
-    e->max_attn_items = max_batch * cfg->n_kv_heads * ((max_pages_per_seq + ppi - 1) / ppi);
-  }
+  e->max_attn_items = max_batch * cfg->n_kv_heads * ((max_pages_per_seq + e->opts.pages_per_item - 1) /
+                                                     e->opts.pages_per_item);
   if (hip_device < 0) {  // host-only engine: plan inspection
-    e->n_cu = 0;
     *out = e.release();
     return MKD_OK;
   }
-  hipError_t rc = hipSetDevice(hip_device);
-  if (rc != hipSuccess) {
-    g_create_error = std::string("hipSetDevice: ") + hipGetErrorString(rc);
-    return MKD_ERR_HIP;
-  }
-  e->device = hip_device;
   hipDeviceProp_t prop;
-  rc = hipGetDeviceProperties(&prop, hip_device);
+  hipError_t rc = hipGetDeviceProperties(&prop, hip_device);
   if (rc != hipSuccess) {
     g_create_error = std::string("hipGetDeviceProperties: ") + hipGetErrorString(rc);
     return MKD_ERR_HIP;
@@ -166,65 +189,15 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
     g_create_error = "device does not support cooperative launches";
     return MKD_ERR_HIP;
   }
+  e->device = hip_device;
   e->n_cu = prop.multiProcessorCount;
-  // workspace layout
-  const int64_t L = cfg->n_layers, B = max_batch, H = cfg->hidden, E = cfg->n_experts, K = cfg->top_k;
-  const int64_t QD = (int64_t)cfg->n_q_heads * cfg->head_dim, hpg = cfg->n_q_heads / cfg->n_kv_heads;
+  const std::string pbad = build_plan(e->geom, e->opts, max_batch, e->n_cu, &e->plan);
+  if (!pbad.empty()) {
+    g_create_error = "plan: " + pbad;
+    return MKD_ERR_ARG;
+  }
+  layout(e.get());
   Params& p = e->base;
-  const size_t part_bytes = sizeof(uint64_t) * (size_t)e->max_attn_items * hpg * (cfg->head_dim + 2);
-  const size_t attn_o_bytes = sizeof(uint64_t) * L * B * QD;
-  const size_t router_bytes = sizeof(uint64_t) * L * B * E;
-  const size_t tbl_bytes = sizeof(uint64_t) * L * kRouteTableWords;
-  const size_t act_bytes = sizeof(uint64_t) * L * B * K * cfg->moe_inter;
-  const size_t h_bytes = sizeof(uint64_t) * (L + 1) * B * H;
-  const size_t q_bytes = sizeof(uint64_t) * L * B * QD;
-  const size_t flag_bytes = sizeof(uint64_t) * L * 2 * cfg->n_kv_heads * 64;
-  const size_t ss_bytes = sizeof(uint64_t) * (L + 1) * B * e->shape.n_rt;
-  const size_t rope_bytes = sizeof(uint64_t) * B * cfg->head_dim;
-  std::vector<std::pair<size_t, void**>> slots = {
-      {h_bytes, (void**)&p.h},
-      {ss_bytes, (void**)&p.ss},
-      {q_bytes, (void**)&p.q},
-      {flag_bytes, (void**)&p.kvflag},
-      {part_bytes, (void**)&p.attn_part},
-      {attn_o_bytes, (void**)&p.attn_o},
-      {router_bytes, (void**)&p.router},
-      {tbl_bytes, (void**)&p.route_tbl},
-      {sizeof(int32_t) * L * B * K, (void**)&p.topk_ids},
-      {sizeof(float) * L * B * K, (void**)&p.topk_w},
-      {act_bytes, (void**)&p.moe_act},
-      {sizeof(double) * cfg->head_dim / 2, (void**)&p.inv_freq},
-      {rope_bytes, (void**)&p.rope},
-      {1024, (void**)&p.dummy},
-      {sizeof(uint32_t) * (size_t)e->ctr.total, (void**)&p.counters},
-  };
-  size_t total = 0;
-  for (auto& s : slots) total += align256(s.first);
-  rc = hipMalloc(&e->ws, total);
-  if (rc != hipSuccess) {
-    g_create_error = std::string("hipMalloc workspace: ") + hipGetErrorString(rc);
-    return MKD_ERR_HIP;
-  }
-  e->ws_bytes = total;
-  size_t at = 0;
-  for (auto& s : slots) {
-    *s.second = (char*)e->ws + at;
-    at += align256(s.first);
-  }
-  e->tagged = {{p.attn_part, part_bytes}, {p.attn_o, attn_o_bytes}, {p.router, router_bytes}, {p.route_tbl, tbl_bytes},
-               {p.moe_act, act_bytes}, {p.h, h_bytes}, {p.ss, ss_bytes}, {p.rope, rope_bytes},
-               {p.q, q_bytes}, {p.kvflag, flag_bytes}};
-  rc = hipMemset(e->ws, 0, total);
-  if (rc == hipSuccess) {
-    std::vector<double> inv(cfg->head_dim / 2);
-    for (int i = 0; i < cfg->head_dim / 2; ++i)
-      inv[i] = std::pow((double)cfg->rope_base, -2.0 * (double)i / (double)cfg->head_dim);
-    rc = hipMemcpy((void*)p.inv_freq, inv.data(), sizeof(double) * inv.size(), hipMemcpyHostToDevice);
-  }
-  if (rc != hipSuccess) {
-    g_create_error = std::string("workspace init: ") + hipGetErrorString(rc);
-    return MKD_ERR_HIP;
-  }
   p.n_layers = cfg->n_layers;
   p.hidden = cfg->hidden;
   p.n_q = cfg->n_q_heads;
@@ -238,21 +211,73 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
   p.rms_eps = cfg->rms_eps;
   p.max_batch = max_batch;
   p.max_pages = max_pages_per_seq;
-  p.shape = e->shape;
-  p.ctr = e->ctr;
+  p.shape = e->plan.shape;
+  p.ctr = e->plan.ctr;
   p.max_attn_items = e->max_attn_items;
-  p.spin_limit = 4000000;
   *out = e.release();
   return MKD_OK;
 }
 
 void mkd_destroy(mkd_engine* eng) { delete eng; }
 
+size_t mkd_workspace_bytes(const mkd_engine* e) { return (e && e->device >= 0) ? e->ws_bytes : 0; }
+
+int mkd_set_workspace(mkd_engine* e, void* dev_ptr, size_t bytes) {
+  if (!e) return MKD_ERR_ARG;
+  if (e->device < 0) return fail(e, MKD_ERR_STATE, "host-only engine has no workspace");
+  if (!dev_ptr) return fail(e, MKD_ERR_ARG, "workspace pointer is NULL");
+  if ((uintptr_t)dev_ptr & 255) return fail(e, MKD_ERR_ARG, "workspace must be 256-byte aligned");
+  if (bytes < e->ws_bytes)
+    return fail(e, MKD_ERR_ARG, "workspace of " + std::to_string(bytes) + " bytes is smaller than the " +
+                                    std::to_string(e->ws_bytes) + " bytes mkd_workspace_bytes asks for");
+  hipError_t rc = hipSetDevice(e->device);
+  if (rc != hipSuccess) return hip_fail(e, rc, "hipSetDevice");
+  e->ws = (char*)dev_ptr;
+  Params& p = e->base;
+  p.h = at_ws<uint64_t>(e, e->r_h);
+  p.ss = at_ws<uint64_t>(e, e->r_ss);
+  p.q = at_ws<uint64_t>(e, e->r_q);
+  p.kvflag = at_ws<uint64_t>(e, e->r_kvflag);
+  p.attn_part = at_ws<uint64_t>(e, e->r_part);
+  p.attn_o = at_ws<uint64_t>(e, e->r_attn_o);
+  p.router = at_ws<uint64_t>(e, e->r_router);
+  p.route_tbl = at_ws<uint64_t>(e, e->r_tbl);
+  p.topk_ids = at_ws<int32_t>(e, e->r_topk_ids);
+  p.topk_w = at_ws<float>(e, e->r_topk_w);
+  p.moe_act = at_ws<uint64_t>(e, e->r_act);
+  p.inv_freq = at_ws<double>(e, e->r_inv_freq);
+  p.rope = at_ws<uint64_t>(e, e->r_rope);
+  p.dummy = e->ws + e->r_dummy.off;
+  p.counters = at_ws<uint32_t>(e, e->r_counters);
+  // every word starts at zero: tagged words then carry epoch 0, which no step uses
+  rc = launch_clear((uint32_t*)e->ws, (int64_t)(e->ws_bytes / 4), nullptr);
+  std::vector<double> inv(e->cfg.head_dim / 2);
+  for (int i = 0; i < e->cfg.head_dim / 2; ++i)
+    inv[i] = std::pow((double)e->cfg.rope_base, -2.0 * (double)i / (double)e->cfg.head_dim);
+  if (rc == hipSuccess) rc = hipDeviceSynchronize();
+  if (rc == hipSuccess) rc = hipMemcpy((void*)p.inv_freq, inv.data(), sizeof(double) * inv.size(), hipMemcpyHostToDevice);
+  const Plan& P = e->plan;
+  if (rc == hipSuccess)
+    rc = hipMemcpy(e->ws + e->r_tasks_cu.off, P.per_cu.data(), sizeof(int32_t) * P.per_cu.size(), hipMemcpyHostToDevice);
+  if (rc == hipSuccess)
+    rc = hipMemcpy(e->ws + e->r_tasks_global.off, P.global.data(), sizeof(int32_t) * P.global.size(),
+                   hipMemcpyHostToDevice);
+  if (rc == hipSuccess)
+    rc = hipMemcpy(e->ws + e->r_offsets.off, P.cu_offsets.data(), sizeof(int32_t) * P.cu_offsets.size(),
+                   hipMemcpyHostToDevice);
+  if (rc != hipSuccess) {
+    e->ws = nullptr;
+    return hip_fail(e, rc, "workspace initialisation");
+  }
+  e->epoch = 0;
+  e->last_batch = 0;
+  return MKD_OK;
+}
+
 int mkd_load_weights(mkd_engine* e, const mkd_weights* w) {
   if (!e) return MKD_ERR_ARG;
   if (!w || !w->embed || !w->norm || !w->w_qkv || !w->w_o || !w->w_router || !w->w_gate_up || !w->w_down)
     return fail(e, MKD_ERR_ARG, "every weight pointer must be non-NULL");
-  e->w = *w;
   e->base.embed = (const uint16_t*)w->embed;
   e->base.norm = (const uint16_t*)w->norm;
   e->base.w_qkv = (const uint16_t*)w->w_qkv;
@@ -271,35 +296,10 @@ int mkd_set_mode(mkd_engine* e, int32_t mode) {
   return MKD_OK;
 }
 
-static int get_plan(mkd_engine* e, int32_t batch, DevPlan** out) {
-  auto it = e->plans.find(batch);
-  if (it != e->plans.end()) {
-    *out = &it->second;
-    return MKD_OK;
-  }
-  DevPlan dp;
-  const std::string bad = build_plan(e->geom, e->opts, e->max_batch, batch, e->n_cu, &dp.plan);
-  if (!bad.empty()) return fail(e, MKD_ERR_ARG, "plan: " + bad);
-  hipError_t rc = hipMalloc(&dp.d_per_cu, sizeof(int32_t) * dp.plan.per_cu.size());
-  if (rc == hipSuccess) rc = hipMalloc(&dp.d_global, sizeof(int32_t) * dp.plan.global.size());
-  if (rc == hipSuccess) rc = hipMalloc(&dp.d_offsets, sizeof(int32_t) * dp.plan.cu_offsets.size());
-  if (rc == hipSuccess)
-    rc = hipMemcpy(dp.d_per_cu, dp.plan.per_cu.data(), sizeof(int32_t) * dp.plan.per_cu.size(),
-                   hipMemcpyHostToDevice);
-  if (rc == hipSuccess)
-    rc = hipMemcpy(dp.d_global, dp.plan.global.data(), sizeof(int32_t) * dp.plan.global.size(),
-                   hipMemcpyHostToDevice);
-  if (rc == hipSuccess)
-    rc = hipMemcpy(dp.d_offsets, dp.plan.cu_offsets.data(), sizeof(int32_t) * dp.plan.cu_offsets.size(),
-                   hipMemcpyHostToDevice);
-  if (rc != hipSuccess) {
-    hipFree(dp.d_per_cu);
-    hipFree(dp.d_global);
-    hipFree(dp.d_offsets);
-    return hip_fail(e, rc, "plan upload");
-  }
-  auto ins = e->plans.emplace(batch, dp);
-  *out = &ins.first->second;
+int mkd_set_watchdog(mkd_engine* e, int32_t polls) {
+  if (!e) return MKD_ERR_ARG;
+  if (polls < 1) return fail(e, MKD_ERR_ARG, "the watchdog bound must be at least one poll");
+  e->spin_limit = polls;
   return MKD_OK;
 }
 
@@ -309,34 +309,13 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
   if (!e) return MKD_ERR_ARG;
   if (e->device < 0) return fail(e, MKD_ERR_STATE, "host-only engine cannot decode");
   if (!e->have_weights) return fail(e, MKD_ERR_STATE, "weights not loaded");
+  if (!e->ws) return fail(e, MKD_ERR_STATE, "no workspace: call mkd_set_workspace first");
   if (batch < 1 || batch > e->max_batch)
     return fail(e, MKD_ERR_CAPACITY, "batch must be in [1, max_batch]");
   if (!d_tokens || !d_seq_lens || !h_seq_lens || !d_page_table || !kv_pool || !d_logits)
     return fail(e, MKD_ERR_ARG, "NULL pointer argument");
   if (n_pages < 1) return fail(e, MKD_ERR_ARG, "n_pages must be positive");
   const int P = e->cfg.page_size;
-  hipError_t rc = hipSetDevice(e->device);
-  if (rc != hipSuccess) return hip_fail(e, rc, "hipSetDevice");
-  DevPlan* dp = nullptr;
-  int r = get_plan(e, batch, &dp);
-  if (r != MKD_OK) return r;
-  // attention items per step: one team takes larger items once the step's items at the
-  // plan's size outnumber the CUs (every item costs a claim, a merge and a partial result),
-  // and the largest once they outnumber them four times over at that larger size
-  int ppi = dp->plan.shape.pages_per_item;
-  if (dp->plan.n_teams == 1) {
-    auto n_items = [&](int size) {
-      int64_t n = 0;
-      for (int b = 0; b < batch; ++b)
-        n += (int64_t)e->cfg.n_kv_heads * ((std::max(h_seq_lens[b], 0) / P + 1 + size - 1) / size);
-      return n;
-    };
-    if (n_items(ppi) > e->n_cu) {
-      ppi = e->opts.pages_per_item_long;
-      if (n_items(ppi) > 4 * (int64_t)e->n_cu) ppi = e->opts.pages_per_item_max;
-    }
-  }
-  int64_t items = 0;
   for (int b = 0; b < batch; ++b) {
     const int32_t s = h_seq_lens[b];
     if (s < 0) return fail(e, MKD_ERR_ARG, "negative sequence length");
@@ -350,12 +329,24 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
                                           ") = " + std::to_string(pg) + " is outside [0, n_pages)");
       }
     }
-    items += (int64_t)e->cfg.n_kv_heads * ((s / P + 1 + ppi - 1) / ppi);
   }
-  if (items > e->max_attn_items) return fail(e, MKD_ERR_CAPACITY, "attention work exceeds the workspace");
+  // Attention items per step: larger items once the step's items at the plan's size
+  // outnumber the CUs (every item costs a claim, a merge and a partial result), and the
+  // largest once they outnumber them four times over at that larger size.
+  auto n_items = [&](int size) {
+    int64_t n = 0;
+    for (int b = 0; b < batch; ++b) n += (int64_t)e->cfg.n_kv_heads * ((h_seq_lens[b] / P + 1 + size - 1) / size);
+    return n;
+  };
+  int ppi = e->plan.shape.pages_per_item;
+  if (n_items(ppi) > e->n_cu) {
+    ppi = e->opts.pages_per_item_long;
+    if (n_items(ppi) > 4 * (int64_t)e->n_cu) ppi = e->opts.pages_per_item_max;
+  }
+  if (n_items(ppi) > e->max_attn_items) return fail(e, MKD_ERR_CAPACITY, "attention work exceeds the workspace");
+  hipError_t rc = hipSetDevice(e->device);
+  if (rc != hipSuccess) return hip_fail(e, rc, "hipSetDevice");
   Params p = e->base;
-  p.n_teams = dp->plan.n_teams;
-  p.shape = dp->plan.shape;
   p.shape.pages_per_item = ppi;
   p.batch = batch;
   p.n_pages = n_pages;
@@ -364,30 +355,32 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
   p.page_table = d_page_table;
   p.kv_pool = (uint16_t*)kv_pool;
   p.logits = d_logits;
-  p.cu_offsets = dp->d_offsets;
+  p.cu_offsets = (const int32_t*)(e->ws + e->r_offsets.off);
   p.trace = e->trace;
   p.trace_cap = e->trace_cap;
+  p.spin_limit = e->spin_limit;
   // A fresh epoch per step (tagged words carry (epoch << 8) | layer).  Epoch 0 is never
   // used, so zeroed words never read as ready; when the 24-bit epoch wraps, the tagged
   // buffers are cleared first, so no word from 2^24 steps ago can pass for a new one.
   hipStream_t s = (hipStream_t)stream;
   if (++e->epoch >= (1u << 24)) {
     e->epoch = 1;
-    for (const auto& t : e->tagged) {
-      rc = launch_clear((uint32_t*)t.first, (int32_t)(t.second / 4), s);
+    for (const Region* r : e->regions()) {
+      if (!r->tagged) continue;
+      rc = launch_clear((uint32_t*)(e->ws + r->off), (int64_t)(r->bytes / 4), s);
       if (rc != hipSuccess) return hip_fail(e, rc, "tag clear");
     }
   }
   p.epoch = e->epoch;
-  rc = launch_clear(p.counters, e->ctr.total, s);
+  rc = launch_clear(p.counters, e->plan.ctr.total, s);
   if (rc != hipSuccess) return hip_fail(e, rc, "counter clear");
   if (e->mode == MKD_MODE_MEGAKERNEL) {
-    p.tasks = dp->d_per_cu;
+    p.tasks = (const int32_t*)(e->ws + e->r_tasks_cu.off);
     rc = launch_persistent(p, e->n_cu, s);
     if (rc != hipSuccess) return hip_fail(e, rc, "megakernel launch");
   } else {
-    p.tasks = dp->d_global;
-    for (const Wave& w : dp->plan.waves) {
+    p.tasks = (const int32_t*)(e->ws + e->r_tasks_global.off);
+    for (const Wave& w : e->plan.waves) {
       if (w.count == 0) continue;
       rc = launch_wave(p, w.first, w.count, s);
       if (rc != hipSuccess) return hip_fail(e, rc, "wave launch");
@@ -401,22 +394,19 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
 
 int mkd_sync_status(mkd_engine* e) {
   if (!e) return MKD_ERR_ARG;
-  if (e->device < 0) return MKD_OK;
+  if (e->device < 0 || !e->ws) return MKD_OK;
   hipError_t rc = hipSetDevice(e->device);
   if (rc == hipSuccess) rc = hipStreamSynchronize(e->last_stream);
   if (rc != hipSuccess) return hip_fail(e, rc, "stream synchronize");
+  uint32_t* gblock = e->base.counters + e->plan.ctr.global_base;
   uint32_t st[G_COUNT];
-  rc = hipMemcpy(st, e->base.counters + e->ctr.global_base, sizeof(st), hipMemcpyDeviceToHost);
+  rc = hipMemcpy(st, gblock, sizeof(st), hipMemcpyDeviceToHost);
   if (rc != hipSuccess) return hip_fail(e, rc, "status read");
   if (st[G_ERR_CODE] == 0) return MKD_OK;
   char buf[256];
-  if (st[G_ERR_CODE] == 1 && (int32_t)st[G_ERR_CTR] == G_TAGGED) {
+  if (st[G_ERR_CODE] == 1) {
     snprintf(buf, sizeof(buf), "watchdog: task %u waited on tagged data (saw tag %u, wanted %u)", st[G_ERR_TASK],
              st[G_ERR_SEEN], st[G_ERR_WANT]);
-    fail(e, MKD_ERR_DEADLOCK, buf);
-  } else if (st[G_ERR_CODE] == 1) {
-    snprintf(buf, sizeof(buf), "watchdog: task %u waited on counter %u (saw %u, wanted %u)", st[G_ERR_TASK],
-             st[G_ERR_CTR], st[G_ERR_SEEN], st[G_ERR_WANT]);
     fail(e, MKD_ERR_DEADLOCK, buf);
   } else {
     snprintf(buf, sizeof(buf), "invalid input on device: task %u saw %d (limit %u)", st[G_ERR_TASK],
@@ -424,7 +414,8 @@ int mkd_sync_status(mkd_engine* e) {
     fail(e, MKD_ERR_ARG, buf);
   }
   const int code = st[G_ERR_CODE] == 1 ? MKD_ERR_DEADLOCK : MKD_ERR_ARG;
-  hipMemset(e->base.counters + e->ctr.global_base, 0, sizeof(st));
+  std::memset(st, 0, sizeof(st));
+  hipMemcpy(gblock, st, sizeof(st), hipMemcpyHostToDevice);
   return code;
 }
 
@@ -440,36 +431,39 @@ const char* mkd_last_error(const mkd_engine* e) { return e ? e->err.c_str() : g_
 
 int mkd_debug_read(mkd_engine* e, int32_t what, void* dst, size_t bytes) {
   if (!e || !dst) return MKD_ERR_ARG;
-  if (e->device < 0) return fail(e, MKD_ERR_STATE, "host-only engine");
+  if (e->device < 0 || !e->ws) return fail(e, MKD_ERR_STATE, "no workspace");
   const int64_t B = e->last_batch, L = e->cfg.n_layers, mb = e->max_batch;
+  const int64_t QD = (int64_t)e->cfg.n_q_heads * e->cfg.head_dim;
   if (B < 1) return fail(e, MKD_ERR_STATE, "no step has run");
-  int64_t inner = 0, outer = 0;  // inner: 4-byte values per (layer, token) row
-  const char* src = nullptr;
-  bool tagged = false;  // the buffer holds tagged words: the value is each word's low half
+  // rows: `outer` blocks of `rows` rows of `inner` 4-byte values; consecutive blocks are
+  // `stride` rows apart in the workspace
+  int64_t inner = 0, outer = 0, rows = B, stride = mb;
+  const Region* r = nullptr;
   switch (what) {
-    case MKD_DEBUG_HIDDEN:
-      inner = e->cfg.hidden; outer = L + 1; src = (const char*)e->base.h; tagged = true; break;
-    case MKD_DEBUG_TOPK_IDS: inner = e->cfg.top_k; outer = L; src = (const char*)e->base.topk_ids; break;
-    case MKD_DEBUG_TOPK_W: inner = e->cfg.top_k; outer = L; src = (const char*)e->base.topk_w; break;
-    case MKD_DEBUG_ROUTER:
-      inner = e->cfg.n_experts; outer = L; src = (const char*)e->base.router; tagged = true; break;
+    case MKD_DEBUG_HIDDEN: inner = e->cfg.hidden; outer = L + 1; r = &e->r_h; break;
+    case MKD_DEBUG_TOPK_IDS: inner = e->cfg.top_k; outer = L; r = &e->r_topk_ids; break;
+    case MKD_DEBUG_TOPK_W: inner = e->cfg.top_k; outer = L; r = &e->r_topk_w; break;
+    case MKD_DEBUG_ROUTER: inner = e->cfg.n_experts; outer = L; r = &e->r_router; break;
+    case MKD_DEBUG_Q: inner = QD; outer = L; r = &e->r_q; break;
+    case MKD_DEBUG_ATTN: inner = QD; outer = L; r = &e->r_attn_o; break;
+    case MKD_DEBUG_ROUTE: inner = kRouteTableWords; outer = L; rows = 1; stride = 1; r = &e->r_tbl; break;
     default: return fail(e, MKD_ERR_ARG, "unknown debug buffer");
   }
-  if (bytes < (size_t)(outer * B * inner * 4)) return fail(e, MKD_ERR_ARG, "debug buffer too small");
+  if (bytes < (size_t)(outer * rows * inner * 4)) return fail(e, MKD_ERR_ARG, "debug buffer too small");
   hipError_t rc = hipSetDevice(e->device);
   if (rc == hipSuccess) rc = hipStreamSynchronize(e->last_stream);
-  // one copy per layer row (a strided 2-D copy was seen to leave the destination
-  // untouched under a profiler's interception)
-  const int64_t wb = tagged ? 8 : 4;  // bytes per stored word
-  std::vector<uint64_t> row(tagged ? (size_t)(B * inner) : 0);
+  // one copy per block (a strided 2-D copy was seen to leave the destination untouched
+  // under a profiler's interception); tagged words keep the value in their low half
+  const int64_t wb = r->tagged ? 8 : 4;
+  std::vector<uint64_t> row(r->tagged ? (size_t)(rows * inner) : 0);
   for (int64_t o = 0; o < outer && rc == hipSuccess; ++o) {
-    char* d = (char*)dst + o * B * inner * 4;
-    const char* sp = src + o * mb * inner * wb;
-    if (!tagged) {
-      rc = hipMemcpy(d, sp, (size_t)(B * inner * 4), hipMemcpyDeviceToHost);
+    char* d = (char*)dst + o * rows * inner * 4;
+    const char* sp = e->ws + r->off + o * stride * inner * wb;
+    if (!r->tagged) {
+      rc = hipMemcpy(d, sp, (size_t)(rows * inner * 4), hipMemcpyDeviceToHost);
     } else {
-      rc = hipMemcpy(row.data(), sp, (size_t)(B * inner * 8), hipMemcpyDeviceToHost);
-      for (int64_t i = 0; i < B * inner; ++i) {
+      rc = hipMemcpy(row.data(), sp, (size_t)(rows * inner * 8), hipMemcpyDeviceToHost);
+      for (int64_t i = 0; i < rows * inner; ++i) {
         const uint32_t v = (uint32_t)row[i];
         std::memcpy(d + i * 4, &v, 4);
       }
@@ -479,14 +473,13 @@ int mkd_debug_read(mkd_engine* e, int32_t what, void* dst, size_t bytes) {
   return MKD_OK;
 }
 
-int mkd_plan_inspect(mkd_engine* e, int32_t batch, int32_t n_cu, int32_t* desc, int32_t max_tasks,
-                     int32_t* cu_offsets, int32_t* n_tasks, int32_t* n_teams) {
+int mkd_plan_inspect(mkd_engine* e, int32_t n_cu, int32_t* desc, int32_t max_tasks, int32_t* cu_offsets,
+                     int32_t* n_tasks) {
   if (!e || !n_tasks) return MKD_ERR_ARG;
   Plan plan;
-  const std::string bad = build_plan(e->geom, e->opts, e->max_batch, batch, n_cu, &plan);
+  const std::string bad = build_plan(e->geom, e->opts, e->max_batch, n_cu, &plan);
   if (!bad.empty()) return fail(e, MKD_ERR_ARG, "plan: " + bad);
   *n_tasks = plan.n_tasks();
-  if (n_teams) *n_teams = plan.n_teams;
   if (plan.n_tasks() > max_tasks) return fail(e, MKD_ERR_CAPACITY, "max_tasks too small");
   if (desc) std::memcpy(desc, plan.per_cu.data(), sizeof(int32_t) * plan.per_cu.size());
   if (cu_offsets) std::memcpy(cu_offsets, plan.cu_offsets.data(), sizeof(int32_t) * plan.cu_offsets.size());

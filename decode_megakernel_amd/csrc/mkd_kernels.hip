@@ -6,20 +6,15 @@
 //    step, walking a host-built task list in global memory; dependencies are counters
 //    that producers increment and consumers spin on.
 //  - "The threadblock shape": every opcode runs under one fixed shape with fixed
-//    roles.  Here: 8 wave64s forming one team of 8 waves or two teams of 4 (small
-//    batches).  A team walks its own task list; its first wave is the controller
-//    (counter polls, queue claims, activation staging into LDS, epilogue stores and
-//    arrives) and the others are workers that only stream weights / K-V from HBM and
-//    compute.  With two teams the attention branch (QKV, attention, O-proj) and the
-//    MoE branch (router, expert up, expert down) of a parallel layer run side by side
-//    on every CU, so one team streams while the other resolves a dependency.  On gfx9 the
-//    vector-memory counter is in order and shared by loads, stores and atomics, so a
-//    wave with weight loads in flight cannot get a quick answer from a poll, a small
-//    load or a store; keeping every latency-critical access on a wave that never
-//    streams weights is what lets the workers keep HBM busy while the controller
-//    resolves dependencies.  Barriers only order LDS, so worker loads stay in flight
-//    across them; a two-team workgroup synchronises each team with an LDS counter
-//    instead of the workgroup-wide s_barrier.
+//    roles.  Here: 8 wave64s per workgroup walking one task list; the first wave is the
+//    controller (polls of tagged data, queue claims, activation staging into LDS,
+//    epilogue stores) and the other seven are workers that stream weights / K-V from
+//    HBM and compute.  On gfx9 the vector-memory counter is in order and shared by
+//    loads, stores and atomics, so a wave with weight loads in flight cannot get a quick
+//    answer from a poll, a small load or a store; keeping every latency-critical access
+//    on a wave that never streams weights is what lets the workers keep HBM busy while
+//    the controller resolves dependencies.  Barriers only order LDS, so worker loads
+//    stay in flight across them.
 //  - "Tasks": the GEMM opcodes share one body (a bf16 GEMV tile held in worker
 //    registers, fp32 accumulation, wave reductions); QKV applies RoPE in the
 //    epilogue; attention is split over KV slices and combined; routing scores the
@@ -36,27 +31,23 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "mkd_common.h"
 #include "mkd_device.h"
 
 namespace mkd {
 
 // ------------------------------------------------------------------ LDS layout
-// One workgroup per CU is forced by the LDS footprint (> half of the 160 KB).  Each team
-// owns a region: activation staging / attention pages and merge (xs), per-row results of a
-// tile (rowsum), routing tables (route) and controller state (misc).  One team of 8 waves
-// has 144 KB of xs (16 tokens x 2048 fp32 plus room for the attention pages held in LDS);
-// each of two teams of 4 waves has 44 KB (4 tokens).
+// One workgroup per CU is forced by the LDS footprint (> half of the 160 KB).  Regions:
+// activation staging / attention pages and merge (xs: 144 KB, 16 tokens x 2048 fp32 plus
+// room for the attention pages held in LDS), per-row results of a tile (rowsum), routing
+// tables (route) and controller state (misc).
 constexpr int kLdsRowsumBytes = 8192;
 constexpr int kLdsRouteBytes = 6400;
 constexpr int kLdsMiscBytes = 1024;
-constexpr int kXsBytes1 = 147456;
-constexpr int kXsBytes2 = 45056;
-constexpr int kTeamBytes1 = kXsBytes1 + kLdsRowsumBytes + kLdsRouteBytes + kLdsMiscBytes;
-constexpr int kTeamBytes2 = kXsBytes2 + kLdsRowsumBytes + kLdsRouteBytes + kLdsMiscBytes;
-constexpr int kLdsBar = kTeamBytes1;   // [2] team barrier counters
-constexpr int kLdsBytes = kLdsBar + 64;
-static_assert(2 * kTeamBytes2 <= kLdsBar, "two team regions must fit");
+constexpr int kXsBytes = 147456;
+constexpr int kLdsBytes = kXsBytes + kLdsRowsumBytes + kLdsRouteBytes + kLdsMiscBytes;
 #ifndef MKD_MAXP
 #define MKD_MAXP 1
 #endif
@@ -79,9 +70,8 @@ struct Smem {
   LAS int32_t* route;
   LAS int32_t* mi;  // misc ints
   LAS float* mf;    // misc floats (inverse RMS per token)
-  __device__ Smem(LAS char* lds, int team, int n_teams) {
-    const int xb = n_teams == 1 ? kXsBytes1 : kXsBytes2;
-    LAS char* base = lds + team * (n_teams == 1 ? kTeamBytes1 : kTeamBytes2);
+  __device__ explicit Smem(LAS char* base) {
+    const int xb = kXsBytes;
     xs = reinterpret_cast<LAS float*>(base);
     rowsum = reinterpret_cast<LAS float*>(base + xb);
     route = reinterpret_cast<LAS int32_t*>(base + xb + kLdsRowsumBytes);
@@ -121,34 +111,26 @@ struct Ctx {
   Smem s;
   const CAS int32_t* d;     // descriptor
   int32_t task;             // global task index
-  int32_t tw, lane, wi;     // wave within the team (uniform), lane, worker index (tw - 1)
-  int32_t nw;               // worker waves in the team (7 or 3)
-  int32_t tid, tthreads;    // thread index within the team, threads in the team
-  LAS uint32_t* barc;       // the team's barrier counter
-  bool ctl;                 // the team's first wave: the controller
+  int32_t tw, lane, wi;     // wave in the workgroup (uniform), lane, worker index (tw - 1)
+  int32_t nw;               // worker waves (7)
+  int32_t tid, tthreads;    // thread index in the workgroup, threads in the workgroup
+  bool ctl;                 // the first wave: the controller
 };
 
 __device__ __forceinline__ GAS uint32_t* layer_ctr(const DParams& p, int l, int off) {
   return p.counters + (int64_t)l * p.ctr.per_layer + off;
 }
-// Team barrier.  A whole-workgroup team uses s_barrier; a 4-wave team counts arrivals in
-// its LDS counter (the counter only grows; an arrival's old value names the barrier
-// instance, whose last arrival brings the count to the next multiple of the team size).
-__device__ __forceinline__ void bar(const Ctx& c) {
-  if (c.nw == kWaves - 1) {
-    __syncthreads();
-    return;
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  uint32_t old = 0;
-  if (c.lane == 0) old = __hip_atomic_fetch_add(c.barc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
-  const uint32_t waves = (uint32_t)(c.nw + 1);
-  const uint32_t target = (old / waves + 1u) * waves;
-  while (__hip_atomic_load(c.barc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
-    __builtin_amdgcn_s_sleep(1);
-  asm volatile("" ::: "memory");
+// Cached length of sequence b as the kernel uses it: clamped to what the page-table row
+// can map (0 .. max_pages * page - 1), so that no index derived from it leaves the page
+// table, the attention items or their partials.  The host validates its mirror of the
+// lengths; a device length outside that range is reported by the embedding task
+// (check_seq_lens) and the step goes on with the clamped value.
+__device__ __forceinline__ int seq_len_of(const DParams& p, int b) {
+  return min(max(p.seq_lens[b], 0), p.max_pages * p.page - 1);
 }
+
+// Workgroup barrier (orders LDS; worker loads in flight stay in flight across it).
+__device__ __forceinline__ void bar(const Ctx&) { __syncthreads(); }
 
 // ------------------------------------------------------------------ controller primitives
 // Claimer queues: claimer i of n takes item i first without touching the queue, then
@@ -539,10 +521,13 @@ __device__ __forceinline__ bool op_embed(Ctx& c) {
     if (c.lane == 0) st_tag(p.ss + (int64_t)b * p.shape.n_rt + rt, t, layer_tag(p.epoch, 0));
   }
   if (rt == 0) {
+    // device lengths outside what the page-table row maps are reported (and clamped)
+    if (c.lane < B && p.seq_lens[c.lane] != seq_len_of(p, c.lane))
+      report_error(p, 2u, c.task, -1, (uint32_t)p.seq_lens[c.lane], (uint32_t)(p.max_pages * p.page));
     const int half = p.head_dim / 2;
     for (int i = c.lane; i < B * half; i += 64) {
       const int b = i / half, k = i % half;
-      const double ang = (double)p.seq_lens[b] * p.inv_freq[k];
+      const double ang = (double)seq_len_of(p, b) * p.inv_freq[k];
       st_tag(p.rope + 2 * i, (float)cos(ang), layer_tag(p.epoch, 0));
       st_tag(p.rope + 2 * i + 1, (float)sin(ang), layer_tag(p.epoch, 0));
     }
@@ -566,7 +551,7 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
   auto stage = [&]() { return team_stage_x(c, l, fresh); };
   if (!c.ctl) {
     // the whole tile in LDS after the staged input and its sums of squares, when it fits
-    const int xs_floats = (c.nw == kWaves - 1 ? kXsBytes1 : kXsBytes2) / 4;
+    const int xs_floats = kXsBytes / 4;
     const int used = B * H + B * p.shape.n_rt;
     if (B == 1 && used + 2 * PB * K / 2 <= xs_floats)
       return gemv_tile_lds<K, 1>(c, src, 2 * PB, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum, stage,
@@ -589,12 +574,18 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
     for (int i = c.lane; i < PB * B; i += 64) {
       const int r = i / B, b = i % B, dim = j0 + r;
       const float a = c.s.rowsum[r * B + b] * c.s.mf[b], bb = c.s.rowsum[(PB + r) * B + b] * c.s.mf[b];
-      const int pos = p.seq_lens[b];
+      const int pos = seq_len_of(p, b);
       float o1 = a, o2 = bb;
       if (rope_head) {
         const GAS uint64_t* rp = p.rope + ((int64_t)b * half + dim) * 2;
         uint64_t cw = i == c.lane ? cw0 : ld_tag(rp), sw = i == c.lane ? sw0 : ld_tag(rp + 1);
+        int32_t spins = 0;
         while (!tag_is(cw, ep0) || !tag_is(sw, ep0)) {  // written long before (embedding task)
+          if ((++spins & 63) == 0 && aborted(p)) break;
+          if (spins > p.spin_limit) {
+            report_error(p, 1u, c.task, G_TAGGED, (uint32_t)(cw >> 32), ep0);
+            break;
+          }
           __builtin_amdgcn_s_sleep(1);
           cw = ld_tag(rp);
           sw = ld_tag(rp + 1);
@@ -896,14 +887,14 @@ __device__ __forceinline__ void ctl_route_ahead(Ctx& c, int l) {
 __device__ __forceinline__ int attn_item_count(const DParams& p) {
   const int ppi = p.shape.pages_per_item;
   int n = 0;
-  for (int b = 0; b < p.batch; ++b) n += ((p.seq_lens[b] / p.page + 1 + ppi - 1) / ppi) * p.n_kv;
+  for (int b = 0; b < p.batch; ++b) n += ((seq_len_of(p, b) / p.page + 1 + ppi - 1) / ppi) * p.n_kv;
   return min(n, p.max_attn_items);
 }
 
 // ------------------------------------------------------------------ OP_MOE_UP (claimer)
 // Items are (active expert, tile of up_rows activation rows); weights = up_rows gate rows
-// and the matching up rows; epilogue silu(gate) * up for every token routed to the expert;
-// each item arrives on the expert's up counter.
+// and the matching up rows; epilogue silu(gate) * up for every token routed to the expert,
+// stored as tagged words that the output tasks poll.
 //
 // Static streaming (when at least kMinFreeClaimers claimers have no attention item): the
 // free claimers take the items round robin (free claimer f: items f, f + n_free, ...) and
@@ -1118,7 +1109,7 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
   const int l = c.d[D_LAYER], rt = c.d[D_ARG0];
   const int R = p.shape.rt_rows, r0 = rt * R, H = p.hidden, B = p.batch, k = p.top_k, E = p.n_experts;
   const int QD = p.n_q * p.head_dim, NSO = QD / KH;  // O-proj column blocks (<= 4)
-  const int xs_floats = (c.nw == kWaves - 1 ? kXsBytes1 : kXsBytes2) / 4;
+  const int xs_floats = kXsBytes / 4;
   LAS float* acc_a = c.s.rowsum + kMaccOffset;  // [R][B] O-proj rows
   LAS float* acc_m = acc_a + R * kMaxBatch;     // [R][B] expert rows
   const int64_t hstride = (int64_t)p.max_batch * H;
@@ -1286,15 +1277,16 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
 //   O^T[d][h] += V^T[d][t] P^T[t][h]    (v_mfma_f32_16x16x16_bf16; V pages are stored
 //                                        dim-major so V^T rows are contiguous)
 // The cached pages are streamed before the controller's wait for this layer's QKV
-// tiles; only the page holding the new token is read after it.  The last item of a
-// (sequence, group) merges all chunks (log-sum-exp) with every wave.
+// tiles; only the page holding the new token is read after it.  Each item leaves its
+// partial (o, m, l per head) as tagged words; after its claim loop, every claimer merges
+// the chunks of the query heads assigned to it (log-sum-exp, below).
 __device__ __forceinline__ void attn_map(const DParams& p, int idx, int& b, int& g, int& chunk, int& nchunks,
                                          int& base_bg) {
   const int ppi = p.shape.pages_per_item;
   b = -1;
   int acc = 0;
   for (int bb = 0; bb < p.batch; ++bb) {
-    const int npg = p.seq_lens[bb] / p.page + 1;
+    const int npg = seq_len_of(p, bb) / p.page + 1;
     const int nit = (npg + ppi - 1) / ppi;
     if (idx < acc + nit * p.n_kv) {
       const int local = idx - acc;
@@ -1324,7 +1316,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
   // kMaxLdsPages); its unnormalised outputs reuse the start of that region once its pages
   // are consumed.
   const int attn_fixed = 16 * HD + 2 * nw * 16 + 16 * (HD + 2);
-  const int xs_floats = (nw == kWaves - 1 ? kXsBytes1 : kXsBytes2) / 4;
+  const int xs_floats = kXsBytes / 4;
   const int keep = p.batch * p.hidden + attn_fixed + nw * hpg * HD <= xs_floats ? p.batch * p.hidden : 0;
   const int page_floats = p.page * HD;  // K and V of one page, bf16
   const int n_lds = min(kMaxLdsPages, (xs_floats - keep - attn_fixed) / nw / page_floats);
@@ -1346,7 +1338,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     uint32_t nxt = 0;  // controller: claim reply for the next item
     int b, g = 0, chunk = 0, nchunks = 0, base_bg = 0;
     attn_map(p, idx, b, g, chunk, nchunks, base_bg);
-    const int pos = p.seq_lens[b];
+    const int pos = seq_len_of(p, b);
     const int npg = pos / p.page + 1, last = npg - 1;
     const int c0 = chunk * ppi, c1 = min(npg, c0 + ppi);
     u32x4 kr[MAXP][NK];
@@ -1643,7 +1635,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
       const int b = dj / p.n_q, qh = dj % p.n_q, g = qh / hpg, h = qh % hpg;
       int base_bg = 0, nch = 0;
       for (int bb = 0; bb <= b; ++bb) {
-        const int nit = (p.seq_lens[bb] / p.page + 1 + ppi - 1) / ppi;
+        const int nit = (seq_len_of(p, bb) / p.page + 1 + ppi - 1) / ppi;
         if (bb == b) {
           base_bg += g * nit;
           nch = nit;
@@ -1704,19 +1696,14 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
 
 #define MKD_EXEC(NAME, BODY)                                                                          \
   template <class G>                                                                                  \
-  __device__ __forceinline__ bool NAME(KParams* kp_in, LAS char* lds_in, const CAS int32_t* d_in, int32_t task_in, \
-                                       int32_t team_in) {                                             \
+  __device__ __forceinline__ bool NAME(KParams* kp_in, LAS char* lds_in, const CAS int32_t* d_in, int32_t task_in) { \
     KParams* kp = (KParams*)uniform_u64((uint64_t)kp_in);                                             \
     const CAS int32_t* d = (const CAS int32_t*)uniform_u64((uint64_t)d_in);                           \
     LAS char* lds = (LAS char*)(uintptr_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_in); \
-    const int32_t team = __builtin_amdgcn_readfirstlane(team_in);                                     \
-    const int32_t n_teams = kp->n_teams;                                                              \
-    const int32_t wpt = kWaves / n_teams;                                                             \
-    const int32_t tw = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6) - team * wpt);      \
+    const int32_t tw = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));                   \
     const int32_t lane = (int32_t)(threadIdx.x & 63);                                                 \
-    Ctx c{kp, Smem(lds, team, n_teams), d, __builtin_amdgcn_readfirstlane(task_in), tw, lane, tw - 1,  \
-          wpt - 1, tw * 64 + lane, wpt * 64, reinterpret_cast<LAS uint32_t*>(lds + kLdsBar) + team,   \
-          tw == 0};                                                                                   \
+    Ctx c{kp, Smem(lds), d, __builtin_amdgcn_readfirstlane(task_in), tw, lane, tw - 1,                \
+          kWaves - 1, tw * 64 + lane, kThreads, tw == 0};                                             \
     BODY                                                                                              \
   }
 
@@ -1729,21 +1716,21 @@ MKD_EXEC(exec_out, return (op_out<G::kHidden, G::kInter>(c));)
 MKD_EXEC(exec_attn, return op_attn<G::kHd>(c);)
 
 template <class G>
-__device__ __forceinline__ bool run_task(KParams* kp, LAS char* lds, const CAS int32_t* d, int32_t task, int32_t team) {
+__device__ __forceinline__ bool run_task(KParams* kp, LAS char* lds, const CAS int32_t* d, int32_t task) {
   switch (d[D_OPCODE]) {
-    case OP_EMBED: return exec_embed<G>(kp, lds, d, task, team);
-    case OP_QKV: return exec_qkv<G>(kp, lds, d, task, team);
-    case OP_ROUTER: return exec_router<G>(kp, lds, d, task, team);
-    case OP_LM_HEAD: return exec_lm_head<G>(kp, lds, d, task, team);
-    case OP_MOE_UP: return exec_moe_up<G>(kp, lds, d, task, team);
-    case OP_OUT: return exec_out<G>(kp, lds, d, task, team);
-    case OP_ATTN: return exec_attn<G>(kp, lds, d, task, team);
+    case OP_EMBED: return exec_embed<G>(kp, lds, d, task);
+    case OP_QKV: return exec_qkv<G>(kp, lds, d, task);
+    case OP_ROUTER: return exec_router<G>(kp, lds, d, task);
+    case OP_LM_HEAD: return exec_lm_head<G>(kp, lds, d, task);
+    case OP_MOE_UP: return exec_moe_up<G>(kp, lds, d, task);
+    case OP_OUT: return exec_out<G>(kp, lds, d, task);
+    case OP_ATTN: return exec_attn<G>(kp, lds, d, task);
     default: return true;
   }
 }
 
-// Trace record of a finished task (the team controller's lane 0; fields in LDS were set
-// by the task).  `list` = workgroup * teams + team.
+// Trace record of a finished task (the controller's lane 0; fields in LDS were set by the
+// task).  `list` = the workgroup.
 __device__ __forceinline__ void trace_task(KParams* kp, LAS int32_t* mi, const CAS int32_t* d, uint64_t t0,
                                            bool leader, int list) {
   GAS uint64_t* trace = gas(kp->trace);
@@ -1766,7 +1753,7 @@ __device__ __forceinline__ void trace_task(KParams* kp, LAS int32_t* mi, const C
   }
 }
 
-// Team state that lives across tasks, set before the workgroup's first barrier: the
+// Workgroup state that lives across tasks, set before the workgroup's first barrier: the
 // workers read the routing-table layer and the claim entries, so their initial values
 // must be visible before any task starts (LDS keeps the previous workgroup's contents).
 __device__ __forceinline__ void init_team_state(LAS int32_t* mi, bool leader) {
@@ -1789,23 +1776,18 @@ __device__ __forceinline__ void reset_task_state(LAS int32_t* mi, bool leader) {
   }
 }
 
-// Persistent interpreter: team t of workgroup i walks task list i * teams + t.  Every wave
-// of a team calls every task of its list; the tasks' own barriers keep its controller and
-// workers in step.
+// Persistent interpreter: workgroup i walks task list i.  Every wave calls every task of
+// the list; the tasks' own barriers keep the controller and the workers in step.
 template <class G>
 __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params prm) {
   __shared__ __align__(16) char lds_raw[kLdsBytes];
   LAS char* lds = (LAS char*)lds_raw;
   KParams* kp = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();
-  const int n_teams = prm.n_teams;
-  const int wpt = kWaves / n_teams;
-  const int team = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) / wpt);
-  const bool leader = (int)threadIdx.x == team * wpt * 64;
-  LAS int32_t* mi = Smem(lds, team, n_teams).mi;
-  if (threadIdx.x < 2) reinterpret_cast<LAS uint32_t*>(lds + kLdsBar)[threadIdx.x] = 0u;
+  const bool leader = threadIdx.x == 0;
+  LAS int32_t* mi = Smem(lds).mi;
   init_team_state(mi, leader);
   __syncthreads();
-  const int list = (int)blockIdx.x * n_teams + team;
+  const int list = (int)blockIdx.x;
   const CAS int32_t* offs = cas(prm.cu_offsets);
   const int begin = offs[list], end = offs[list + 1];
   for (int t = begin; t < end; ++t) {
@@ -1826,7 +1808,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params prm) {
 #endif
     reset_task_state(mi, leader);
     const uint64_t t0 = kpt->trace ? wall_clock64() : 0;
-    const bool ok = run_task<G>(kpt, lds, d, t, team);
+    const bool ok = run_task<G>(kpt, lds, d, t);
     trace_task(kpt, mi, d, t0, leader, list);
 #ifndef MKD_NO_DESC_PREFETCH
     asm volatile("" ::"v"(dpre));
@@ -1835,26 +1817,26 @@ __global__ void __launch_bounds__(kThreads, 1) mk_persistent(Params prm) {
   }
 }
 
-// Ablation: one launch per wave of tasks; block i (one team) runs task first + i.
+// Ablation: one launch per wave of tasks; block i runs task first + i.
 template <class G>
 __global__ void __launch_bounds__(kThreads, 1) mk_wave(Params prm, int32_t first) {
   __shared__ __align__(16) char lds_raw[kLdsBytes];
   LAS char* lds = (LAS char*)lds_raw;
   KParams* kp = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();
-  LAS int32_t* mi = Smem(lds, 0, prm.n_teams).mi;
-  if (threadIdx.x == 0) reinterpret_cast<LAS uint32_t*>(lds + kLdsBar)[0] = 0u;
+  LAS int32_t* mi = Smem(lds).mi;
   init_team_state(mi, threadIdx.x == 0);
   reset_task_state(mi, threadIdx.x == 0);
   __syncthreads();
   const int32_t t = first + (int32_t)blockIdx.x;
   const CAS int32_t* d = cas(prm.tasks) + (int64_t)t * D_WORDS;
   const uint64_t t0 = prm.trace ? wall_clock64() : 0;
-  run_task<G>(kp, lds, d, t, 0);
+  run_task<G>(kp, lds, d, t);
   trace_task(kp, mi, d, t0, threadIdx.x == 0, (int)blockIdx.x);
 }
 
-__global__ void mk_clear(uint32_t* counters, int32_t n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) counters[i] = 0u;
+__global__ void mk_clear(uint32_t* words, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    words[i] = 0u;
 }
 
 }  // namespace mkd
@@ -1862,8 +1844,9 @@ __global__ void mk_clear(uint32_t* counters, int32_t n) {
 // ------------------------------------------------------------------ launch wrappers
 namespace mkd {
 
-hipError_t launch_clear(uint32_t* counters, int32_t n, hipStream_t s) {
-  hipLaunchKernelGGL(mk_clear, dim3(64), dim3(256), 0, s, counters, n);
+hipError_t launch_clear(uint32_t* words, int64_t n, hipStream_t s) {
+  const int64_t blocks = std::min<int64_t>(1024, std::max<int64_t>(1, (n + 255) / 256));
+  hipLaunchKernelGGL(mk_clear, dim3((unsigned)blocks), dim3(256), 0, s, words, n);
   return hipGetLastError();
 }
 
@@ -1886,8 +1869,8 @@ hipError_t launch_persistent(const Params& p, int n_wg, hipStream_t s) {
 
 hipError_t launch_wave(const Params& p, int32_t first, int32_t count, hipStream_t s) {
   const int gi = geometry_index(p.hidden, p.inter, p.head_dim);
-  if (gi == 0) hipLaunchKernelGGL(mk_wave<GeomFull>, dim3(count), dim3(kThreads / p.n_teams), 0, s, p, first);
-  else if (gi == 1) hipLaunchKernelGGL(mk_wave<GeomTiny>, dim3(count), dim3(kThreads / p.n_teams), 0, s, p, first);
+  if (gi == 0) hipLaunchKernelGGL(mk_wave<GeomFull>, dim3(count), dim3(kThreads), 0, s, p, first);
+  else if (gi == 1) hipLaunchKernelGGL(mk_wave<GeomTiny>, dim3(count), dim3(kThreads), 0, s, p, first);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

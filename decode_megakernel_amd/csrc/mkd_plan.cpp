@@ -6,11 +6,6 @@
 
 namespace mkd {
 
-int32_t plan_teams(const PlanOptions& o, int32_t batch) {
-  if (o.teams == 1 || o.teams == 2) return o.teams;
-  return batch <= o.two_team_max_batch ? 2 : 1;
-}
-
 // MoE-up item rows: the largest divisor of the expert inter size not above the option.
 static int32_t up_rows_for(const Geometry& g, const PlanOptions& o) {
   int32_t r = std::max(1, std::min(o.up_rows, g.inter));
@@ -18,22 +13,20 @@ static int32_t up_rows_for(const Geometry& g, const PlanOptions& o) {
   return r;
 }
 
-PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t n_teams) {
+PlanShape make_shape(const Geometry& g, const PlanOptions& o) {
   PlanShape s{};
   s.rt_rows = o.rt_rows;
   s.n_rt = g.hidden / o.rt_rows;
   s.up_rows = up_rows_for(g, o);
   s.n_up_tiles = g.inter / s.up_rows;
-  s.pages_per_item = n_teams == 2 ? o.pages_per_item_2 : o.pages_per_item;
+  s.pages_per_item = o.pages_per_item;
   s.qkv_rows = 2 * o.qkv_max_pairs;
   s.router_rows = o.router_rows;
   s.lm_rows = o.lm_rows;
   return s;
 }
 
-CounterLayout make_counters(const Geometry& g, const PlanShape& s, int32_t max_batch) {
-  (void)s;
-  (void)max_batch;
+CounterLayout make_counters(const Geometry& g) {
   CounterLayout c{};
   int32_t at = 0;
   c.attn_claim = at++;
@@ -49,8 +42,7 @@ namespace {
 struct Emitter {
   std::vector<int32_t>* v;
   int32_t wave_id = 0;
-  int32_t emit(int32_t op, int32_t layer, int32_t a0, int32_t a1, int32_t a2, int32_t a3, int32_t wait,
-               int32_t target, int32_t signal) {
+  int32_t emit(int32_t op, int32_t layer, int32_t a0, int32_t a1, int32_t a2, int32_t a3) {
     const size_t at = v->size();
     v->resize(at + D_WORDS, 0);
     int32_t* d = v->data() + at;
@@ -60,9 +52,6 @@ struct Emitter {
     d[D_ARG1] = a1;
     d[D_ARG2] = a2;
     d[D_ARG3] = a3;
-    d[D_WAIT] = wait;
-    d[D_TARGET] = target;
-    d[D_SIGNAL] = signal;
     d[D_WAVE] = wave_id;
     d[D_GIDX] = (int32_t)(at / D_WORDS);
     return d[D_GIDX];
@@ -71,9 +60,8 @@ struct Emitter {
 
 }  // namespace
 
-std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batch, int32_t batch,
-                       int32_t n_cu, Plan* out) {
-  if (batch < 1 || batch > max_batch) return "batch out of range";
+std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batch, int32_t n_cu, Plan* out) {
+  if (max_batch < 1 || max_batch > 16) return "max_batch must be in [1, 16]";
   if (n_cu < 1) return "n_cu must be positive";
   if (g.hidden % o.rt_rows) return "hidden must be a multiple of rt_rows";
   if (o.rt_rows & (o.rt_rows - 1)) return "rt_rows must be a power of two";
@@ -84,11 +72,10 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
     return "output tiles are limited to 35 GEMV rows";
   if (o.up_rows < 1) return "up_rows must be positive";
   if (o.qkv_max_pairs < 1) return "qkv_max_pairs must be positive";
-  const int n_teams = plan_teams(o, batch);
-  if (n_teams == 2 && batch > 4) return "two teams hold at most 4 sequences";
+  // the output task keeps each lane's (row, token) residual words in registers: 2 per lane
+  if (o.rt_rows * max_batch > 128) return "rt_rows * max_batch must be at most 128";
   if (g.n_experts > 256) return "at most 256 experts";
   if (o.pages_per_item < 1 || o.pages_per_item > 64) return "pages_per_item must be in [1, 64]";
-  if (o.pages_per_item_2 < 1 || o.pages_per_item_2 > 64) return "pages_per_item_2 must be in [1, 64]";
   if (o.pages_per_item_long < o.pages_per_item || o.pages_per_item_max < o.pages_per_item_long ||
       o.pages_per_item_max > 64)
     return "pages_per_item <= pages_per_item_long <= pages_per_item_max <= 64 is required";
@@ -97,11 +84,9 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
     return "GEMV tiles are limited to 35 rows";
   Plan& P = *out;
   P = Plan();
-  P.batch = batch;
   P.n_cu = n_cu;
-  P.n_teams = n_teams;
-  P.shape = make_shape(g, o, n_teams);
-  P.ctr = make_counters(g, P.shape, max_batch);
+  P.shape = make_shape(g, o);
+  P.ctr = make_counters(g);
   const PlanShape& s = P.shape;
   const CounterLayout& c = P.ctr;
   auto L = [&](int l, int off) { return l * c.per_layer + off; };
@@ -128,7 +113,7 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
 
   begin_wave(-1, 0);
   // residual rows, their sums of squares and the RoPE table leave as tagged words
-  for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_EMBED, 0, rt, 0, 0, 0, -1, 0, -1);
+  for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_EMBED, 0, rt, 0, 0, 0);
   end_wave();
   for (int l = 0; l < g.n_layers; ++l) {
     for (int wi = 0; wi < W_KINDS; ++wi) {
@@ -140,27 +125,27 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
             for (int t = 0; t < qkv_tph; ++t) {
               const int j0 = t * half / qkv_tph, j1 = (t + 1) * half / qkv_tph;
               // queries leave tagged; K / V tiles raise a tagged flag (ARG3: tile of the head)
-              em.emit(OP_QKV, l, hh, j0, j1 - j0, t, -1, 0, -1);
+              em.emit(OP_QKV, l, hh, j0, j1 - j0, t);
             }
           break;
         case W_ROUTER:
           for (int r0 = 0; r0 < g.n_experts; r0 += o.router_rows)
             // logits leave as tagged words (no counter): consumers wait on the data itself
             // ARG2 = 1: the first tile also builds and publishes the layer's routing tables
-            em.emit(OP_ROUTER, l, r0, std::min(o.router_rows, g.n_experts - r0), r0 == 0 ? 1 : 0, 0, -1, 0, -1);
+            em.emit(OP_ROUTER, l, r0, std::min(o.router_rows, g.n_experts - r0), r0 == 0 ? 1 : 0, 0);
           break;
         case W_ATTN:
           for (int i = 0; i < n_attn; ++i)
-            em.emit(OP_ATTN, l, i, n_attn, 0, 0, -1, 0, -1);
+            em.emit(OP_ATTN, l, i, n_attn, 0, 0);
           break;
         case W_MOE_UP:
           for (int i = 0; i < n_up; ++i)
-            em.emit(OP_MOE_UP, l, i, n_up, 0, 0, -1, 0, -1);
+            em.emit(OP_MOE_UP, l, i, n_up, 0, 0);
           break;
         case W_OUT:
           // waits inside the task: the combined attention of every KV group, then the up
           // tiles of every active expert (dynamic: routing decides the experts)
-          for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_OUT, l, rt, 0, 0, 0, -1, 0, -1);
+          for (int rt = 0; rt < s.n_rt; ++rt) em.emit(OP_OUT, l, rt, 0, 0, 0);
           break;
         default:
           return "bad wave order";
@@ -170,33 +155,15 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   }
   begin_wave(-2, g.n_layers);
   for (int r0 = 0; r0 < g.vocab; r0 += o.lm_rows)
-    em.emit(OP_LM_HEAD, g.n_layers, r0, std::min(o.lm_rows, g.vocab - r0), 0, 0, -1, 0, -1);
+    em.emit(OP_LM_HEAD, g.n_layers, r0, std::min(o.lm_rows, g.vocab - r0), 0, 0);
   end_wave();
 
-  // Deal the tasks round robin, keeping global order within each list.  One team: task k
-  // goes to CU k mod n_cu.  Two teams: each branch has its own round robin over the CUs'
-  // team slot; embedding and LM-head tiles fill team 0 of every CU, then team 1.
+  // Deal the tasks round robin, keeping global order within each list: task k goes to CU
+  // k mod n_cu.
   const int n = P.n_tasks();
-  const int n_lists = n_cu * n_teams;
+  const int n_lists = n_cu;
   std::vector<std::vector<int32_t>> lists(n_lists);
-  if (n_teams == 1) {
-    for (int k = 0; k < n; ++k) lists[k % n_cu].push_back(k);
-  } else {
-    int64_t rr[2] = {0, 0}, rr_all = 0;
-    for (const Wave& w : P.waves) {
-      for (int k = w.first; k < w.first + w.count; ++k) {
-        if (w.kind < 0) {
-          const int cu = (int)(rr_all % n_cu), t = (int)((rr_all / n_cu) % 2);
-          ++rr_all;
-          lists[cu * 2 + t].push_back(k);
-        } else {
-          const int t = (w.kind == W_QKV || w.kind == W_ATTN) ? 0 : 1;
-          lists[(rr[t] % n_cu) * 2 + t].push_back(k);
-          ++rr[t];
-        }
-      }
-    }
-  }
+  for (int k = 0; k < n; ++k) lists[k % n_cu].push_back(k);
   P.cu_offsets.assign(n_lists + 1, 0);
   P.per_cu.reserve(P.global.size());
   for (int li = 0; li < n_lists; ++li) {
@@ -211,16 +178,14 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
 
 std::string validate_plan(const Geometry& g, const Plan& P) {
   const int n = P.n_tasks();
-  // Every descriptor is well formed.  The interpreter carries every data edge as tagged
-  // words and uses counters only for the claim queues: a descriptor asking for a counter
-  // wait or arrive would be ignored, so it is rejected.
+  // Every descriptor is well formed; the reserved words are zero.
   for (int k = 0; k < n; ++k) {
     const int32_t* d = P.global.data() + (size_t)k * D_WORDS;
     if (d[D_GIDX] != k) return "task " + std::to_string(k) + ": global index mismatch";
     const int op = d[D_OPCODE];
     if (op < OP_NOP || op >= OP_COUNT) return "task " + std::to_string(k) + ": bad opcode";
-    if (d[D_WAIT] >= 0 || d[D_SIGNAL] >= 0)
-      return "task " + std::to_string(k) + ": counter waits and arrives are not used by this interpreter";
+    for (int w = D_GIDX + 1; w < D_WORDS; ++w)
+      if (d[w] != 0) return "task " + std::to_string(k) + ": reserved descriptor word set";
   }
   // Edges carried by tagged data (no counter): the router logits (MoE-up claimers and
   // output tasks read them), the attention partials and combined output (output tasks),
@@ -265,7 +230,7 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
     if (lm_first >= 0 && lm_first < last_out_end) return "the LM-head wave must follow the last output wave";
   }
   // every list in increasing global order, every task in exactly one list
-  if ((int)P.cu_offsets.size() != P.n_cu * P.n_teams + 1) return "wrong number of task lists";
+  if ((int)P.cu_offsets.size() != P.n_cu + 1) return "wrong number of task lists";
   std::vector<char> seen(n, 0);
   for (int li = 0; li + 1 < (int)P.cu_offsets.size(); ++li) {
     int32_t prev = -1;

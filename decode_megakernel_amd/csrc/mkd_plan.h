@@ -17,9 +17,6 @@
 #ifndef MKD_MAXP
 #define MKD_MAXP 1  // attention pages per worker wave (kernel register budget)
 #endif
-#ifndef MKD_TEAMS
-#define MKD_TEAMS 1
-#endif
 #ifndef MKD_UP_ROWS
 #define MKD_UP_ROWS 12  // batch 1, 8K context: 4 -> 268, 8 -> 289, 12 -> 293, 16 -> 291 tok/s
 #endif
@@ -46,16 +43,13 @@ struct PlanOptions {
   int32_t rt_rows = 8;         // residual rows per output task (O-proj + expert down rows)
   int32_t up_rows = MKD_UP_ROWS;  // activation rows per MoE-up item at most (weights: 2x rows); the
                                   // largest divisor of the expert inter size not above it is used
-  int32_t pages_per_item = MKD_PPI;  // attention pages per claimed item, one team of 7 workers
-  int32_t pages_per_item_2 = 6;  // the same with two teams of 3 workers each
-  // one team, when the step's attention items at pages_per_item outnumber the CUs (long
-  // contexts): larger items, since every item pays a claim, a merge and a partial result;
-  // when they still outnumber the CUs four times over (batch 1 at 256K: 56 -> 97, 64 -> 107
-  // tok/s; batch 4 at 64K: 315 -> 320), the largest, pages_per_item_max
+  int32_t pages_per_item = MKD_PPI;  // attention pages per claimed item (7 worker waves)
+  // when the step's attention items at pages_per_item outnumber the CUs (long contexts):
+  // larger items, since every item pays a claim, a merge and a partial result; when they
+  // still outnumber the CUs four times over (batch 1 at 256K: 56 -> 97, 64 -> 107 tok/s;
+  // batch 4 at 64K: 315 -> 320), the largest, pages_per_item_max
   int32_t pages_per_item_long = MKD_PPI_LONG;
   int32_t pages_per_item_max = 64;
-  int32_t teams = MKD_TEAMS;    // teams per workgroup: 1, 2, or 0 = 2 when batch <= two_team_max_batch
-  int32_t two_team_max_batch = 4;
   int32_t qkv_max_pairs = 17;  // RoPE pairs per QKV tile at most (tile = 2x rows); a head is
                                // split into about n_cu / heads tiles so that one pass of QKV
                                // tiles covers the compute units once
@@ -79,37 +73,30 @@ struct Wave {
 };
 
 struct Plan {
-  int32_t batch = 0;
   int32_t n_cu = 0;
-  int32_t n_teams = 1;              // task lists per CU
   PlanShape shape{};
   CounterLayout ctr{};
   std::vector<int32_t> global;      // [n][32] tasks in global (flattened) order
   std::vector<Wave> waves;          // ranges of `global`
-  std::vector<int32_t> per_cu;      // [n][32] tasks grouped by list (cu * n_teams + team), each in global order
-  std::vector<int32_t> cu_offsets;  // [n_cu * n_teams + 1]
+  std::vector<int32_t> per_cu;      // [n][32] tasks grouped by CU, each list in global order
+  std::vector<int32_t> cu_offsets;  // [n_cu + 1]
   int32_t n_tasks() const { return (int32_t)(global.size() / D_WORDS); }
 };
 
-// Shape constants and counter layout (independent of the batch size except
-// attn_items, sized by max_batch).
-PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t n_teams);
-// Teams per workgroup the plan for `batch` uses.
-int32_t plan_teams(const PlanOptions& o, int32_t batch);
-CounterLayout make_counters(const Geometry& g, const PlanShape& s, int32_t max_batch);
+// Shape constants and counter layout (independent of the batch size).
+PlanShape make_shape(const Geometry& g, const PlanOptions& o);
+CounterLayout make_counters(const Geometry& g);
 
-// Build the plan for `batch` sequences on `n_cu` compute units.  With two teams per
-// workgroup, the attention branch (QKV, attention) goes to team 0 and the MoE branch
-// (router, expert up) with the output tasks to team 1 of every CU; embedding and LM-head
-// tiles are dealt over both.  Returns "" on success, else a description of the violated
+// Build the schedule for batches of up to `max_batch` sequences on `n_cu` compute units.
+// The task lists do not depend on the batch size: the claimers size their work from the
+// step's sequence lengths.  Returns "" on success, else a description of the violated
 // constraint.
-std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batch, int32_t batch,
-                       int32_t n_cu, Plan* out);
+std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batch, int32_t n_cu, Plan* out);
 
-// Static checks of a plan: every counter a task waits on receives at least the
-// awaited number of arrivals from tasks earlier in the global order (static
-// producers), claimers wait only on earlier waves, and every compute unit's list is
-// in increasing global order (so no circular wait exists).  Returns "" if valid.
+// Static checks of a plan: every tagged edge's producer wave precedes its consumer wave
+// in the global order, and every compute unit's list is in increasing global order (so
+// no task waits for one placed after it on its own CU and no circular wait exists).
+// Returns "" if valid.
 std::string validate_plan(const Geometry& g, const Plan& p);
 
 }  // namespace mkd

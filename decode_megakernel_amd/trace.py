@@ -1,7 +1,7 @@
 """Decode the per-task trace of a megakernel step (see mkd_set_trace in include/mkd.h).
 
-Each task record holds the 100 MHz wall-clock time it started, the time its input
-counter was satisfied, the time it ended, and its opcode / workgroup / number of
+Each task record holds the 100 MHz wall-clock time it started, the time its first
+wait on input data (tagged words) completed, the time it ended, and its opcode / workgroup / number of
 claimed items.  `summarize` reports, per opcode, the time spent waiting for inputs
 and working, per layer the span between its first start and last end, and per
 workgroup the idle time; `chrome_trace` writes the timeline in the Chrome /
@@ -19,7 +19,7 @@ TICK_US = 0.01  # 100 MHz
 
 def decode(desc: np.ndarray, trace: np.ndarray) -> dict:
     """desc: [n][32] descriptors (any order, field 10 = global index); trace: [>=n][4] uint64."""
-    gidx = desc[:, 10]
+    gidx = desc[:, 7]  # descriptor word D_GIDX
     order = np.argsort(gidx)
     d = desc[order]
     t = trace[: len(d)].astype(np.int64)
@@ -28,7 +28,7 @@ def decode(desc: np.ndarray, trace: np.ndarray) -> dict:
     return {
         "op": d[:, 0],
         "layer": d[:, 1],
-        "gidx": d[:, 10],
+        "gidx": d[:, 7],
         "start": (t[:, 0] - t0) * TICK_US,
         "ready": (t[:, 1] - t0) * TICK_US,
         "end": (t[:, 2] - t0) * TICK_US,

@@ -10,14 +10,7 @@
  * the compute units.
  *
  * Source of the method: "Inside the megakernel serving engine for North Mini Code"
- * (Cohere), sections "What is a Megakernel?" (persistent kernel, per-SM task lists,
- * counters in global memory), "Tasks" and "The task descriptor" (opcodes, 32-int32
- * descriptors), "Barriers" (wait = spin until count >= target, arrive = fence then
- * atomic add), "The task scheduler: mapping tasks to SMs" (named waves dealt round
- * robin, claimers on shared queues), "The serving engine around the kernel" (the
- * host loop updates KV positions, clears per-step state, selects a schedule,
- * launches, samples), and "Performance" (batch-1 decode against a synthetic KV
- * cache).
+ * (Cohere).  Each call below names the section of that page it follows.
  *
  * Conventions
  *  - Every function returns MKD_OK (0) or a negative MKD_ERR_* code; the text of the
@@ -25,10 +18,13 @@
  *  - Device pointers are plain `void*` / typed pointers into the memory of the HIP
  *    device given to mkd_create(); streams are `hipStream_t` passed as `void*`
  *    (NULL = the default stream).
- *  - The caller owns every buffer it passes (weights, KV pool, page tables, token
- *    ids, sequence lengths, logits).  The engine owns only its own workspace
- *    (activations, counters, task lists) and frees it in mkd_destroy().
- *  - An engine is used from one host thread at a time.
+ *  - Ownership: the caller owns every device buffer: weights, KV pool, page tables,
+ *    token ids, sequence lengths, logits, the trace buffer and the engine's workspace
+ *    (sized by mkd_workspace_bytes, handed over with mkd_set_workspace).  The engine
+ *    owns only host memory (its schedule and configuration) and never frees caller
+ *    memory.  mkd_decode_step allocates nothing and makes no synchronous copy.
+ *  - An engine is used from one host thread at a time.  Two engines must not share a
+ *    workspace.
  */
 #ifndef MKD_H
 #define MKD_H
@@ -51,9 +47,10 @@ extern "C" {
 #define MKD_MODE_MEGAKERNEL 0    /* one persistent cooperative launch per step (default) */
 #define MKD_MODE_OP_PER_KERNEL 1 /* ablation: each wave of tasks is its own launch      */
 
-/* Model geometry ("Where the speedup comes from": parallel layers; "Tasks": 128
-   experts, top-k routing; Figure 7: 4 KV groups).  page_size is the number of
-   tokens per paged-KV page. */
+/* Model geometry (section "Where the speedup comes from": parallel layers whose
+   attention and MoE read one normalised input; section "Tasks": 128 experts, top-k
+   routing, SwiGLU experts; Figure 7: grouped-query attention with 4 KV groups).
+   page_size is the number of tokens per paged-KV page. */
 typedef struct mkd_config {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim;
   int32_t n_experts, top_k, moe_inter, vocab, page_size;
@@ -63,8 +60,8 @@ typedef struct mkd_config {
 /* Device weights, bf16, row-major [out][in].  BORROWED: they must stay valid and
    unchanged while the engine uses them.
      embed     [vocab][hidden]                         token embedding, tied LM head
-     norm      [n_layers+1][hidden]                    RMSNorm gammas; gamma_l feeds
-                                                       layer l, gamma_L the LM head
+     norm      [n_layers+1][hidden]                    RMSNorm gains; gain_l feeds
+                                                       layer l, gain_L the LM head
      w_qkv     [n_layers][(nq+2*nkv)*hd][hidden]       rows: q heads | k heads | v heads
      w_o       [n_layers][hidden][nq*hd]
      w_router  [n_layers][n_experts][hidden]
@@ -82,28 +79,55 @@ typedef struct mkd_weights {
 
 typedef struct mkd_engine mkd_engine;
 
-/* Create an engine for `cfg` on HIP device `hip_device`, able to decode batches of
-   up to `max_batch` sequences whose page-table rows hold `max_pages_per_seq`
-   entries.  Allocates the engine's device workspace.  Geometry limits (the kernel is
-   compiled for these row lengths): hidden in {256, 2048}, n_q_heads * head_dim /
-   n_kv_heads in {256, 1024}, moe_inter in {128, 768}, head_dim in {64, 128},
-   n_q_heads / n_kv_heads <= 16, n_kv_heads <= 16, n_experts <= 256, top_k <= 16,
-   page_size == 16, max_batch <= 16, max_pages_per_seq <= 24576.
-   hip_device = -1 creates a host-only engine (plan inspection, no decoding).
-   On error *out is set to NULL. */
+/* Create an engine for `cfg` on HIP device `hip_device`, able to decode batches of up
+   to `max_batch` sequences whose page-table rows hold `max_pages_per_seq` entries
+   (section "The serving engine around the kernel": the batch size and the page
+   tables are the per-step inputs; section "The task scheduler: mapping tasks to SMs":
+   the host builds the task lists once, here in mkd_create).  No device memory is
+   allocated.  Geometry limits (the kernel is compiled for these row lengths):
+   (hidden, moe_inter, head_dim) in {(2048, 768, 128), (256, 128, 64)},
+   n_q_heads * head_dim a multiple (1 to 4) of hidden, n_q_heads / n_kv_heads <= 16,
+   n_kv_heads <= 16, n_experts <= 256, top_k <= 16, page_size == 16, max_batch <= 16,
+   max_pages_per_seq <= 24576.  hip_device = -1 creates a host-only engine (plan
+   inspection, no decoding).  On error *out is set to NULL and MKD_ERR_ARG (bad
+   configuration) or MKD_ERR_HIP is returned. */
 int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch,
                int32_t max_pages_per_seq, mkd_engine** out);
 
-/* Release the engine and its workspace (never caller memory).  NULL is ignored. */
+/* Release the engine's host memory.  Caller memory (workspace included) is never
+   freed.  NULL is ignored. */
 void mkd_destroy(mkd_engine* eng);
 
-/* Record the weight pointers (no copy).  Returns MKD_ERR_ARG on a NULL pointer. */
+/* Bytes of device workspace the engine needs: the tagged activation words of every
+   layer, the attention partials, the claim counters, the RoPE frequencies and the
+   task lists (section "Barriers": counters and per-step state in global memory;
+   section "The task descriptor": the task lists the kernel reads).  Depends only on
+   the configuration, max_batch and max_pages_per_seq.  0 for a host-only engine. */
+size_t mkd_workspace_bytes(const mkd_engine* eng);
+
+/* Hand the engine its workspace: `dev_ptr` is device memory of at least
+   mkd_workspace_bytes() bytes, 256-byte aligned, owned by the caller and BORROWED
+   until mkd_destroy or the next mkd_set_workspace.  The call clears it and copies the
+   task lists and RoPE frequencies into it, then waits for those copies (a
+   configuration call, not a per-step one; section "The serving engine around the
+   kernel": per-step state is cleared on the device, the schedule is chosen by the
+   host).  MKD_ERR_ARG for a NULL, misaligned or too small buffer. */
+int mkd_set_workspace(mkd_engine* eng, void* dev_ptr, size_t bytes);
+
+/* Record the weight pointers (no copy).  Returns MKD_ERR_ARG on a NULL pointer
+   (section "Performance": bf16 weights streamed from HBM every step). */
 int mkd_load_weights(mkd_engine* eng, const mkd_weights* w);
 
-/* Choose MKD_MODE_MEGAKERNEL or MKD_MODE_OP_PER_KERNEL for later steps. */
+/* Choose MKD_MODE_MEGAKERNEL or MKD_MODE_OP_PER_KERNEL for later steps (section
+   "Where the speedup comes from": the launch and synchronisation gaps between per-op
+   kernels that the megakernel removes; the ablation runs the same tile bodies with one
+   launch per wave of tasks, so those gaps come back).
+   MKD_ERR_ARG for another value. */
 int mkd_set_mode(mkd_engine* eng, int32_t mode);
 
-/* One decode step for a ragged batch ("The serving engine around the kernel").
+/* One decode step for a ragged batch (section "The serving engine around the kernel":
+   the host updates the KV positions and page tables, clears per-step state, selects
+   the schedule and launches; sampling is the caller's).
      stream        HIP stream (void*), the step is asynchronous on it
      batch         number of sequences, 1 <= batch <= max_batch
      d_tokens      [batch] int32 device: the token id fed to each sequence
@@ -111,7 +135,7 @@ int mkd_set_mode(mkd_engine* eng, int32_t mode);
                    token sits at this 0-based position and attends to positions
                    0..seq_len inclusive
      h_seq_lens    [batch] int32 host mirror of d_seq_lens (validation and the
-                   per-step schedule choice)
+                   per-step choice of attention item size)
      d_page_table  [batch][max_pages_per_seq] int32 device: physical page of each
                    logical page; entries 0..seq_len/page_size must be valid pages
      h_page_table  optional host mirror of d_page_table (NULL to skip the host check
@@ -123,59 +147,91 @@ int mkd_set_mode(mkd_engine* eng, int32_t mode);
                    changes no other byte.
      n_pages       physical pages in kv_pool
      d_logits      [batch][vocab] fp32 device, written
-   Errors: MKD_ERR_ARG for a bad argument (including a used page-table entry outside
-   [0, n_pages) when h_page_table is given), MKD_ERR_STATE before mkd_load_weights,
-   MKD_ERR_HIP on a launch failure.  A page-table entry found invalid on the device
-   is skipped (never dereferenced) and reported by mkd_sync_status(). */
+   Allocates nothing; the only host work is validation and two kernel launches (a
+   counter clear and the step kernel).  Errors: MKD_ERR_STATE before
+   mkd_load_weights or mkd_set_workspace, MKD_ERR_CAPACITY for batch > max_batch or a
+   sequence longer than max_pages_per_seq pages, MKD_ERR_ARG for a bad argument
+   (including a used page-table entry outside [0, n_pages) when h_page_table is given),
+   MKD_ERR_HIP on a launch failure.  On the device, a page-table entry or token id out
+   of range, or a sequence length past the page-table row, is never dereferenced; it is
+   reported by mkd_sync_status(). */
 int mkd_decode_step(mkd_engine* eng, void* stream, int32_t batch, const int32_t* d_tokens,
                     const int32_t* d_seq_lens, const int32_t* h_seq_lens,
                     const int32_t* d_page_table, const int32_t* h_page_table, void* kv_pool,
                     int32_t n_pages, float* d_logits);
 
-/* Wait for the engine's last step on its stream and report device-side errors:
-   MKD_ERR_DEADLOCK if the wait watchdog fired (a dependency's data or counter
-   never arrived), MKD_ERR_ARG if a page-table entry was out of range, else MKD_OK.
-   The error record is cleared. */
+/* Wait for the engine's last step on its stream and report device-side errors
+   (section "How do you write a megakernel?": a dependency that is counted wrong shows
+   up as a wait that never ends, so every wait here has a bound):
+   MKD_ERR_DEADLOCK if the wait watchdog fired (a dependency's data never arrived),
+   MKD_ERR_ARG if an input was out of range on the device, else MKD_OK.  The error
+   record is cleared.  Synchronous (a status call, not part of a step). */
 int mkd_sync_status(mkd_engine* eng);
+
+/* Watchdog bound of the kernel's waits: the number of polls after which a wait on data
+   that never arrives gives up, marks the step failed (MKD_ERR_DEADLOCK from
+   mkd_sync_status) and makes every workgroup leave the step (section "Barriers": a
+   waiter spins until its dependency is met).  Default 4000000 (seconds of waiting);
+   MKD_ERR_ARG unless 1 <= polls. */
+int mkd_set_watchdog(mkd_engine* eng, int32_t polls);
 
 /* Text of the engine's last error ("" if none).  The pointer stays valid until the
    next call on the engine.  With eng == NULL returns the last creation error. */
 const char* mkd_last_error(const mkd_engine* eng);
 
-/* Debug read-back of the last step's intermediate values (synchronous copy to the
-   host buffer dst of `bytes` bytes; MKD_ERR_ARG if too small):
+/* Debug read-back of the last step's intermediate values (synchronous copy to the host
+   buffer dst of `bytes` bytes; MKD_ERR_ARG if too small).  Section "Tasks" names the
+   operations whose outputs these are:
      MKD_DEBUG_HIDDEN   fp32 [n_layers+1][batch][hidden]  residual entering each layer
                         and after the last one
      MKD_DEBUG_TOPK_IDS int32 [n_layers][batch][top_k]    selected experts, descending
      MKD_DEBUG_TOPK_W   fp32  [n_layers][batch][top_k]    their routing weights
-     MKD_DEBUG_ROUTER   fp32  [n_layers][batch][n_experts] router logits        */
+     MKD_DEBUG_ROUTER   fp32  [n_layers][batch][n_experts] router logits
+     MKD_DEBUG_Q        fp32  [n_layers][batch][nq*hd]    queries after RoPE (QKV_PROJ)
+     MKD_DEBUG_ATTN     fp32  [n_layers][batch][nq*hd]    attention output per head,
+                        after the merge of the page chunks (ATTN_DECODE + ATTN_COMBINE)
+     MKD_DEBUG_ROUTE    int32 [n_layers][MKD_ROUTE_WORDS] routing table of each layer
+                        (ROUTE_FINALIZE / MOE_GATHER), words:
+                          [b*16 + j]          expert of choice j of token b
+                          [256 + b*16 + j]    its routing weight (fp32 bits)
+                          [512]               n_act, the number of distinct experts
+                          [520 + a]           active expert a, ascending (a < n_act)
+                          [776 + a]           start of expert a's entries (a <= n_act)
+                          [1036 + i]          entry i = b*top_k + j, experts ascending,
+                                              tokens ascending within an expert
+                          [1292 + b*top_k + j] (active index << 16) | position of the
+                                              entry in its expert's list               */
 #define MKD_DEBUG_HIDDEN 0
 #define MKD_DEBUG_TOPK_IDS 1
 #define MKD_DEBUG_TOPK_W 2
 #define MKD_DEBUG_ROUTER 3
+#define MKD_DEBUG_Q 4
+#define MKD_DEBUG_ATTN 5
+#define MKD_DEBUG_ROUTE 6
+#define MKD_ROUTE_WORDS 1548
 int mkd_debug_read(mkd_engine* eng, int32_t what, void* dst, size_t bytes);
 
-/* Optional per-task trace of later steps (the tracing subsystem): dev_buf is a device
-   buffer of `bytes` bytes receiving, for the task at global index i of the step's
-   schedule, four uint64 at offset 32*i: wall-clock (100 MHz) start, time its input
-   counter was satisfied, end, and meta = opcode (8 bits) | task list << 8 (12 bits) |
-   claimed items << 20 (12 bits) | ticks from start until the inputs were staged << 32
-   (16 bits) | ticks from start until the compute finished << 48 (16 bits).  Tasks
-   beyond the buffer are not recorded.  dev_buf = NULL disables it.
-   The caller owns the buffer. */
+/* Optional per-task trace of later steps (section "How do you write a megakernel?",
+   its last step: task order and placement are tuned for throughput, which needs the
+   time line of every task on every CU).  dev_buf is a device buffer of
+   `bytes` bytes receiving, for the task at global index i of the schedule, four uint64
+   at offset 32*i: wall-clock (100 MHz) start, time its first wait on input data
+   completed, end, and meta = opcode (8 bits) | CU << 8 (12 bits) | claimed items << 20
+   (12 bits) | ticks from start until the inputs were staged << 32 (16 bits) | ticks
+   from start until the compute finished << 48 (16 bits).  Tasks beyond the buffer are
+   not recorded.  dev_buf = NULL disables it.  The caller owns the buffer. */
 int mkd_set_trace(mkd_engine* eng, void* dev_buf, size_t bytes);
 
-/* Plan inspection (host only; works on an engine created with hip_device = -1):
-   writes the task descriptors the scheduler builds for `batch` sequences onto
-   `n_cu` compute units.  Each CU runs n_teams task lists side by side (1 or 2;
-   *n_teams receives it if n_teams is not NULL); list cu * n_teams + t belongs to team
-   t of CU cu.  desc receives n_tasks * 32 int32, list after list, each in execution
-   order; cu_offsets (room for 2 * n_cu + 1 entries) receives the start of each list
-   and the total.  *n_tasks is set to the total; MKD_ERR_CAPACITY if max_tasks is too
-   small.  The descriptor layout (32 int32; field 0 = opcode) is documented in
-   decode_megakernel_amd/csrc/mkd_common.h. */
-int mkd_plan_inspect(mkd_engine* eng, int32_t batch, int32_t n_cu, int32_t* desc,
-                     int32_t max_tasks, int32_t* cu_offsets, int32_t* n_tasks, int32_t* n_teams);
+/* Plan inspection (host only; works on an engine created with hip_device = -1): writes
+   the task descriptors the scheduler builds onto `n_cu` compute units (section "The
+   task scheduler: mapping tasks to SMs"; section "The task descriptor": 32 int32 per
+   task, field 0 the opcode).  desc receives n_tasks * 32 int32, list after list, each
+   in execution order; cu_offsets (room for n_cu + 1 entries) receives the start of
+   each CU's list and the total.  *n_tasks is set to the total; MKD_ERR_CAPACITY if
+   max_tasks is too small.  The schedule does not depend on the batch size.  The
+   descriptor fields are documented in decode_megakernel_amd/csrc/mkd_common.h. */
+int mkd_plan_inspect(mkd_engine* eng, int32_t n_cu, int32_t* desc, int32_t max_tasks,
+                     int32_t* cu_offsets, int32_t* n_tasks);
 
 #ifdef __cplusplus
 }

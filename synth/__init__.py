@@ -37,7 +37,6 @@ STREAM = {
 }
 WEIGHT_STD = 0.02
 KV_STD = 1.0
-BF16_ONE = 0x3F80
 
 
 @dataclasses.dataclass(frozen=True)
@@ -176,6 +175,7 @@ def host_lib():
         u64, f32 = ctypes.c_uint64, ctypes.c_float
         lib.synth_host_normal_bf16.argtypes = [ctypes.c_void_p, u64, u64, u64, f32, u64]
         lib.synth_host_normal_f32.argtypes = [ctypes.c_void_p, u64, u64, u64, f32, u64]
+        lib.synth_host_gain_bf16.argtypes = [ctypes.c_void_p, u64, u64, u64, u64]
         lib.synth_host_uniform_int.argtypes = [ctypes.c_void_p, u64, u64, u64, ctypes.c_uint32,
                                                u64]
         _host_lib = lib
@@ -201,13 +201,21 @@ def host_tokens(wl: Workload, step: int = 0) -> np.ndarray:
     return out
 
 
+def host_gains(n: int, seed: int, offset: int = 0) -> np.ndarray:
+    """bf16 bits of n RMSNorm gains 1 + 0.25 * N(0, 1) (counters offset .. offset+n-1)."""
+    out = np.empty(n, dtype=np.uint16)
+    host_lib().synth_host_gain_bf16(out.ctypes.data, n, seed, STREAM["norm"], offset)
+    return out
+
+
 def host_weight(wl: Workload, name: str, offset: int = 0, n: Optional[int] = None) -> np.ndarray:
     """bf16 bits of weight tensor `name` (elements [offset, offset+n)).  RMSNorm
-    gammas are ones (standard initialisation)."""
+    gains are 1 + 0.25 * N(0, 1), so that each layer's gains differ from one and from
+    each other's."""
     numel = wl.geom.tensor_numel()[name]
     n = numel - offset if n is None else n
     if name == "norm":
-        return np.full(n, BF16_ONE, dtype=np.uint16)
+        return host_gains(n, wl.weight_seed, offset)
     return host_normal_bf16(n, wl.weight_seed, STREAM[name], WEIGHT_STD, offset)
 
 
@@ -243,6 +251,8 @@ def gpu_lib():
         lib.synth_gpu_normal_bf16.argtypes = [ctypes.c_void_p, u64, u64, u64, ctypes.c_float, u64,
                                               ctypes.c_void_p]
         lib.synth_gpu_normal_bf16.restype = ctypes.c_int
+        lib.synth_gpu_gain_bf16.argtypes = [ctypes.c_void_p, u64, u64, u64, u64, ctypes.c_void_p]
+        lib.synth_gpu_gain_bf16.restype = ctypes.c_int
         lib.synth_gpu_fill_u16.argtypes = [ctypes.c_void_p, u64, ctypes.c_uint32, ctypes.c_void_p]
         lib.synth_gpu_fill_u16.restype = ctypes.c_int
         _gpu_lib = lib
@@ -252,7 +262,8 @@ def gpu_lib():
 def gpu_fill_weight(wl: Workload, name: str, dev_ptr: int, stream_handle: int = 0) -> None:
     numel = wl.geom.tensor_numel()[name]
     if name == "norm":
-        rc = gpu_lib().synth_gpu_fill_u16(dev_ptr, numel, BF16_ONE, stream_handle)
+        rc = gpu_lib().synth_gpu_gain_bf16(dev_ptr, numel, wl.weight_seed, STREAM["norm"], 0,
+                                           stream_handle)
     else:
         rc = gpu_lib().synth_gpu_normal_bf16(dev_ptr, numel, wl.weight_seed, STREAM[name],
                                              WEIGHT_STD, 0, stream_handle)

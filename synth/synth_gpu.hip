@@ -17,6 +17,13 @@ synth_normal_bf16_kernel(uint16_t* __restrict__ dst, uint64_t n, uint64_t key, f
 }
 
 __global__ void __launch_bounds__(256)
+synth_gain_bf16_kernel(uint16_t* __restrict__ dst, uint64_t n, uint64_t key, uint64_t offset) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += stride)
+    dst[j] = synth_gain_bf16(key, offset + j);
+}
+
+__global__ void __launch_bounds__(256)
 synth_fill_u16_kernel(uint16_t* __restrict__ dst, uint64_t n, uint16_t value) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += stride)
@@ -41,6 +48,15 @@ int synth_gpu_normal_bf16(void* dst, uint64_t n, uint64_t seed, uint64_t stream,
   hipLaunchKernelGGL(synth_normal_bf16_kernel, dim3(synth_grid(n)), dim3(256), 0,
                      (hipStream_t)stream_handle, (uint16_t*)dst, n, key,
                      synth_scale_factor(scale), offset);
+  return (int)hipGetLastError();
+}
+
+/* Fill n bf16 RMSNorm gains (synth_gain_bf16) at counters offset .. offset+n-1. */
+int synth_gpu_gain_bf16(void* dst, uint64_t n, uint64_t seed, uint64_t stream, uint64_t offset,
+                        void* stream_handle) {
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(synth_gain_bf16_kernel, dim3(synth_grid(n)), dim3(256), 0,
+                     (hipStream_t)stream_handle, (uint16_t*)dst, n, synth_key(seed, stream), offset);
   return (int)hipGetLastError();
 }
 

@@ -26,6 +26,13 @@ void synth_host_normal_f32(float* dst, uint64_t n, uint64_t seed, uint64_t strea
     dst[j] = synth_normal_f32(key, offset + (uint64_t)j, factor);
 }
 
+/* dst[j] = bf16 RMSNorm gain at counter offset + j (synth_gain_bf16). */
+void synth_host_gain_bf16(uint16_t* dst, uint64_t n, uint64_t seed, uint64_t stream, uint64_t offset) {
+  const uint64_t key = synth_key(seed, stream);
+#pragma omp parallel for schedule(static)
+  for (long long j = 0; j < (long long)n; ++j) dst[j] = synth_gain_bf16(key, offset + (uint64_t)j);
+}
+
 /* dst[j] = uniform integer in [0, range) at counter offset + j. */
 void synth_host_uniform_int(int32_t* dst, uint64_t n, uint64_t seed, uint64_t stream,
                             uint32_t range, uint64_t offset) {

@@ -25,6 +25,9 @@
  *     N / 65536 (exact in fp32 since |N| < 2^19).  A value of scale s is
  *     N * (s * 2^-16), one fp32 multiply, then rounded to bf16
  *     (round-to-nearest-even) where a bf16 tensor is wanted.
+ *   - RMSNorm gains: 1 + 0.25 * deviate (synth_gain_bf16), so that every gain differs
+ *     from one and a kernel that drops the gain multiply, or reads another layer's
+ *     gains, gives different results.
  */
 #ifndef SYNTH_RNG_H
 #define SYNTH_RNG_H
@@ -81,6 +84,14 @@ SYNTH_FN uint16_t synth_f32_to_bf16(float f) {
   uint32_t u = v.u;
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+/* i-th RMSNorm gain: bf16(1 + 0.25 * deviate).  The deviate's numerator N is an
+   integer with |N| < 2^19, so N * 2^-18 and 1 + N * 2^-18 are exact in fp32 (at most
+   21 significant bits): the value is the same whether or not a compiler fuses the
+   multiply and the add, and the one rounding is the bf16 conversion. */
+SYNTH_FN uint16_t synth_gain_bf16(uint64_t key, uint64_t i) {
+  return synth_f32_to_bf16(1.0f + (float)synth_normal_num(key, i) * (1.0f / 262144.0f));
 }
 
 /* i-th uniform integer in [0, n). */

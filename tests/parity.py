@@ -3,11 +3,16 @@ the same step on the CPU reference from identical seeded inputs, and compare the
 with the acceptance rules:
 
 - hidden states and logits: per row, max|gpu - ref| / max|ref| <= 2e-2 (bf16
-  weights, fp32 accumulation);
+  weights, fp32 accumulation); the same bound per query-head row for the queries after
+  RoPE and the attention output of every layer (each replayed by the reference layer
+  function from the residual stream entering the layer), and per token for the
+  routing weights;
 - page-table / KV-slot indexing: bit-exact (every pool byte outside the written
   slots unchanged; written slots hold the bf16 of k and v);
 - expert selection identical, except where the reference's gap between the k-th
-  and (k+1)-th router logit is < 1e-3 (reported, not failed);
+  and (k+1)-th router logit is < 1e-3 (reported, not failed); the routing table the
+  kernel publishes (active experts, per-expert token lists, entry records) bit-exact
+  against the table derived from the selected ids;
 - greedy argmax identical, except a near-tie of the reference's top two logits
   within the tolerance band (reported separately, never silently passed).
 """
@@ -39,6 +44,9 @@ class GpuStep:
     topk_ids: np.ndarray
     topk_w: np.ndarray
     router: np.ndarray
+    q: np.ndarray            # [L][B][nq*hd]
+    attn: np.ndarray         # [L][B][nq*hd]
+    route: np.ndarray        # [L][ROUTE_WORDS] int32
     pool_after: np.ndarray   # uint16 bits
     pool_before: np.ndarray
     weights_bits: dict
@@ -69,6 +77,9 @@ def gpu_step(wl, mode=0, check_weights=False):
         topk_ids=eng.debug_read(mkd.DEBUG_TOPK_IDS, wl.batch),
         topk_w=eng.debug_read(mkd.DEBUG_TOPK_W, wl.batch),
         router=eng.debug_read(mkd.DEBUG_ROUTER, wl.batch),
+        q=eng.debug_read(mkd.DEBUG_Q, wl.batch),
+        attn=eng.debug_read(mkd.DEBUG_ATTN, wl.batch),
+        route=eng.debug_read(mkd.DEBUG_ROUTE, wl.batch),
         pool_after=sdev.bf16_bits(pool),
         pool_before=pool_before,
         weights_bits={k: sdev.bf16_bits(v) for k, v in W.items()} if check_weights else {},
@@ -113,6 +124,75 @@ def router_near_tie(router_logits, k):
     return (s[..., k - 1] - s[..., k]) < ROUTER_TIE
 
 
+def route_table(ids, weights, k):
+    """Expected routing-table words of one layer from the selected ids [B][k] and weights:
+    choices and weights per token, active experts ascending, CSR offsets, entries
+    (b*k + j) expert-major with tokens ascending, and each entry's (active index << 16 |
+    position in its expert's list).  Layout of MKD_DEBUG_ROUTE in include/mkd.h."""
+    ids = np.asarray(ids)
+    B = ids.shape[0]
+    t = np.zeros(1548, np.int64)
+    for b in range(B):
+        for j in range(k):
+            t[b * 16 + j] = ids[b, j]
+            t[256 + b * 16 + j] = int(np.asarray(weights[b, j], np.float32).view(np.int32))
+    act = sorted(set(int(e) for e in ids.reshape(-1)))
+    t[512] = len(act)
+    at = 0
+    for a, e in enumerate(act):
+        t[520 + a] = e
+        t[776 + a] = at
+        pos = 0
+        for b in range(B):
+            for j in range(k):
+                if ids[b, j] == e:
+                    t[1036 + at] = b * k + j
+                    t[1292 + b * k + j] = (a << 16) | pos
+                    at += 1
+                    pos += 1
+    t[776 + len(act)] = at
+    return t.astype(np.int64)
+
+
+def check_route(table, ids, w, ref_ids, ref_w, ref_router, k):
+    """One layer's routing against the reference: ids identical except near ties, weights
+    within the bar where the ids agree, and the published table bit-exact (the lists
+    derived from the kernel's own ids, which equal the reference's where no tie)."""
+    rep = dict(topk_w_rel=0.0, ties=0)
+    B = ids.shape[0]
+    mism = np.any(ids != ref_ids, axis=-1)
+    tie = router_near_tie(ref_router, k)
+    assert not (mism & ~tie).any(), f"expert selection differs without a near tie: {np.argwhere(mism & ~tie)}"
+    rep["ties"] = int((mism & tie).sum())
+    same = ~mism
+    if same.any():
+        rep["topk_w_rel"] = max_rel_rows(w[same], ref_w[same])
+        assert rep["topk_w_rel"] <= REL_TOL, rep
+    exp = route_table(ids, w, k)
+    got = np.asarray(table, np.int64) & 0xFFFFFFFF
+    exp_u = exp & 0xFFFFFFFF
+    n_ent = B * k
+    words = np.r_[[512], 520 + np.arange(exp[512]), 776 + np.arange(exp[512] + 1), 1036 + np.arange(n_ent),
+                  1292 + np.arange(n_ent)]
+    assert np.array_equal(got[words], exp_u[words]), "published expert lists differ from the selected ids"
+    choice = np.array([b * 16 + j for b in range(B) for j in range(k)])
+    assert np.array_equal(got[choice], exp_u[choice]), "published choices differ from the selected ids"
+    assert np.array_equal(got[256 + choice], exp_u[256 + choice]), "published weights differ from topk_w"
+    if not mism.any():
+        ref_tab = route_table(ref_ids, ref_w, k) & 0xFFFFFFFF
+        assert np.array_equal(got[words], ref_tab[words]), "expert lists differ from the reference's"
+    return rep
+
+
+def check_attention(q, attn, ref_q, ref_attn, head_dim):
+    """Queries after RoPE and attention outputs, per query-head row, within the bar."""
+    rep = dict(q_rel=max_rel_rows(np.asarray(q).reshape(-1, head_dim), np.asarray(ref_q).reshape(-1, head_dim)),
+               attn_rel=max_rel_rows(np.asarray(attn).reshape(-1, head_dim),
+                                     np.asarray(ref_attn).reshape(-1, head_dim)))
+    assert rep["q_rel"] <= REL_TOL and rep["attn_rel"] <= REL_TOL, rep
+    return rep
+
+
 def compare(wl, g: GpuStep, r: dict):
     """Returns a dict of measured errors; raises AssertionError on a failed rule."""
     geo = wl.geom
@@ -132,19 +212,19 @@ def compare(wl, g: GpuStep, r: dict):
     rk = oracle.bf16_to_f32(r["pool_after"][slots]).astype(np.float64)
     rep["kv_rel"] = float(np.max(np.abs(gk - rk)) / max(np.max(np.abs(rk)), 1e-30))
     assert rep["kv_rel"] <= REL_TOL, rep
-    # routing
-    mism = g.topk_ids != r["ids"]
-    tie = np.zeros(mism.shape[:2], bool)
-    # recompute the reference router logits' near ties from the GPU logits' order is not
-    # allowed; the reference layer function gives them exactly
-    rep["topk_mismatch_rows"] = int(np.any(mism, axis=-1).sum())
-    rep["router_ties"] = 0
-    if rep["topk_mismatch_rows"]:
-        ref_router = reference_router_logits(wl, r, g)
-        tie = router_near_tie(ref_router, geo.top_k)
-        bad = np.any(mism, axis=-1) & ~tie
-        rep["router_ties"] = int((np.any(mism, axis=-1) & tie).sum())
-        assert not bad.any(), f"expert selection differs without a near-tie: {np.argwhere(bad)}"
+    # per layer: queries, attention output and routing against the reference layer
+    # function replayed from the reference residual stream (near ties of the reference's
+    # router logits come from that replay)
+    lay = reference_layers(wl, r)
+    rep.update(q_rel=0.0, attn_rel=0.0, topk_w_rel=0.0, router_ties=0)
+    for layer in range(geo.n_layers):
+        a = check_attention(g.q[layer], g.attn[layer], lay["q"][layer], lay["attn"][layer], geo.head_dim)
+        rt = check_route(g.route[layer], g.topk_ids[layer], g.topk_w[layer], r["ids"][layer], r["w"][layer],
+                         lay["router"][layer], geo.top_k)
+        rep["q_rel"] = max(rep["q_rel"], a["q_rel"])
+        rep["attn_rel"] = max(rep["attn_rel"], a["attn_rel"])
+        rep["topk_w_rel"] = max(rep["topk_w_rel"], rt["topk_w_rel"])
+        rep["router_ties"] += rt["ties"]
     # greedy argmax
     ga, ra = g.logits.argmax(-1), r["logits"].argmax(-1)
     srt = -np.sort(-r["logits"].astype(np.float64), axis=-1)
@@ -155,12 +235,16 @@ def compare(wl, g: GpuStep, r: dict):
     return rep
 
 
-def reference_router_logits(wl, r, g):
-    """Reference router logits per layer, recomputed layer by layer with the reference
-    layer function from the reference residual stream."""
+def reference_layers(wl, r):
+    """Reference intermediate values per layer (queries, attention output, router logits),
+    recomputed layer by layer with the reference layer function from the reference
+    residual stream and the reference KV cache."""
     geo = wl.geom
     H = geo.hidden
-    out = np.empty((geo.n_layers, wl.batch, geo.n_experts), np.float32)
+    qd = geo.n_q_heads * geo.head_dim
+    out = dict(q=np.empty((geo.n_layers, wl.batch, qd), np.float32),
+               attn=np.empty((geo.n_layers, wl.batch, qd), np.float32),
+               router=np.empty((geo.n_layers, wl.batch, geo.n_experts), np.float32))
     pool = r["pool_before"].copy()
     nl = geo.kv_layer_numel(wl.n_pages)
     W = r["W"]
@@ -172,5 +256,7 @@ def reference_router_logits(wl, r, g):
                          W["w_router"].reshape(geo.n_layers, -1)[layer],
                          W["w_gate_up"].reshape(geo.n_layers, -1)[layer],
                          W["w_down"].reshape(geo.n_layers, -1)[layer], h, debug=True)
-        out[layer] = o["router"]
+        for key in out:
+            out[key][layer] = o[key]
+    assert np.array_equal(h, r["hidden"][geo.n_layers]), "layer replay differs from the reference step"
     return out

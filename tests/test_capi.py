@@ -17,7 +17,7 @@ OP_EMBED, OP_QKV, OP_ROUTER, OP_ATTN, OP_MOE_UP, OP_OUT, OP_LM_HEAD = range(1, 8
 
 def test_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "mkd.h")).read()
-    declared = set(re.findall(r"^\s*(?:int|void|const char\*)\s+(mkd_\w+)\s*\(", header, re.M))
+    declared = set(re.findall(r"^\s*(?:int|void|size_t|const char\*)\s+(mkd_\w+)\s*\(", header, re.M))
     assert declared == set(mkd.EXPORTS)
     L = mkd.lib()
     for name in declared:
@@ -41,33 +41,43 @@ def test_host_engine_refuses_to_decode():
     rc = mkd.lib().mkd_decode_step(e._h, None, 1, None, None, None, None, None, None, 1, None)
     assert rc == mkd.MKD_ERR_STATE
     assert mkd.lib().mkd_sync_status(None) == mkd.MKD_ERR_ARG
+    # a host-only engine has no workspace and refuses one
+    assert mkd.lib().mkd_workspace_bytes(e._h) == 0
+    assert mkd.lib().mkd_set_workspace(e._h, 256, 1 << 20) == mkd.MKD_ERR_STATE
+    assert mkd.lib().mkd_set_watchdog(e._h, 0) == mkd.MKD_ERR_ARG
+    assert mkd.lib().mkd_set_watchdog(e._h, 1000) == mkd.MKD_OK
+
+
+def test_plan_rejects_oversized_output_tiles():
+    # the output task holds (row, token) residual words two per lane: rt_rows * max_batch
+    # <= 128 at the default 8 rows per tile holds for max_batch 16, the engine's limit
+    with pytest.raises(mkd.MkdError):
+        mkd.Engine(synth.FULL, -1, 17, 64)
 
 
 def _waves(desc):
     return desc[:, 0], desc[:, 1]
 
 
-@pytest.mark.parametrize("geom,batch,n_cu", [(synth.TINY, 1, 256), (synth.TINY, 3, 7),
-                                             (synth.FULL, 1, 256), (synth.FULL, 16, 256)])
-def test_plan_structure(geom, batch, n_cu):
-    e = mkd.Engine(geom, -1, 16, 64)
-    desc, offs, teams = e.plan(batch, n_cu)
-    assert teams in (1, 2)
-    assert len(offs) == n_cu * teams + 1
+GI = mkd.D_GIDX
+
+
+@pytest.mark.parametrize("geom,max_batch,n_cu", [(synth.TINY, 1, 256), (synth.TINY, 3, 7),
+                                                 (synth.FULL, 1, 256), (synth.FULL, 16, 256)])
+def test_plan_structure(geom, max_batch, n_cu):
+    e = mkd.Engine(geom, -1, max_batch, 64)
+    desc, offs = e.plan(n_cu)
+    assert len(offs) == n_cu + 1
     assert offs[0] == 0 and offs[-1] == desc.shape[0] and (np.diff(offs) >= 0).all()
-    # every task in exactly one list, each list in global order
-    assert sorted(desc[:, 10].tolist()) == list(range(desc.shape[0]))
-    for li in range(n_cu * teams):
-        gidx = desc[offs[li]:offs[li + 1], 10]
+    # every task in exactly one list, each list in global order; reserved words zero
+    assert sorted(desc[:, GI].tolist()) == list(range(desc.shape[0]))
+    assert (desc[:, GI + 1:] == 0).all()
+    for li in range(n_cu):
+        gidx = desc[offs[li]:offs[li + 1], GI]
         assert (np.diff(gidx) > 0).all()
-    if teams == 1:  # round robin: CU c holds global indices c, c + n_cu, ...
-        for cu in range(n_cu):
-            assert (desc[offs[cu]:offs[cu + 1], 10] % n_cu == cu).all()
-    else:  # attention branch on team 0, MoE branch on team 1
-        team_of = np.repeat(np.arange(n_cu * teams) % teams, np.diff(offs))
-        ops_ = desc[:, 0]
-        assert (team_of[np.isin(ops_, [OP_QKV, OP_ATTN])] == 0).all()
-        assert (team_of[np.isin(ops_, [OP_ROUTER, OP_MOE_UP, OP_OUT])] == 1).all()
+    # round robin: CU c holds global indices c, c + n_cu, ...
+    for cu in range(n_cu):
+        assert (desc[offs[cu]:offs[cu + 1], GI] % n_cu == cu).all()
     ops = desc[:, 0]
     gq = geom.n_q_heads + 2 * geom.n_kv_heads
     n_rt = geom.hidden // 8
@@ -80,25 +90,20 @@ def test_plan_structure(geom, batch, n_cu):
         t = qkv[qkv[:, 1] == layer]
         covered = sorted((h, j0 + i) for h, j0, pb in t[:, 2:5] for i in range(pb))
         assert covered == [(h, i) for h in range(gq) for i in range(geom.head_dim // 2)]
-    # queries and the K / V flags are tagged words: no counter between QKV tiles and the
-    # attention claimers, which come after the layer's QKV wave; ARG3 numbers the tiles of
-    # a head
+    # queries and the K / V flags are tagged words: the attention claimers come after the
+    # layer's QKV wave; ARG3 numbers the tiles of a head
     attn = desc[ops == OP_ATTN]
     for layer in range(geom.n_layers):
         a = attn[attn[:, 1] == layer]
         t = qkv[qkv[:, 1] == layer]
-        assert (a[:, 6] == -1).all() and (t[:, 8] == -1).all()
-        assert a[:, 10].min() > t[:, 10].max()
+        assert a[:, GI].min() > t[:, GI].max()
         for h in range(gq):
             assert sorted(t[t[:, 2] == h][:, 5].tolist()) == list(range((t[:, 2] == h).sum()))
     # one output task per residual row tile and layer; the residual rows travel as tagged
-    # words, so neither the output tasks nor the next layer's consumers use a counter, and
-    # the next layer's tasks come after the output wave in the global order
+    # words and the next layer's tasks come after the output wave in the global order
     out = desc[ops == OP_OUT]
     for layer in range(geom.n_layers):
         o = out[out[:, 1] == layer]
         assert sorted(o[:, 2].tolist()) == list(range(n_rt))
-        assert (o[:, 8] == -1).all()
         nxt = qkv[qkv[:, 1] == layer + 1] if layer + 1 < geom.n_layers else desc[ops == OP_LM_HEAD]
-        assert (nxt[:, 6] == -1).all()
-        assert nxt[:, 10].min() > o[:, 10].max()
+        assert nxt[:, GI].min() > o[:, GI].max()

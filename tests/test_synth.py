@@ -42,3 +42,16 @@ def test_tokens_in_vocab():
     wl = synth.ragged_workload(synth.TINY, [3] * 16)
     t = synth.host_tokens(wl)
     assert t.dtype == np.int32 and ((t >= 0) & (t < wl.geom.vocab)).all()
+
+
+def test_gains_differ_from_one_and_per_layer():
+    g = synth.host_gains(100000, seed=0)
+    f = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert abs(f.mean() - 1.0) < 0.01 and abs(f.std() - 0.25) < 0.01
+    assert (g != 0x3F80).mean() > 0.95
+    # counter-based, like the other streams
+    assert np.array_equal(synth.host_gains(500, seed=0, offset=2048), g[2048:2548])
+    # equal to bf16(1 + 0.25 * deviate) of the f32 normal stream
+    n = synth.host_normal_f32(1000, seed=0, stream=synth.STREAM["norm"], scale=0.25)
+    ref = torch.tensor(1.0 + n.astype(np.float64)).to(torch.float32).to(torch.bfloat16)
+    assert np.array_equal(g[:1000], ref.view(torch.int16).numpy().view(np.uint16))
