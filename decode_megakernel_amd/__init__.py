@@ -38,7 +38,8 @@ D_GIDX = 7  # descriptor word holding the task's position in the global order
 
 # every symbol include/mkd.h declares
 EXPORTS = ("mkd_create", "mkd_destroy", "mkd_workspace_bytes", "mkd_set_workspace",
-           "mkd_load_weights", "mkd_set_mode", "mkd_decode_step", "mkd_sync_status",
+           "mkd_load_weights", "mkd_set_mode", "mkd_decode_step", "mkd_decode_step_static",
+           "mkd_sync_status",
            "mkd_set_watchdog", "mkd_last_error", "mkd_debug_read", "mkd_plan_inspect",
            "mkd_set_trace")
 
@@ -83,6 +84,7 @@ def lib():
             "mkd_load_weights": ([VP, P(Weights)], I32),
             "mkd_set_mode": ([VP, I32], I32),
             "mkd_decode_step": ([VP, VP, I32, VP, VP, VP, VP, VP, VP, I32, VP], I32),
+            "mkd_decode_step_static": ([VP, VP, I32, VP, VP, VP, VP, VP, VP, I32, VP], I32),
             "mkd_sync_status": ([VP], I32),
             "mkd_last_error": ([VP], ctypes.c_char_p),
             "mkd_debug_read": ([VP, I32, VP, ctypes.c_size_t], I32),
@@ -176,15 +178,16 @@ class Engine:
         self._check(lib().mkd_set_mode(self._h, mode))
 
     def decode_step(self, tokens, seq_lens, h_seq_lens: np.ndarray, page_table, kv_pool, n_pages,
-                    logits, h_page_table: Optional[np.ndarray] = None, stream=None):
+                    logits, h_page_table: Optional[np.ndarray] = None, stream=None, static=False):
         """Enqueue one step.  tokens, seq_lens, page_table: int32 device tensors; kv_pool
-        bf16 device tensor; logits fp32 device tensor [batch][vocab]."""
+        bf16 device tensor; logits fp32 device tensor [batch][vocab].  static=True calls
+        mkd_decode_step_static (the library's static scratch instead of the workspace)."""
         h_seq_lens = np.ascontiguousarray(h_seq_lens, dtype=np.int32)
         hpt = None if h_page_table is None else np.ascontiguousarray(h_page_table, dtype=np.int32)
         s = None if stream is None else ctypes.c_void_p(stream)
-        self._check(lib().mkd_decode_step(self._h, s, int(h_seq_lens.size), _ptr(tokens),
-                                          _ptr(seq_lens), _ptr(h_seq_lens), _ptr(page_table),
-                                          _ptr(hpt), _ptr(kv_pool), int(n_pages), _ptr(logits)))
+        fn = lib().mkd_decode_step_static if static else lib().mkd_decode_step
+        self._check(fn(self._h, s, int(h_seq_lens.size), _ptr(tokens), _ptr(seq_lens), _ptr(h_seq_lens),
+                       _ptr(page_table), _ptr(hpt), _ptr(kv_pool), int(n_pages), _ptr(logits)))
 
     def sync_status(self) -> int:
         return self._check(lib().mkd_sync_status(self._h))

@@ -47,6 +47,7 @@ struct Region {
 }  // namespace
 
 struct mkd_engine {
+  uint64_t id = 0;  // distinct for every engine created in the process
   mkd_config cfg{};
   Geometry geom{};
   int32_t device = -1;
@@ -65,10 +66,12 @@ struct mkd_engine {
   std::string err;
   int32_t last_batch = 0;
   hipStream_t last_stream = nullptr;
+  char* last_ws = nullptr;  // workspace of the last step (the engine's or the static scratch)
   uint64_t* trace = nullptr;
   int32_t trace_cap = 0;
   int32_t spin_limit = 4000000;
   uint32_t epoch = 0;  // number of the last step, in [1, 2^24) (0: none since the workspace was cleared)
+  std::vector<double> inv_freq;  // RoPE frequencies base^(-2i/hd), copied into every workspace
   std::vector<const Region*> regions() const {
     return {&r_h, &r_ss, &r_q, &r_kvflag, &r_part, &r_attn_o, &r_router, &r_tbl, &r_topk_ids,
             &r_topk_w, &r_act, &r_inv_freq, &r_rope, &r_dummy, &r_counters, &r_tasks_cu,
@@ -145,12 +148,53 @@ void layout(mkd_engine* e) {
   e->ws_bytes = at;
 }
 
-template <typename T>
-T* at_ws(mkd_engine* e, const Region& r) {
-  return reinterpret_cast<T*>(e->ws + r.off);
+// Workspace pointers of the kernel parameters for a workspace starting at `ws`.
+void point_params(const mkd_engine* e, char* ws, Params& p) {
+  p.h = (uint64_t*)(ws + e->r_h.off);
+  p.ss = (uint64_t*)(ws + e->r_ss.off);
+  p.q = (uint64_t*)(ws + e->r_q.off);
+  p.kvflag = (uint64_t*)(ws + e->r_kvflag.off);
+  p.attn_part = (uint64_t*)(ws + e->r_part.off);
+  p.attn_o = (uint64_t*)(ws + e->r_attn_o.off);
+  p.router = (uint64_t*)(ws + e->r_router.off);
+  p.route_tbl = (uint64_t*)(ws + e->r_tbl.off);
+  p.topk_ids = (int32_t*)(ws + e->r_topk_ids.off);
+  p.topk_w = (float*)(ws + e->r_topk_w.off);
+  p.moe_act = (uint64_t*)(ws + e->r_act.off);
+  p.inv_freq = (const double*)(ws + e->r_inv_freq.off);
+  p.rope = (uint64_t*)(ws + e->r_rope.off);
+  p.dummy = ws + e->r_dummy.off;
+  p.counters = (uint32_t*)(ws + e->r_counters.off);
 }
 
+uint64_t g_next_engine_id = 1;
+
 }  // namespace
+
+namespace mkd {
+
+// Clear a workspace at `ws` and copy the schedule and the RoPE frequencies into it, in
+// order on `stream` (every tagged word then carries epoch 0, which no step uses).
+hipError_t init_workspace(const mkd_engine* e, char* ws, hipStream_t stream) {
+  hipError_t rc = launch_clear((uint32_t*)ws, (int64_t)(e->ws_bytes / 4), stream);
+  const Plan& P = e->plan;
+  if (rc == hipSuccess)
+    rc = hipMemcpyAsync(ws + e->r_inv_freq.off, e->inv_freq.data(), sizeof(double) * e->inv_freq.size(),
+                        hipMemcpyHostToDevice, stream);
+  if (rc == hipSuccess)
+    rc = hipMemcpyAsync(ws + e->r_tasks_cu.off, P.per_cu.data(), sizeof(int32_t) * P.per_cu.size(),
+                        hipMemcpyHostToDevice, stream);
+  if (rc == hipSuccess)
+    rc = hipMemcpyAsync(ws + e->r_tasks_global.off, P.global.data(), sizeof(int32_t) * P.global.size(),
+                        hipMemcpyHostToDevice, stream);
+  if (rc == hipSuccess)
+    rc = hipMemcpyAsync(ws + e->r_offsets.off, P.cu_offsets.data(), sizeof(int32_t) * P.cu_offsets.size(),
+                        hipMemcpyHostToDevice, stream);
+  // the sources are the engine's own vectors, which outlive the copies
+  return rc;
+}
+
+}  // namespace mkd
 
 extern "C" {
 
@@ -168,11 +212,14 @@ int mkd_create(const mkd_config* cfg, int32_t hip_device, int32_t max_batch, int
     return MKD_ERR_ARG;
   }
   std::unique_ptr<mkd_engine> e(new mkd_engine());
+  e->id = g_next_engine_id++;
   e->cfg = *cfg;
   e->geom = Geometry{cfg->n_layers, cfg->hidden, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim,
                      cfg->n_experts, cfg->top_k, cfg->moe_inter, cfg->vocab, cfg->page_size};
   e->max_batch = max_batch;
   e->max_pages = max_pages_per_seq;
+  for (int i = 0; i < cfg->head_dim / 2; ++i)
+    e->inv_freq.push_back(std::pow((double)cfg->rope_base, -2.0 * (double)i / (double)cfg->head_dim));
   e->max_attn_items = max_batch * cfg->n_kv_heads * ((max_pages_per_seq + e->opts.pages_per_item - 1) /
                                                      e->opts.pages_per_item);
   if (hip_device < 0) {  // host-only engine: plan inspection
@@ -232,45 +279,15 @@ int mkd_set_workspace(mkd_engine* e, void* dev_ptr, size_t bytes) {
                                     std::to_string(e->ws_bytes) + " bytes mkd_workspace_bytes asks for");
   hipError_t rc = hipSetDevice(e->device);
   if (rc != hipSuccess) return hip_fail(e, rc, "hipSetDevice");
+  e->ws = nullptr;
+  rc = init_workspace(e, (char*)dev_ptr, nullptr);
+  if (rc == hipSuccess) rc = hipStreamSynchronize(nullptr);
+  if (rc != hipSuccess) return hip_fail(e, rc, "workspace initialisation");
   e->ws = (char*)dev_ptr;
-  Params& p = e->base;
-  p.h = at_ws<uint64_t>(e, e->r_h);
-  p.ss = at_ws<uint64_t>(e, e->r_ss);
-  p.q = at_ws<uint64_t>(e, e->r_q);
-  p.kvflag = at_ws<uint64_t>(e, e->r_kvflag);
-  p.attn_part = at_ws<uint64_t>(e, e->r_part);
-  p.attn_o = at_ws<uint64_t>(e, e->r_attn_o);
-  p.router = at_ws<uint64_t>(e, e->r_router);
-  p.route_tbl = at_ws<uint64_t>(e, e->r_tbl);
-  p.topk_ids = at_ws<int32_t>(e, e->r_topk_ids);
-  p.topk_w = at_ws<float>(e, e->r_topk_w);
-  p.moe_act = at_ws<uint64_t>(e, e->r_act);
-  p.inv_freq = at_ws<double>(e, e->r_inv_freq);
-  p.rope = at_ws<uint64_t>(e, e->r_rope);
-  p.dummy = e->ws + e->r_dummy.off;
-  p.counters = at_ws<uint32_t>(e, e->r_counters);
-  // every word starts at zero: tagged words then carry epoch 0, which no step uses
-  rc = launch_clear((uint32_t*)e->ws, (int64_t)(e->ws_bytes / 4), nullptr);
-  std::vector<double> inv(e->cfg.head_dim / 2);
-  for (int i = 0; i < e->cfg.head_dim / 2; ++i)
-    inv[i] = std::pow((double)e->cfg.rope_base, -2.0 * (double)i / (double)e->cfg.head_dim);
-  if (rc == hipSuccess) rc = hipDeviceSynchronize();
-  if (rc == hipSuccess) rc = hipMemcpy((void*)p.inv_freq, inv.data(), sizeof(double) * inv.size(), hipMemcpyHostToDevice);
-  const Plan& P = e->plan;
-  if (rc == hipSuccess)
-    rc = hipMemcpy(e->ws + e->r_tasks_cu.off, P.per_cu.data(), sizeof(int32_t) * P.per_cu.size(), hipMemcpyHostToDevice);
-  if (rc == hipSuccess)
-    rc = hipMemcpy(e->ws + e->r_tasks_global.off, P.global.data(), sizeof(int32_t) * P.global.size(),
-                   hipMemcpyHostToDevice);
-  if (rc == hipSuccess)
-    rc = hipMemcpy(e->ws + e->r_offsets.off, P.cu_offsets.data(), sizeof(int32_t) * P.cu_offsets.size(),
-                   hipMemcpyHostToDevice);
-  if (rc != hipSuccess) {
-    e->ws = nullptr;
-    return hip_fail(e, rc, "workspace initialisation");
-  }
+  point_params(e, e->ws, e->base);
   e->epoch = 0;
   e->last_batch = 0;
+  e->last_ws = nullptr;
   return MKD_OK;
 }
 
@@ -303,13 +320,21 @@ int mkd_set_watchdog(mkd_engine* e, int32_t polls) {
   return MKD_OK;
 }
 
-int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d_tokens,
-                    const int32_t* d_seq_lens, const int32_t* h_seq_lens, const int32_t* d_page_table,
-                    const int32_t* h_page_table, void* kv_pool, int32_t n_pages, float* d_logits) {
-  if (!e) return MKD_ERR_ARG;
-  if (e->device < 0) return fail(e, MKD_ERR_STATE, "host-only engine cannot decode");
-  if (!e->have_weights) return fail(e, MKD_ERR_STATE, "weights not loaded");
-  if (!e->ws) return fail(e, MKD_ERR_STATE, "no workspace: call mkd_set_workspace first");
+}  // extern "C"
+
+namespace mkd {
+
+uint64_t engine_id(const mkd_engine* e) { return e->id; }
+int32_t engine_device(const mkd_engine* e) { return e->device; }
+size_t engine_ws_bytes(const mkd_engine* e) { return e->ws_bytes; }
+int engine_fail(mkd_engine* e, int code, const char* msg) { return fail(e, code, msg); }
+
+// One step on the workspace at `ws` whose last step used epoch *epoch (advanced here):
+// validation, the step's attention item size, the counter clear and the launch.  Shared
+// by mkd_decode_step (the caller's workspace) and mkd_decode_step_static.
+int enqueue_step(mkd_engine* e, char* ws, uint32_t* epoch, void* stream, int32_t batch, const int32_t* d_tokens,
+                 const int32_t* d_seq_lens, const int32_t* h_seq_lens, const int32_t* d_page_table,
+                 const int32_t* h_page_table, void* kv_pool, int32_t n_pages, float* d_logits) {
   if (batch < 1 || batch > e->max_batch)
     return fail(e, MKD_ERR_CAPACITY, "batch must be in [1, max_batch]");
   if (!d_tokens || !d_seq_lens || !h_seq_lens || !d_page_table || !kv_pool || !d_logits)
@@ -347,6 +372,7 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
   hipError_t rc = hipSetDevice(e->device);
   if (rc != hipSuccess) return hip_fail(e, rc, "hipSetDevice");
   Params p = e->base;
+  point_params(e, ws, p);
   p.shape.pages_per_item = ppi;
   p.batch = batch;
   p.n_pages = n_pages;
@@ -355,7 +381,7 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
   p.page_table = d_page_table;
   p.kv_pool = (uint16_t*)kv_pool;
   p.logits = d_logits;
-  p.cu_offsets = (const int32_t*)(e->ws + e->r_offsets.off);
+  p.cu_offsets = (const int32_t*)(ws + e->r_offsets.off);
   p.trace = e->trace;
   p.trace_cap = e->trace_cap;
   p.spin_limit = e->spin_limit;
@@ -363,23 +389,23 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
   // used, so zeroed words never read as ready; when the 24-bit epoch wraps, the tagged
   // buffers are cleared first, so no word from 2^24 steps ago can pass for a new one.
   hipStream_t s = (hipStream_t)stream;
-  if (++e->epoch >= (1u << 24)) {
-    e->epoch = 1;
+  if (++*epoch >= (1u << 24)) {
+    *epoch = 1;
     for (const Region* r : e->regions()) {
       if (!r->tagged) continue;
-      rc = launch_clear((uint32_t*)(e->ws + r->off), (int64_t)(r->bytes / 4), s);
+      rc = launch_clear((uint32_t*)(ws + r->off), (int64_t)(r->bytes / 4), s);
       if (rc != hipSuccess) return hip_fail(e, rc, "tag clear");
     }
   }
-  p.epoch = e->epoch;
+  p.epoch = *epoch;
   rc = launch_clear(p.counters, e->plan.ctr.total, s);
   if (rc != hipSuccess) return hip_fail(e, rc, "counter clear");
   if (e->mode == MKD_MODE_MEGAKERNEL) {
-    p.tasks = (const int32_t*)(e->ws + e->r_tasks_cu.off);
+    p.tasks = (const int32_t*)(ws + e->r_tasks_cu.off);
     rc = launch_persistent(p, e->n_cu, s);
     if (rc != hipSuccess) return hip_fail(e, rc, "megakernel launch");
   } else {
-    p.tasks = (const int32_t*)(e->ws + e->r_tasks_global.off);
+    p.tasks = (const int32_t*)(ws + e->r_tasks_global.off);
     for (const Wave& w : e->plan.waves) {
       if (w.count == 0) continue;
       rc = launch_wave(p, w.first, w.count, s);
@@ -388,17 +414,40 @@ int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d
   }
   e->last_batch = batch;
   e->last_stream = s;
+  e->last_ws = ws;
   e->err.clear();
   return MKD_OK;
 }
 
+// Checks shared by both step entry points before the workspace is known.
+int check_step_state(mkd_engine* e) {
+  if (e->device < 0) return fail(e, MKD_ERR_STATE, "host-only engine cannot decode");
+  if (!e->have_weights) return fail(e, MKD_ERR_STATE, "weights not loaded");
+  return MKD_OK;
+}
+
+}  // namespace mkd
+
+extern "C" {
+
+int mkd_decode_step(mkd_engine* e, void* stream, int32_t batch, const int32_t* d_tokens,
+                    const int32_t* d_seq_lens, const int32_t* h_seq_lens, const int32_t* d_page_table,
+                    const int32_t* h_page_table, void* kv_pool, int32_t n_pages, float* d_logits) {
+  if (!e) return MKD_ERR_ARG;
+  const int st = check_step_state(e);
+  if (st != MKD_OK) return st;
+  if (!e->ws) return fail(e, MKD_ERR_STATE, "no workspace: call mkd_set_workspace first");
+  return enqueue_step(e, e->ws, &e->epoch, stream, batch, d_tokens, d_seq_lens, h_seq_lens, d_page_table,
+                      h_page_table, kv_pool, n_pages, d_logits);
+}
+
 int mkd_sync_status(mkd_engine* e) {
   if (!e) return MKD_ERR_ARG;
-  if (e->device < 0 || !e->ws) return MKD_OK;
+  if (e->device < 0 || !e->last_ws) return MKD_OK;
   hipError_t rc = hipSetDevice(e->device);
   if (rc == hipSuccess) rc = hipStreamSynchronize(e->last_stream);
   if (rc != hipSuccess) return hip_fail(e, rc, "stream synchronize");
-  uint32_t* gblock = e->base.counters + e->plan.ctr.global_base;
+  uint32_t* gblock = (uint32_t*)(e->last_ws + e->r_counters.off) + e->plan.ctr.global_base;
   uint32_t st[G_COUNT];
   rc = hipMemcpy(st, gblock, sizeof(st), hipMemcpyDeviceToHost);
   if (rc != hipSuccess) return hip_fail(e, rc, "status read");
@@ -432,6 +481,7 @@ const char* mkd_last_error(const mkd_engine* e) { return e ? e->err.c_str() : g_
 int mkd_debug_read(mkd_engine* e, int32_t what, void* dst, size_t bytes) {
   if (!e || !dst) return MKD_ERR_ARG;
   if (e->device < 0 || !e->ws) return fail(e, MKD_ERR_STATE, "no workspace");
+  if (e->last_ws != e->ws) return fail(e, MKD_ERR_STATE, "the last step did not run on the engine's workspace");
   const int64_t B = e->last_batch, L = e->cfg.n_layers, mb = e->max_batch;
   const int64_t QD = (int64_t)e->cfg.n_q_heads * e->cfg.head_dim;
   if (B < 1) return fail(e, MKD_ERR_STATE, "no step has run");

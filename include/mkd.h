@@ -160,6 +160,24 @@ int mkd_decode_step(mkd_engine* eng, void* stream, int32_t batch, const int32_t*
                     const int32_t* d_page_table, const int32_t* h_page_table, void* kv_pool,
                     int32_t n_pages, float* d_logits);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+   serving loops, harnesses that forbid hipMalloc): the same step as mkd_decode_step,
+   same arguments and errors, with the engine's workspace placed in a library-owned
+   static device array of MKD_STATIC_SCRATCH_BYTES on each device instead of a caller
+   buffer (mkd_set_workspace is not needed).  It calls no hipMalloc or hipFree.
+   MKD_ERR_CAPACITY if mkd_workspace_bytes(eng) exceeds MKD_STATIC_SCRATCH_BYTES.  Every
+   call on one GPU shares that GPU's array, which keeps the last call's contents until
+   the process ends; a call from another engine than the last one to use the array
+   clears it and copies its schedule in first (in order on `stream`).  Calls that overlap
+   on one GPU (other streams or host threads) race: serialise them.  mkd_sync_status
+   reports the errors of the last step of either kind; mkd_debug_read reads only the
+   engine's own workspace. */
+#define MKD_STATIC_SCRATCH_BYTES (64u << 20)
+int mkd_decode_step_static(mkd_engine* eng, void* stream, int32_t batch, const int32_t* d_tokens,
+                           const int32_t* d_seq_lens, const int32_t* h_seq_lens,
+                           const int32_t* d_page_table, const int32_t* h_page_table, void* kv_pool,
+                           int32_t n_pages, float* d_logits);
+
 /* Wait for the engine's last step on its stream and report device-side errors
    (section "How do you write a megakernel?": a dependency that is counted wrong shows
    up as a wait that never ends, so every wait here has a bound):
