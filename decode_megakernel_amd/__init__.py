@@ -32,6 +32,7 @@ DEBUG_ROUTER = 3
 DEBUG_Q = 4
 DEBUG_ATTN = 5
 DEBUG_ROUTE = 6
+DEBUG_ACT = 7
 ROUTE_WORDS = 1548
 DESC_WORDS = 32
 D_GIDX = 7  # descriptor word holding the task's position in the global order
@@ -201,7 +202,8 @@ class Engine:
                   DEBUG_ROUTER: ((g.n_layers, batch, g.n_experts), np.float32),
                   DEBUG_Q: ((g.n_layers, batch, qd), np.float32),
                   DEBUG_ATTN: ((g.n_layers, batch, qd), np.float32),
-                  DEBUG_ROUTE: ((g.n_layers, ROUTE_WORDS), np.int32)}
+                  DEBUG_ROUTE: ((g.n_layers, ROUTE_WORDS), np.int32),
+                  DEBUG_ACT: ((g.n_layers, batch * g.top_k, g.moe_inter), np.float32)}
         shape, dt = shapes[what]
         out = np.empty(shape, dtype=dt)
         self._check(lib().mkd_debug_read(self._h, what, out.ctypes.data, out.nbytes))

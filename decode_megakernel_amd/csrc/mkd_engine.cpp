@@ -497,6 +497,9 @@ int mkd_debug_read(mkd_engine* e, int32_t what, void* dst, size_t bytes) {
     case MKD_DEBUG_Q: inner = QD; outer = L; r = &e->r_q; break;
     case MKD_DEBUG_ATTN: inner = QD; outer = L; r = &e->r_attn_o; break;
     case MKD_DEBUG_ROUTE: inner = kRouteTableWords; outer = L; rows = 1; stride = 1; r = &e->r_tbl; break;
+    case MKD_DEBUG_ACT:
+      inner = e->cfg.moe_inter; outer = L; rows = B * e->cfg.top_k; stride = mb * e->cfg.top_k; r = &e->r_act;
+      break;
     default: return fail(e, MKD_ERR_ARG, "unknown debug buffer");
   }
   if (bytes < (size_t)(outer * rows * inner * 4)) return fail(e, MKD_ERR_ARG, "debug buffer too small");

@@ -58,7 +58,7 @@ constexpr int kMaxPagesPerWave = MKD_MAXP;  // attention pages each worker holds
 constexpr int kMaxLdsPages = MKD_LDS_PAGES;  // attention pages each worker prefetches into LDS
 constexpr int kMaccOffset = 640;      // MoE-down accumulator, floats after rowsum
 #ifndef MKD_RING
-#define MKD_RING 6
+#define MKD_RING 8
 #endif
 constexpr int kRing = MKD_RING;       // 16-byte weight chunks in flight per worker lane
 constexpr int kMaxSteps = 5;          // row steps per worker in one GEMV tile

@@ -26,6 +26,9 @@
 #ifndef MKD_PPI
 #define MKD_PPI 28  // batch 1, 8K context, 4 QKV tiles per head: 24 -> 388, 28 -> 405, 32 -> 400 tok/s
 #endif
+#ifndef MKD_ROUTER_ROWS
+#define MKD_ROUTER_ROWS 8
+#endif
 #ifndef MKD_PPI_LONG
 #define MKD_PPI_LONG 56  // batch 1, 32K context: 28 -> 257, 42 -> 312, 56 -> 321, 64 -> 311 tok/s
 #endif
@@ -55,7 +58,7 @@ struct PlanOptions {
                                // tiles covers the compute units once
   int32_t qkv_tph = MKD_QKV_TPH;  // QKV tiles per head when > 0 (tiles of up to 24 pairs): fewer,
                                   // larger tiles leave the CUs after them free for attention
-  int32_t router_rows = 16;
+  int32_t router_rows = MKD_ROUTER_ROWS;
   int32_t lm_rows = 32;
   int32_t n_attn_claimers = 0; // 0: automatic
   int32_t n_up_claimers = 0;

@@ -218,7 +218,10 @@ const char* mkd_last_error(const mkd_engine* eng);
                           [1036 + i]          entry i = b*top_k + j, experts ascending,
                                               tokens ascending within an expert
                           [1292 + b*top_k + j] (active index << 16) | position of the
-                                              entry in its expert's list               */
+                                              entry in its expert's list
+     MKD_DEBUG_ACT      fp32  [n_layers][batch*top_k][moe_inter] expert activation
+                        silu(gate) * up of choice j of token b at row b*top_k + j
+                        (MOE_UPGATE_ACT)                                                */
 #define MKD_DEBUG_HIDDEN 0
 #define MKD_DEBUG_TOPK_IDS 1
 #define MKD_DEBUG_TOPK_W 2
@@ -226,6 +229,7 @@ const char* mkd_last_error(const mkd_engine* eng);
 #define MKD_DEBUG_Q 4
 #define MKD_DEBUG_ATTN 5
 #define MKD_DEBUG_ROUTE 6
+#define MKD_DEBUG_ACT 7
 #define MKD_ROUTE_WORDS 1548
 int mkd_debug_read(mkd_engine* eng, int32_t what, void* dst, size_t bytes);
 

@@ -46,6 +46,7 @@ def load(path):
         "orc_qkv_rope_append": ([D, I64, P, P, P, P, I32, P], None),
         "orc_attention": ([D, I64, P, P, I32, P, P], None),
         "orc_topk_softmax": ([I32, I32, P, P, P], None),
+        "orc_expert_act": ([I32, I32, P, P, P], None),
         "orc_expert_ffn": ([I32, I32, P, P, P, P], None),
         "orc_moe": ([D, P, P, P, P, P, P], None),
         "orc_layer": ([D, I32, P, P, I32, P, I32, P, P, P, P, P, P, P, P, P, P, P, P, P],
@@ -150,6 +151,15 @@ def topk_softmax(logits, k):
     w = np.empty(k, dtype=np.float32)
     lib().orc_topk_softmax(logits.size, k, _p(logits), _p(ids), _p(w))
     return ids, w
+
+
+def expert_act(x, w_gate_up):
+    """silu(gate rows . x) * (up rows . x); w_gate_up [2I][H] uint16."""
+    x, w_gate_up = _f32(x), _u16(w_gate_up)
+    I = w_gate_up.shape[0] // 2
+    act = np.empty(I, dtype=np.float32)
+    lib().orc_expert_act(w_gate_up.shape[1], I, _p(x), _p(w_gate_up), _p(act))
+    return act
 
 
 def expert_ffn(x, w_gate_up, w_down):

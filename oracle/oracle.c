@@ -160,8 +160,7 @@ void orc_topk_softmax(int32_t n, int32_t k, const float* logits, int32_t* ids, f
 
 /* One expert ("Tasks": MOE_UPGATE_ACT fuses SiLU-and-multiply into the gate/up
    GEMM, MOE_DOWN projects back). */
-void orc_expert_ffn(int32_t hidden, int32_t inter, const float* x, const uint16_t* w_gate_up,
-                    const uint16_t* w_down, float* y) {
+void orc_expert_act(int32_t hidden, int32_t inter, const float* x, const uint16_t* w_gate_up, float* act) {
   float* gu = (float*)malloc(sizeof(float) * 2 * (size_t)inter);
   orc_matvec_bf16(2 * inter, hidden, w_gate_up, x, gu);
   for (int32_t i = 0; i < inter; ++i) {
@@ -169,8 +168,16 @@ void orc_expert_ffn(int32_t hidden, int32_t inter, const float* x, const uint16_
     const float silu = g / (1.0f + expf(-g));
     gu[i] = silu * gu[inter + i];
   }
-  orc_matvec_bf16(hidden, inter, w_down, gu, y);
+  memcpy(act, gu, sizeof(float) * (size_t)inter);
   free(gu);
+}
+
+void orc_expert_ffn(int32_t hidden, int32_t inter, const float* x, const uint16_t* w_gate_up,
+                    const uint16_t* w_down, float* y) {
+  float* act = (float*)malloc(sizeof(float) * (size_t)inter);
+  orc_expert_act(hidden, inter, x, w_gate_up, act);
+  orc_matvec_bf16(hidden, inter, w_down, act, y);
+  free(act);
 }
 
 /* MoE feed-forward ("Tasks": MOE_COMBINE sums a token's expert outputs weighted

@@ -75,6 +75,10 @@ void orc_attention(const orc_dims* d, int64_t pos, const int32_t* page_row,
    selected logits. */
 void orc_topk_softmax(int32_t n, int32_t k, const float* logits, int32_t* ids, float* w);
 
+/* act = silu(W_gate x) * (W_up x) for one expert ("Tasks": MOE_UPGATE_ACT); w_gate_up is
+   [2*inter][hidden], the gate rows first. */
+void orc_expert_act(int32_t hidden, int32_t inter, const float* x, const uint16_t* w_gate_up, float* act);
+
 /* y = W_down (silu(W_gate x) * (W_up x)) for one expert; w_gate_up is [2*inter][hidden]. */
 void orc_expert_ffn(int32_t hidden, int32_t inter, const float* x, const uint16_t* w_gate_up,
                     const uint16_t* w_down, float* y);

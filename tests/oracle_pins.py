@@ -274,6 +274,7 @@ def check_expert_ffn_structured():
     ref[perm] = act
     y = oracle.expert_ffn(x.astype(np.float32), gu, dn)
     assert _rel(y, ref) < 1e-5
+    assert _rel(oracle.expert_act(x.astype(np.float32), gu), act) < 1e-5
 
 
 def check_moe_equals_dense_masked_sum():

@@ -9,6 +9,7 @@ with the acceptance rules:
   routing weights;
 - page-table / KV-slot indexing: bit-exact (every pool byte outside the written
   slots unchanged; written slots hold the bf16 of k and v);
+- expert activations silu(gate) * up of the selected experts: the same bar per row;
 - expert selection identical, except where the reference's gap between the k-th
   and (k+1)-th router logit is < 1e-3 (reported, not failed); the routing table the
   kernel publishes (active experts, per-expert token lists, entry records) bit-exact
@@ -47,6 +48,7 @@ class GpuStep:
     q: np.ndarray            # [L][B][nq*hd]
     attn: np.ndarray         # [L][B][nq*hd]
     route: np.ndarray        # [L][ROUTE_WORDS] int32
+    act: np.ndarray          # [L][B*k][moe_inter]
     pool_after: np.ndarray   # uint16 bits
     pool_before: np.ndarray
     weights_bits: dict
@@ -80,6 +82,7 @@ def gpu_step(wl, mode=0, check_weights=False):
         q=eng.debug_read(mkd.DEBUG_Q, wl.batch),
         attn=eng.debug_read(mkd.DEBUG_ATTN, wl.batch),
         route=eng.debug_read(mkd.DEBUG_ROUTE, wl.batch),
+        act=eng.debug_read(mkd.DEBUG_ACT, wl.batch),
         pool_after=sdev.bf16_bits(pool),
         pool_before=pool_before,
         weights_bits={k: sdev.bf16_bits(v) for k, v in W.items()} if check_weights else {},
@@ -193,6 +196,22 @@ def check_attention(q, attn, ref_q, ref_attn, head_dim):
     return rep
 
 
+def check_act(act, ids, x, w_gate_up, k):
+    """Expert activations silu(gate) * up of every token's selected experts (the kernel's
+    own choices, which equal the reference's except at near ties) against the reference
+    expert activation on the reference's normalised input x [B][H]; per row within the bar.
+    w_gate_up: one layer's [E][2I][H] bits."""
+    ids = np.asarray(ids)
+    B = ids.shape[0]
+    worst = 0.0
+    for b in range(B):
+        for j in range(k):
+            ref = oracle.expert_act(x[b], w_gate_up[ids[b, j]])
+            worst = max(worst, max_rel_rows(act[b * k + j], ref))
+    assert worst <= REL_TOL, dict(act_rel=worst)
+    return dict(act_rel=worst)
+
+
 def compare(wl, g: GpuStep, r: dict):
     """Returns a dict of measured errors; raises AssertionError on a failed rule."""
     geo = wl.geom
@@ -216,8 +235,11 @@ def compare(wl, g: GpuStep, r: dict):
     # function replayed from the reference residual stream (near ties of the reference's
     # router logits come from that replay)
     lay = reference_layers(wl, r)
-    rep.update(q_rel=0.0, attn_rel=0.0, topk_w_rel=0.0, router_ties=0)
+    rep.update(q_rel=0.0, attn_rel=0.0, topk_w_rel=0.0, act_rel=0.0, router_ties=0)
+    wgu = r["W"]["w_gate_up"].reshape(geo.n_layers, geo.n_experts, 2 * geo.moe_inter, geo.hidden)
     for layer in range(geo.n_layers):
+        ac = check_act(g.act[layer], g.topk_ids[layer], lay["x"][layer], wgu[layer], geo.top_k)
+        rep["act_rel"] = max(rep["act_rel"], ac["act_rel"])
         a = check_attention(g.q[layer], g.attn[layer], lay["q"][layer], lay["attn"][layer], geo.head_dim)
         rt = check_route(g.route[layer], g.topk_ids[layer], g.topk_w[layer], r["ids"][layer], r["w"][layer],
                          lay["router"][layer], geo.top_k)
@@ -236,13 +258,15 @@ def compare(wl, g: GpuStep, r: dict):
 
 
 def reference_layers(wl, r):
-    """Reference intermediate values per layer (queries, attention output, router logits),
+    """Reference intermediate values per layer (normalised input, queries, attention output,
+    router logits),
     recomputed layer by layer with the reference layer function from the reference
     residual stream and the reference KV cache."""
     geo = wl.geom
     H = geo.hidden
     qd = geo.n_q_heads * geo.head_dim
-    out = dict(q=np.empty((geo.n_layers, wl.batch, qd), np.float32),
+    out = dict(x=np.empty((geo.n_layers, wl.batch, H), np.float32),
+               q=np.empty((geo.n_layers, wl.batch, qd), np.float32),
                attn=np.empty((geo.n_layers, wl.batch, qd), np.float32),
                router=np.empty((geo.n_layers, wl.batch, geo.n_experts), np.float32))
     pool = r["pool_before"].copy()

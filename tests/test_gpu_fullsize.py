@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import synth
-from parity import REL_TOL, check_attention, check_route, max_rel_rows
+from parity import REL_TOL, check_act, check_attention, check_route, max_rel_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -104,7 +104,8 @@ class GpuRun:
         self.eng.sync_status()
         rd = lambda what: self.eng.debug_read(what, B)  # noqa: E731
         return dict(logits=logits.cpu().numpy(), hidden=rd(mkd.DEBUG_HIDDEN), ids=rd(mkd.DEBUG_TOPK_IDS),
-                    w=rd(mkd.DEBUG_TOPK_W), q=rd(mkd.DEBUG_Q), attn=rd(mkd.DEBUG_ATTN), route=rd(mkd.DEBUG_ROUTE))
+                    w=rd(mkd.DEBUG_TOPK_W), q=rd(mkd.DEBUG_Q), attn=rd(mkd.DEBUG_ATTN), route=rd(mkd.DEBUG_ROUTE),
+                    act=rd(mkd.DEBUG_ACT))
 
     def pool_bits(self, layer, idx):
         nl = self.wl.geom.kv_layer_numel(self.wl.n_pages)
@@ -122,7 +123,9 @@ def check_layer_steps(wl, layer, steps_inputs, steps_out, gpu):
     g = wl.geom
     Wl = host_layer(wl, layer)
     kv = synth.host_kv_layer(wl, layer)
-    rep = dict(layer=layer, hidden_rel=0.0, kv_rel=0.0, q_rel=0.0, attn_rel=0.0, topk_w_rel=0.0, ties=0)
+    rep = dict(layer=layer, hidden_rel=0.0, kv_rel=0.0, q_rel=0.0, attn_rel=0.0, topk_w_rel=0.0, act_rel=0.0,
+               ties=0)
+    wgu = Wl["w_gate_up"].reshape(g.n_experts, 2 * g.moe_inter, g.hidden)
     for s, ((tokens, seq_lens, pt), out) in enumerate(zip(steps_inputs, steps_out)):
         h = np.array(out["hidden"][layer], dtype=np.float32, copy=True)
         o = oracle.layer(g, seq_lens, pt, kv, wl.n_pages, Wl["gamma"], Wl["w_qkv"], Wl["w_o"],
@@ -138,6 +141,8 @@ def check_layer_steps(wl, layer, steps_inputs, steps_out, gpu):
             rep[key] = max(rep[key], a[key])
         rep["topk_w_rel"] = max(rep["topk_w_rel"], rt["topk_w_rel"])
         rep["ties"] += rt["ties"]
+        ac = check_act(out["act"][layer], out["ids"][layer], o["x"], wgu, g.top_k)
+        rep["act_rel"] = max(rep["act_rel"], ac["act_rel"])
     # Pages that received a new token in any step (the GPU pool is read after the last
     # step): the new slots within tolerance of the reference's, every other slot
     # bit-exact.
