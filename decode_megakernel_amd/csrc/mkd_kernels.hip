@@ -56,7 +56,10 @@ constexpr int kMaxPagesPerWave = MKD_MAXP;  // attention pages each worker holds
 #define MKD_LDS_PAGES 4
 #endif
 constexpr int kMaxLdsPages = MKD_LDS_PAGES;  // attention pages each worker prefetches into LDS
-constexpr int kMaccOffset = 640;      // MoE-down accumulator, floats after rowsum
+#ifndef MKD_MACC
+#define MKD_MACC 1536
+#endif
+constexpr int kMaccOffset = MKD_MACC;  // output-task accumulators, floats after rowsum
 #ifndef MKD_RING
 #define MKD_RING 8
 #endif
@@ -262,6 +265,9 @@ struct RowSrc {
   // activation blocks from a table (LDS), or evenly spaced when null
   const LAS int32_t* xtab;
   int32_t xbase;
+  // with xtab: segment s has its own token count xtab[s + 1] - xtab[s], and its sums go to
+  // rowsum[(xtab[s] - xbase + j) * n1 + row % n1] (one slot per activation row)
+  int32_t segtok;
   __device__ uint32_t row_off(int i) const {
     if (eids) return (uint32_t)eids[i >> xsh] * escale + seg0 + (uint32_t)(i & (n1 - 1)) * ld;
     if (i < n1) return seg0 + (uint32_t)i * ld;
@@ -272,7 +278,7 @@ struct RowSrc {
   __device__ int32_t x_off(int i) const { return ((xtab ? xtab[i >> xsh] - xbase : (i >> xsh))) * xstep; }
 };
 __device__ __forceinline__ RowSrc row_src(const GAS uint16_t* b1, const GAS uint16_t* b2, int64_t ld, int n1) {
-  return RowSrc{b1, 0u, (uint32_t)(b2 - b1), 0u, 0u, (uint32_t)ld, n1, 0, 0, 0, nullptr, 0u, nullptr, 0};
+  return RowSrc{b1, 0u, (uint32_t)(b2 - b1), 0u, 0u, (uint32_t)ld, n1, 0, 0, 0, nullptr, 0u, nullptr, 0, 0};
 }
 
 // Lane mapping of a K-long bf16 row onto a worker wave: LPR lanes per row, CPL
@@ -346,25 +352,36 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
       if (f < F) {
         const int cc = f % G::CPL;
         const int kc = c.lane % G::LPR + G::LPR * cc;
-        const int xrow = XSEG ? src.x_off((c.wi + c.nw * (f / G::CPL)) * G::RPS + c.lane / G::LPR) : 0;
+        const int row = (c.wi + c.nw * (f / G::CPL)) * G::RPS + c.lane / G::LPR;
+        const int xrow = XSEG ? src.x_off(row) : 0;
+        // tokens of this row step (its RPS rows lie in one segment)
+        int nbs = nb, ebase = 0;
+        if (XSEG && src.segtok) {
+          const int sg = __builtin_amdgcn_readfirstlane(row >> src.xsh);
+          ebase = __builtin_amdgcn_readfirstlane(src.xtab[sg]) - src.xbase;
+          nbs = __builtin_amdgcn_readfirstlane(src.xtab[sg + 1]) - src.xbase - ebase;
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          if (NB == 1 || j < nb) {
+          if (NB == 1 || (j & ~3) < nbs) {
             const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(xs + xrow + toff[j] + kc * 8);
             acc[j] += dot8(w, xp[0], xp[1]);
           }
-          // bound the activations in flight to 4 tokens (32 registers)
+          // tokens go in groups of four without a branch inside a group, so that the
+          // group's LDS reads overlap (a token past nb reads token 0's row, toff = 0, and
+          // its sum is never stored); the barrier bounds the activations in flight to one
+          // group (32 registers)
           if (NB > 1 && (j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
         if (cc == G::CPL - 1) {
-          const int row = (c.wi + c.nw * (f / G::CPL)) * G::RPS + c.lane / G::LPR;
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
-            if (NB == 1 || j < nb) {
+            if (NB == 1 || j < nbs) {
               const float t = group_sum<G::LPR>(acc[j]);
-              if (c.lane % G::LPR == 0 && row < R) rowsum[row * nb + j] = t;
-              acc[j] = 0.0f;
+              const int slot = XSEG && src.segtok ? (ebase + j) * src.n1 + (row & (src.n1 - 1)) : row * nb + j;
+              if (c.lane % G::LPR == 0 && row < R) rowsum[slot] = t;
             }
+            acc[j] = 0.0f;
           }
         }
       }
@@ -432,6 +449,7 @@ __device__ __forceinline__ bool worker_gemv(const Ctx& c, const RowSrc& src, int
                                             const LAS int32_t* tok, int nb, LAS float* rowsum,
                                             Stage stage = Stage()) {
   if (nb == 1) return gemv_tile<K, 1, XSEG>(c, src, R, xs, tok, nb, rowsum, stage);
+  if (nb <= 4) return gemv_tile<K, 4, XSEG>(c, src, R, xs, tok, nb, rowsum, stage);
   return gemv_tile<K, kMaxBatch, XSEG>(c, src, R, xs, tok, nb, rowsum, stage);
 }
 
@@ -904,7 +922,14 @@ __device__ __forceinline__ int attn_item_count(const DParams& p) {
 // while the workers compute the next one (rows sums double-buffered).  Claimers with an
 // attention item take no MoE-up item then.  Otherwise the shared queue of the pages'
 // design is drained (below).
-constexpr int kMinFreeClaimers = 64;
+#ifndef MKD_MIN_FREE
+#define MKD_MIN_FREE 64
+#endif
+constexpr int kMinFreeClaimers = MKD_MIN_FREE;
+#ifndef MKD_STATIC_ITEMS
+#define MKD_STATIC_ITEMS 4
+#endif
+constexpr int kStaticItemsPerClaimer = MKD_STATIC_ITEMS;
 constexpr int kRowsumHalf = 1024;  // floats: the two row-sum buffers of static streaming
 
 template <int K, int NB>
@@ -972,7 +997,7 @@ __device__ __forceinline__ bool moe_up_static(Ctx& c, const DParams& p, int l, i
           const int kc = c.lane % G::LPR + G::LPR * cc;
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
-            if (NB == 1 || j < nb) {
+            if (NB == 1 || (j & ~3) < nb) {
               const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(c.s.xs + toff[j] + kc * 8);
               acc[j] += dot8(w, xp[0], xp[1]);
             }
@@ -1034,7 +1059,11 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   const int UR = p.shape.up_rows, NT = p.shape.n_up_tiles, H = p.hidden, I = p.inter, k = p.top_k;
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.up_claim);
   const int n_attn = attn_item_count(p), ci = c.d[D_ARG0], n_cl = c.d[D_ARG1];
-  const bool stat = n_cl - n_attn >= kMinFreeClaimers;
+  // static streaming when enough claimers are free of attention and each of them has a
+  // few items at most (bounded by the batch's k choices per token): otherwise the
+  // attention claimers, idle after their item, share the items through the queue
+  const int max_items = min(p.n_experts, p.batch * k) * NT;
+  const bool stat = n_cl - n_attn >= kMinFreeClaimers && max_items <= kStaticItemsPerClaimer * (n_cl - n_attn);
   if (stat && ci < n_attn) return true;  // busy with attention: no MoE-up item
   // Queue mode: static first items go to the claimers that had no attention item in this
   // step (claimer i of both queues runs on the same CU, attention first): claimer
@@ -1059,6 +1088,7 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   const int n_items = __builtin_amdgcn_readfirstlane(rt[RT_NACT]) * NT;
   if (stat) {
     if (p.batch == 1) return moe_up_static<K, 1>(c, p, l, ci - n_attn, n_cl - n_attn, n_items);
+    if (p.batch <= 4) return moe_up_static<K, 4>(c, p, l, ci - n_attn, n_cl - n_attn, n_items);
     return moe_up_static<K, kMaxBatch>(c, p, l, ci - n_attn, n_cl - n_attn, n_items);
   }
   for (int j = 0;; ++j) {
@@ -1137,7 +1167,7 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
     so.ld = (uint32_t)QD; so.n1 = R; so.xld = QD;
     so.xstep = KH; so.xsh = 31 - __builtin_clz(R);
     so.eids = nullptr; so.escale = 0u;
-    so.xtab = nullptr; so.xbase = 0;
+    so.xtab = nullptr; so.xbase = 0; so.segtok = 0;
     const int TG = min(kMaxBatch, xs_floats / QD);
     for (int t0 = 0; t0 < B; t0 += TG) {
       const int nb = min(TG, B - t0);
@@ -1166,27 +1196,34 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
       }
     }
   }
-  // (2) expert down rows: one GEMV per group of up to EPG active experts (all of them at
-  // small batch), segment s = expert a0 + s, rows addressed through the routing table
+  // (2) expert down rows: one GEMV per group of consecutive active experts whose (expert,
+  // token) entries fit the LDS (one group for the whole layer up to batch 4), segment s =
+  // expert a0 + s with its own token count, rows addressed through the routing table
   {
     const LAS int32_t* rtab = c.s.route;
     const LAS float* rw = reinterpret_cast<const LAS float*>(rtab + RT_W);
     const int n_act = __builtin_amdgcn_readfirstlane(rtab[RT_NACT]);
-    const int EPG = max(1, min(xs_floats / (B * KI), (kMaxBatch * 40) / (R * B)));
-    for (int a0 = 0; a0 < n_act; a0 += EPG) {
-      const int na = min(EPG, n_act - a0);
-      int nb = 1;
-      for (int a = a0; a < a0 + na; ++a)
-        nb = max(nb, __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a + 1]) - __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a]));
+    // entries per group: staged rows (three spare rows for the reads of a partial group of
+    // four tokens) and row-sum slots (one per entry and row, below the accumulators)
+    const int cap = min(xs_floats / KI - 4, kMaccOffset / R);
+    for (int a0 = 0; a0 < n_act;) {
+      const int ob0 = __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a0]);
+      int na = 1, nb = __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a0 + 1]) - ob0;
+      while (a0 + na < n_act) {
+        const int o1 = __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a0 + na]);
+        const int o2 = __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a0 + na + 1]);
+        if (o2 - ob0 > cap) break;
+        nb = max(nb, o2 - o1);
+        ++na;
+      }
       RowSrc sd;
       sd.base = p.w_down + (int64_t)l * E * H * KI;
       sd.seg0 = (uint32_t)r0 * KI; sd.seg1 = sd.seg2 = sd.seg3 = 0u;
       sd.ld = (uint32_t)KI; sd.n1 = R; sd.xld = KI;
       // activations entry-major: row (expert a0 + s, token j) at xs + (off[a0 + s] - off[a0] + j) * KI
-      const int ob0 = __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a0]);
       sd.xstep = KI; sd.xsh = 31 - __builtin_clz(R);
       sd.eids = rtab + RT_ACT + a0; sd.escale = (uint32_t)(H * KI);
-      sd.xtab = rtab + RT_OFF + a0; sd.xbase = ob0;
+      sd.xtab = rtab + RT_OFF + a0; sd.xbase = ob0; sd.segtok = 1;
       // activation rows of the group's (expert, token) entries in CSR order, waited for on
       // their tags by every wave: row r (entry ob0 + r) goes to xs + r * KI
       const int n_rows = __builtin_amdgcn_readfirstlane(rtab[RT_OFF + a0 + na]) - ob0;
@@ -1218,12 +1255,14 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
           const int r = i / B, b = i % B;
           float a = acc_m[r * kMaxBatch + b];
           for (int j = 0; j < k; ++j) {
-            const int ep = rtab[RT_EPOS + b * k + j], ai = (ep >> 16) - a0;
-            if (ai >= 0 && ai < na) a += rw[b * 16 + j] * c.s.rowsum[(ai * R + r) * nb + (ep & 0xFFFF)];
+            const int ep = rtab[RT_EPOS + b * k + j], ae = ep >> 16;
+            if (ae >= a0 && ae < a0 + na)
+              a += rw[b * 16 + j] * c.s.rowsum[(rtab[RT_OFF + ae] - ob0 + (ep & 0xFFFF)) * R + r];
           }
           acc_m[r * kMaxBatch + b] = a;
         }
       }
+      a0 += na;
     }
   }
   // (3) h_{l+1}[rows] = h_l + a + m and the tile's sums of squares, as tagged words (the
