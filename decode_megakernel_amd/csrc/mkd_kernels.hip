@@ -361,6 +361,11 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
           ebase = __builtin_amdgcn_readfirstlane(src.xtab[sg]) - src.xbase;
           nbs = __builtin_amdgcn_readfirstlane(src.xtab[sg + 1]) - src.xbase - ebase;
         }
+        if (NB > 1 && nbs == 1) {
+          // one token in this row step (an expert with a single token): no group of four
+          const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(xs + xrow + toff[0] + kc * 8);
+          acc[0] += dot8(w, xp[0], xp[1]);
+        } else {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           if (NB == 1 || (j & ~3) < nbs) {
@@ -372,6 +377,7 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
           // its sum is never stored); the barrier bounds the activations in flight to one
           // group (32 registers)
           if (NB > 1 && (j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
         }
         if (cc == G::CPL - 1) {
 #pragma unroll
