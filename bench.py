@@ -236,6 +236,7 @@ def run(args):
         eng.sync_status()
         eng.set_trace(None)
         rec = mtrace.decode(desc, buf.cpu().numpy())
+        del buf
         summ = mtrace.summarize(rec)
         if args.chrome:
             mtrace.chrome_trace(rec, args.trace + ".chrome.json")
@@ -243,7 +244,15 @@ def run(args):
             json.dump(summ, f, indent=1)
         out["trace_summary"] = {k: summ[k] for k in ("span_us", "layer_span_us_median",
                                                       "workgroup_busy_fraction_mean")}
-    del W, pool
+    # Release every device resource before returning: the engine (its handle; the
+    # workspace and weight references it holds), the weights, the KV pool and the step
+    # buffers, then return the caching allocator's blocks to the driver.  Nothing is left
+    # for C++ static destructors to free inside exit(), where a profiler that has already
+    # finalized its own state intercepts the calls.
+    torch.cuda.synchronize()
+    eng.close()
+    del eng, W, pool, inp, logits, tokens, seq_lens, tokens_i64
+    torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if args.calibrate_copy:
         # plain device-to-device copies of a known size, for scaling the HBM byte counters
@@ -254,6 +263,7 @@ def run(args):
             torch.mul(src, 2.0, out=dst)  # an elementwise kernel: reads and writes COPY_BYTES
         torch.cuda.synchronize()
         del src, dst
+        torch.cuda.empty_cache()
     return out, wl
 
 
@@ -289,6 +299,38 @@ def traffic_from_counters(fetch_csv, write_csv, kernel="mk_persistent"):
     return res
 
 
+def sq_summary(csv_paths, kernel="mk_persistent", n_cu=256, waves_per_cu=8):
+    """Per-dispatch medians of the SQ counters that rocprofv3 --pmc wrote for the step kernel
+    (several CSVs, one per pass), and the ratios that describe where its waves' cycles go.
+    SQ_WAVE_CYCLES and the SQ_WAIT_* / SQ_ACTIVE_INST_* counters are summed over waves (in
+    units of 4 cycles on this part, the same unit for all of them, so ratios are exact);
+    SQ_INSTS_* count wave instructions."""
+    import numpy as np
+    med = {}
+    for path in csv_paths:
+        import csv
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if kernel in row["Kernel_Name"]:
+                    vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+        med.update({k: float(np.median(v)) for k, v in vals.items()})
+    out = {"counters_median_per_dispatch": med}
+    wc = med.get("SQ_WAVE_CYCLES")
+    if wc:
+        for key in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                    "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM"):
+            if key in med:
+                out[key.lower() + "_per_wave_cycle"] = round(med[key] / wc, 4)
+    if "SQ_INSTS_LDS" in med and "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med:
+        out["lds_bank_conflict_per_active_cycle"] = round(med["SQ_LDS_BANK_CONFLICT"] / max(med["SQ_LDS_IDX_ACTIVE"], 1), 4)
+    if "SQ_INSTS_VALU" in med and "SQ_INSTS_VMEM" in med:
+        out["valu_per_vmem_inst"] = round(med["SQ_INSTS_VALU"] / max(med["SQ_INSTS_VMEM"], 1), 2)
+    if "SQ_INSTS_LDS" in med and "SQ_INSTS_VMEM" in med:
+        out["lds_per_vmem_inst"] = round(med["SQ_INSTS_LDS"] / max(med["SQ_INSTS_VMEM"], 1), 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,7 +350,13 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="reduce two rocprofv3 counter CSVs to HBM bytes per step launch and write "
                          "profiles/mk_persistent_full_b1_ctx8k_traffic.json (no GPU run)")
+    ap.add_argument("--counters", nargs="+", metavar="CSV",
+                    help="reduce rocprofv3 SQ counter CSVs of the step kernel to per-dispatch medians "
+                         "and wait/active ratios, printed as JSON (no GPU run)")
     args = ap.parse_args()
+    if args.counters:
+        print(json.dumps(sq_summary(args.counters), indent=1))
+        return
     if args.traffic:
         res = traffic_from_counters(*args.traffic)
         res["kernel_source"] = kernel_source_hash()
