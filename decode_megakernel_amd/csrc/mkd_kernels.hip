@@ -318,6 +318,25 @@ __device__ __forceinline__ uint32_t gemv_chunk_off(const Ctx& c, const RowSrc& s
 // rowsum[row * nb + j] = W[row] . x_j, x_j = xs + xo(row) + tok[j] * xld, rows < R.  NB bounds nb.
 // `stage` runs between the prefetch and the first barrier: the worker's share of a
 // team-wide wait on tagged inputs (a no-op when the controller stages alone).
+// Staged activations in LDS: rows of K fp32 values back to back, each row split so that
+// the first four values of every 8-value chunk fill its first half and the last four its
+// second half.  The lane that multiplies chunk kc (16 bytes of bf16 weights) reads its
+// activations as two 16-byte words at kc * 4 and K / 2 + kc * 4: neighbouring lanes read
+// neighbouring 16-byte slots, so a 64-lane read touches every bank once (with the natural
+// layout the 32-byte stride between lanes made every read a two-way bank conflict).
+// xsplit<K>(i) is the position of element i of the row-major activation block.
+template <int K>
+__device__ __forceinline__ int xsplit(int i) {
+  const int r = i / K, k = i - r * K;
+  return r * K + ((k & 4) ? K / 2 : 0) + ((k >> 3) << 2) + (k & 3);
+}
+template <int K>
+__device__ __forceinline__ float dot8x(const u32x4 w, const LAS float* row, int kc) {
+  const LAS f32x4* lo = reinterpret_cast<const LAS f32x4*>(row + kc * 4);
+  const LAS f32x4* hi = reinterpret_cast<const LAS f32x4*>(row + K / 2 + kc * 4);
+  return dot8(w, lo[0], hi[0]);
+}
+
 struct NoStage {
   __device__ bool operator()() const { return true; }
 };
@@ -363,14 +382,12 @@ __device__ __forceinline__ bool gemv_tile(const Ctx& c, const RowSrc& src, int R
         }
         if (NB > 1 && nbs == 1) {
           // one token in this row step (an expert with a single token): no group of four
-          const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(xs + xrow + toff[0] + kc * 8);
-          acc[0] += dot8(w, xp[0], xp[1]);
+          acc[0] += dot8x<K>(w, xs + xrow + toff[0], kc);
         } else {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           if (NB == 1 || (j & ~3) < nbs) {
-            const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(xs + xrow + toff[j] + kc * 8);
-            acc[j] += dot8(w, xp[0], xp[1]);
+            acc[j] += dot8x<K>(w, xs + xrow + toff[j], kc);
           }
           // tokens go in groups of four without a branch inside a group, so that the
           // group's LDS reads overlap (a token past nb reads token 0's row, toff = 0, and
@@ -429,8 +446,7 @@ __device__ __forceinline__ bool gemv_tile_lds(const Ctx& c, const RowSrc& src, i
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (NB == 1 || j < nb) {
-        const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(xs + toff[j] + kc * 8);
-        acc[j] += dot8(w, xp[0], xp[1]);
+        acc[j] += dot8x<K>(w, xs + toff[j], kc);
       }
     }
     if (cc == G::CPL - 1) {
@@ -480,7 +496,8 @@ __device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_entr
 }
 
 // ------------------------------------------------------------------ activation staging (team)
-// xs[b][k] = h_l[b][k] * gamma_l[k] for every token of the batch, and mf[b] = inv_rms_b:
+// xs[b][k] = h_l[b][k] * gamma_l[k] for every token of the batch (rows in the split layout
+// of xsplit), and mf[b] = inv_rms_b:
 // the RMSNorm that every consumer of layer l's input applies, with the per-token scale
 // moved to the consumer's epilogue (row sums times mf[token]).  Every wave of the team
 // waits for its share of the tagged residual rows and of the per-row-tile sums of squares
@@ -489,6 +506,7 @@ __device__ __forceinline__ bool ctl_gemv_barriers(Ctx& c, bool ok, int next_entr
 // kept while the next tasks on this CU read the same layer's input (MI_XS_LAYER, set by
 // the controller after that barrier, so that every wave of this task saw the old value).
 // Returns false on abort / watchdog; `fresh` tells whether this call staged.
+template <int K>
 __device__ __forceinline__ bool team_stage_x(const Ctx& c, int l, bool& fresh) {
   fresh = read_mi(const_cast<Ctx&>(c), MI_XS_LAYER) != l;
   if (!fresh) return true;
@@ -500,7 +518,7 @@ __device__ __forceinline__ bool team_stage_x(const Ctx& c, int l, bool& fresh) {
   LAS float* xs = c.s.xs;
   return team_poll<5>(
       c, layer_tag(p.epoch, l), nh + B * NRT, [&](int i) { return i < nh ? hb + i : sb + (i - nh); },
-      [&](int i) -> LAS float& { return xs[i]; },
+      [&](int i) -> LAS float& { return xs[i < nh ? xsplit<K>(i) : i]; },
       [&](int i) { return i < nh ? bf16_to_f32(gamma[i % H]) : 1.0f; });
 }
 __device__ __forceinline__ void stage_x_finish(Ctx& c, int l, bool fresh) {
@@ -572,7 +590,7 @@ __device__ __forceinline__ bool op_qkv(Ctx& c) {
   const GAS uint16_t* wl = p.w_qkv + (int64_t)l * (p.n_q + 2 * p.n_kv) * hd * H;
   const RowSrc src = row_src(wl + ((int64_t)hh * hd + j0) * H, wl + ((int64_t)hh * hd + half + j0) * H, H, PB);
   bool fresh = false;
-  auto stage = [&]() { return team_stage_x(c, l, fresh); };
+  auto stage = [&]() { return team_stage_x<K>(c, l, fresh); };
   if (!c.ctl) {
     // the whole tile in LDS after the staged input and its sums of squares, when it fits
     const int xs_floats = kXsBytes / 4;
@@ -665,7 +683,7 @@ __device__ __forceinline__ bool op_rows_on_x(Ctx& c, bool lm_head) {
   const GAS uint16_t* base = lm_head ? p.embed + (int64_t)r0 * H : p.w_router + ((int64_t)l * p.n_experts + r0) * H;
   const RowSrc src = row_src(base, base, H, R);
   bool fresh = false;
-  auto stage = [&]() { return team_stage_x(c, l, fresh); };
+  auto stage = [&]() { return team_stage_x<K>(c, l, fresh); };
   if (!c.ctl) {
     if (!worker_gemv<K>(c, src, R, c.s.xs, c.s.mi + MI_TOK, B, c.s.rowsum, stage)) return false;
   } else {
@@ -1004,8 +1022,7 @@ __device__ __forceinline__ bool moe_up_static(Ctx& c, const DParams& p, int l, i
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
             if (NB == 1 || (j & ~3) < nb) {
-              const LAS f32x4* xp = reinterpret_cast<const LAS f32x4*>(c.s.xs + toff[j] + kc * 8);
-              acc[j] += dot8(w, xp[0], xp[1]);
+              acc[j] += dot8x<K>(w, c.s.xs + toff[j], kc);
             }
             if (NB > 1 && (j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
           }
@@ -1079,7 +1096,7 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   int n_static = 0;
   // the layer's normed input (normally still staged by this CU's QKV or router task)
   bool fresh = false;
-  const bool staged = team_stage_x(c, l, fresh);
+  const bool staged = team_stage_x<K>(c, l, fresh);
   if (!staged && !c.ctl) c.s.mi[MI_WFAIL] = 1;
   if (c.ctl) {
     n_static = max(0, n_cl - n_attn);
@@ -1182,7 +1199,7 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
       LAS float* xs = c.s.xs;
       auto stage = [&]() {
         return team_poll<8>(c, layer_tag(p.epoch, l), nb * QD, [&](int i) { return asrc + i; },
-                            [&](int i) -> LAS float& { return xs[i]; });
+                            [&](int i) -> LAS float& { return xs[xsplit<KH>(i)]; });
       };
       if (!c.ctl) {
         if (!worker_gemv<KH, true>(c, so, NSO * R, c.s.xs, c.s.mi + MI_TOK, nb, c.s.rowsum, stage)) return false;
@@ -1239,7 +1256,7 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
         return team_poll<12>(
             c, layer_tag(p.epoch, l), n_rows * KI,
             [&](int i) { return abase + (int64_t)rtab[RT_FLAT + ob0 + i / KI] * KI + i % KI; },
-            [&](int i) -> LAS float& { return xs[i]; });
+            [&](int i) -> LAS float& { return xs[xsplit<KI>(i)]; });
       };
       if (!c.ctl) {
         if (!worker_gemv<KI, true>(c, sd, na * R, c.s.xs, c.s.mi + MI_TOK, nb, c.s.rowsum, stage)) return false;
