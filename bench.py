@@ -107,6 +107,10 @@ def cpu_baseline(wl, n_layers_sample=2, reps=2):
     }
 
 
+ORDERS = {"default": 0, "attention-first": 1, "moe-first": 2, "interleaved": 3}
+PLACEMENTS = {"round-robin": 0, "xcd": 1}
+
+
 def run(args):
     import numpy as np
     import torch
@@ -132,6 +136,7 @@ def run(args):
     eng = mkd.Engine(g, 0, max_batch=batch, max_pages_per_seq=wl.max_pages)
     eng.load_weights(W)
     eng.set_mode(mkd.MODE_OP_PER_KERNEL if args.mode == "ablation" else mkd.MODE_MEGAKERNEL)
+    eng.set_schedule(ORDERS[args.order], PLACEMENTS[args.placement])
     stream = torch.cuda.current_stream()
     logits = torch.empty((batch, g.vocab), dtype=torch.float32, device="cuda")
     tokens = inp["tokens"].clone()
@@ -199,6 +204,7 @@ def run(args):
                         f"batch {batch}, {ctx} cached tokens, greedy decode",
             "batch": batch, "context": ctx, "layers": g.n_layers, "experts": g.n_experts, "top_k": g.top_k,
             "mode": "megakernel" if args.mode != "ablation" else "op-per-kernel",
+            "order": args.order, "placement": args.placement,
         },
         "achieved_TBps": round(mean_bytes / (ms_per_step * 1e-3) / 1e12, 4),
         "sol_fraction": round(sol_ms / ms_per_step, 4),
@@ -341,6 +347,10 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (diagnostics)")
     ap.add_argument("--mode", choices=["megakernel", "ablation"], default="megakernel")
     ap.add_argument("--max-positions", type=int, default=128)
+    ap.add_argument("--order", choices=list(ORDERS), default="default",
+                    help="wave order of the task lists (the scheduler's named orders)")
+    ap.add_argument("--placement", choices=list(PLACEMENTS), default="round-robin",
+                    help="placement of the global task order onto workgroups")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace", default="", help="write a per-task trace summary (JSON) here")
     ap.add_argument("--chrome", action="store_true", help="with --trace: also write the Chrome trace")

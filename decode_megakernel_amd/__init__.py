@@ -33,8 +33,11 @@ DEBUG_Q = 4
 DEBUG_ATTN = 5
 DEBUG_ROUTE = 6
 DEBUG_ACT = 7
+ORDER_DEFAULT, ORDER_ATTN_FIRST, ORDER_MOE_FIRST, ORDER_INTERLEAVED = 0, 1, 2, 3
+PLACE_ROUND_ROBIN, PLACE_XCD = 0, 1
 ROUTE_WORDS = 1548
 DESC_WORDS = 32
+D_WAVE = 6  # descriptor word holding the task's wave index
 D_GIDX = 7  # descriptor word holding the task's position in the global order
 
 # every symbol include/mkd.h declares
@@ -42,7 +45,7 @@ EXPORTS = ("mkd_create", "mkd_destroy", "mkd_workspace_bytes", "mkd_set_workspac
            "mkd_load_weights", "mkd_set_mode", "mkd_decode_step", "mkd_decode_step_static",
            "mkd_sync_status",
            "mkd_set_watchdog", "mkd_last_error", "mkd_debug_read", "mkd_plan_inspect",
-           "mkd_set_trace")
+           "mkd_set_trace", "mkd_set_schedule")
 
 
 class MkdError(RuntimeError):
@@ -90,6 +93,7 @@ def lib():
             "mkd_last_error": ([VP], ctypes.c_char_p),
             "mkd_debug_read": ([VP, I32, VP, ctypes.c_size_t], I32),
             "mkd_plan_inspect": ([VP, I32, VP, I32, VP, P(I32)], I32),
+            "mkd_set_schedule": ([VP, I32, I32], I32),
             "mkd_set_trace": ([VP, VP, ctypes.c_size_t], I32),
         }
         for name, (args, res) in sig.items():
@@ -216,6 +220,10 @@ class Engine:
         else:
             self._check(lib().mkd_set_trace(self._h, _ptr(buf), buf.numel() * buf.element_size()))
         self._trace = buf
+
+    def set_schedule(self, order: int, placement: int = PLACE_ROUND_ROBIN):
+        """Wave order (ORDER_*) and placement (PLACE_*) of the task lists."""
+        self._check(lib().mkd_set_schedule(self._h, int(order), int(placement)))
 
     def plan(self, n_cu: int):
         """(descriptors [n_tasks][32] int32 grouped by CU, list offsets [n_cu + 1]); the

@@ -291,6 +291,33 @@ int mkd_set_workspace(mkd_engine* e, void* dev_ptr, size_t bytes) {
   return MKD_OK;
 }
 
+int mkd_set_schedule(mkd_engine* e, int32_t order, int32_t placement) {
+  if (!e) return MKD_ERR_ARG;
+  PlanOptions o = e->opts;
+  const std::string bad = set_schedule(&o, order, placement);
+  if (!bad.empty()) return fail(e, MKD_ERR_ARG, bad);
+  if (e->device >= 0) {
+    Plan plan;
+    const std::string pbad = build_plan(e->geom, o, e->max_batch, e->n_cu, &plan);
+    if (!pbad.empty()) return fail(e, MKD_ERR_ARG, "plan: " + pbad);
+    // the same number of tasks and waves: the workspace layout does not change
+    if (plan.per_cu.size() != e->plan.per_cu.size() || plan.global.size() != e->plan.global.size())
+      return fail(e, MKD_ERR_STATE, "schedule changed the task count");
+    e->plan = std::move(plan);
+    if (e->ws) {
+      hipError_t rc = hipSetDevice(e->device);
+      if (rc == hipSuccess) rc = init_workspace(e, e->ws, nullptr);
+      if (rc == hipSuccess) rc = hipStreamSynchronize(nullptr);
+      if (rc != hipSuccess) return hip_fail(e, rc, "schedule upload");
+      e->epoch = 0;
+      e->last_batch = 0;
+      e->last_ws = nullptr;
+    }
+  }
+  e->opts = o;
+  return MKD_OK;
+}
+
 int mkd_load_weights(mkd_engine* e, const mkd_weights* w) {
   if (!e) return MKD_ERR_ARG;
   if (!w || !w->embed || !w->norm || !w->w_qkv || !w->w_o || !w->w_router || !w->w_gate_up || !w->w_down)

@@ -60,6 +60,21 @@ struct Emitter {
 
 }  // namespace
 
+std::string set_schedule(PlanOptions* o, int32_t order, int32_t placement) {
+  static const int32_t orders[ORDER_COUNT][W_KINDS] = {
+      {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT},
+      {W_QKV, W_ATTN, W_ROUTER, W_MOE_UP, W_OUT},
+      {W_ROUTER, W_QKV, W_MOE_UP, W_ATTN, W_OUT},
+      {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT},
+  };
+  if (order < 0 || order >= ORDER_COUNT) return "unknown schedule order";
+  if (placement < 0 || placement >= PLACE_COUNT) return "unknown placement";
+  for (int i = 0; i < W_KINDS; ++i) o->order[i] = orders[order][i];
+  o->interleave = order == ORDER_INTERLEAVED ? 1 : 0;
+  o->placement = placement;
+  return "";
+}
+
 std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batch, int32_t n_cu, Plan* out) {
   if (max_batch < 1 || max_batch > 16) return "max_batch must be in [1, 16]";
   if (n_cu < 1) return "n_cu must be positive";
@@ -118,6 +133,17 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   for (int l = 0; l < g.n_layers; ++l) {
     for (int wi = 0; wi < W_KINDS; ++wi) {
       const int kind = o.order[wi];
+      if (o.interleave && kind == W_MOE_UP) continue;  // merged into the attention wave
+      if (o.interleave && kind == W_ATTN) {
+        // claimer i of each queue at global positions 2i and 2i + 1
+        begin_wave(W_ATTN_MOE, l);
+        for (int i = 0; i < std::max(n_attn, n_up); ++i) {
+          if (i < n_attn) em.emit(OP_ATTN, l, i, n_attn, 0, 0);
+          if (i < n_up) em.emit(OP_MOE_UP, l, i, n_up, 0, 0);
+        }
+        end_wave();
+        continue;
+      }
       begin_wave(kind, l);
       switch (kind) {
         case W_QKV:
@@ -158,12 +184,19 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
     em.emit(OP_LM_HEAD, g.n_layers, r0, std::min(o.lm_rows, g.vocab - r0), 0, 0);
   end_wave();
 
-  // Deal the tasks round robin, keeping global order within each list: task k goes to CU
-  // k mod n_cu.
+  // Deal the tasks round robin, keeping global order within each list: task k goes to
+  // workgroup k mod n_cu, or with XCD placement to the workgroup of XCD-major slot
+  // k mod n_cu (slot q: XCD q / (n_cu / 8), workgroup (q mod (n_cu / 8)) * 8 + XCD).
   const int n = P.n_tasks();
   const int n_lists = n_cu;
+  const bool xcd = o.placement == PLACE_XCD && n_cu % kXcds == 0;
+  if (o.placement == PLACE_XCD && !xcd) return "XCD placement needs a multiple of 8 compute units";
+  const int per_xcd = n_cu / kXcds;
   std::vector<std::vector<int32_t>> lists(n_lists);
-  for (int k = 0; k < n; ++k) lists[k % n_cu].push_back(k);
+  for (int k = 0; k < n; ++k) {
+    const int q = k % n_cu;
+    lists[xcd ? (q % per_xcd) * kXcds + q / per_xcd : q].push_back(k);
+  }
   P.cu_offsets.assign(n_lists + 1, 0);
   P.per_cu.reserve(P.global.size());
   for (int li = 0; li < n_lists; ++li) {
@@ -202,6 +235,10 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
         if (w.kind == W_MOE_UP) {
           up_first = w.first;
           up_end = w.first + w.count;
+        }
+        if (w.kind == W_ATTN_MOE) {
+          attn_first = up_first = w.first;
+          attn_end = up_end = w.first + w.count;
         }
         if (w.kind == W_OUT) out_first = w.first;
       }

@@ -39,8 +39,26 @@ struct Geometry {
   int32_t n_layers, hidden, n_q, n_kv, head_dim, n_experts, top_k, inter, vocab, page;
 };
 
-// Wave kinds of one layer, in the order they can be arranged.
-enum WaveKind : int32_t { W_QKV = 0, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT, W_KINDS };
+// Wave kinds of one layer, in the order they can be arranged.  W_ATTN_MOE is the merged
+// wave of the interleaved order (attention and MoE-up claimers alternating).
+enum WaveKind : int32_t { W_QKV = 0, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT, W_KINDS, W_ATTN_MOE = W_KINDS };
+
+// Named wave orders ("The task scheduler: mapping tasks to SMs": the default order and
+// its two ablations, mapped onto this design's waves, in which the attention combine
+// belongs to the attention claimers and the O-proj to the output tasks):
+//   ORDER_DEFAULT      qkv -> router -> attention -> MoE-up -> output
+//   ORDER_ATTN_FIRST   qkv -> attention -> router -> MoE-up -> output (attention is dealt
+//                      before any routing or expert work)
+//   ORDER_MOE_FIRST    router -> qkv -> MoE-up -> attention -> output
+//   ORDER_INTERLEAVED  qkv -> router -> (attention, MoE-up claimers alternating) -> output:
+//                      dealt round robin, the two branches run side by side on disjoint CUs
+enum ScheduleOrder : int32_t { ORDER_DEFAULT = 0, ORDER_ATTN_FIRST, ORDER_MOE_FIRST, ORDER_INTERLEAVED, ORDER_COUNT };
+// Placement of the global order onto workgroups (workgroup w runs on XCD w mod 8):
+//   PLACE_ROUND_ROBIN  task k -> workgroup k mod n_cu (consecutive tasks on different XCDs)
+//   PLACE_XCD          task k -> the (k mod n_cu)-th slot of an XCD-major numbering, so that
+//                      runs of n_cu / 8 consecutive tasks share one XCD and its L2
+enum SchedulePlacement : int32_t { PLACE_ROUND_ROBIN = 0, PLACE_XCD, PLACE_COUNT };
+constexpr int32_t kXcds = 8;
 
 struct PlanOptions {
   int32_t rt_rows = 8;         // residual rows per output task (O-proj + expert down rows)
@@ -66,7 +84,12 @@ struct PlanOptions {
   // attention -> MoE -> output), which measured fastest of the orders tried (MoE-up
   // before attention: 25% slower; router before QKV: no change).
   int32_t order[W_KINDS] = {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT};
+  int32_t interleave = 0;  // merge the attention and MoE-up waves (ORDER_INTERLEAVED)
+  int32_t placement = PLACE_ROUND_ROBIN;
 };
+
+// Sets o.order / o.interleave / o.placement for a named schedule; "" or an error.
+std::string set_schedule(PlanOptions* o, int32_t order, int32_t placement);
 
 struct Wave {
   int32_t kind;   // WaveKind, or -1 for embed, -2 for LM head

@@ -244,6 +244,24 @@ int mkd_debug_read(mkd_engine* eng, int32_t what, void* dst, size_t bytes);
    not recorded.  dev_buf = NULL disables it.  The caller owns the buffer. */
 int mkd_set_trace(mkd_engine* eng, void* dev_buf, size_t bytes);
 
+/* Schedule of the engine's task lists (section "The task scheduler: mapping tasks to
+   SMs": the wave order and the placement of tasks on SMs; every schedule that keeps each
+   producer wave ahead of its consumers computes the same step, bit for bit, because every
+   task waits only on tasks earlier in the global order and every reduction has a fixed
+   order).  order: MKD_ORDER_*; placement: MKD_PLACE_* (workgroup w runs on XCD w mod 8;
+   XCD placement puts runs of n_cu / 8 consecutive tasks on one XCD).  Rebuilds the lists
+   and, when a workspace is set, uploads them synchronously (a set-up call, not for the
+   decode loop; the next step starts a new epoch).  Also applies to mkd_plan_inspect.
+   MKD_ERR_ARG for an unknown order or placement, or an XCD placement on a device whose
+   compute-unit count is not a multiple of 8. */
+#define MKD_ORDER_DEFAULT 0     /* qkv, router, attention, MoE-up, output */
+#define MKD_ORDER_ATTN_FIRST 1  /* qkv, attention, router, MoE-up, output */
+#define MKD_ORDER_MOE_FIRST 2   /* router, qkv, MoE-up, attention, output */
+#define MKD_ORDER_INTERLEAVED 3 /* qkv, router, attention and MoE-up claimers alternating, output */
+#define MKD_PLACE_ROUND_ROBIN 0
+#define MKD_PLACE_XCD 1
+int mkd_set_schedule(mkd_engine* eng, int32_t order, int32_t placement);
+
 /* Plan inspection (host only; works on an engine created with hip_device = -1): writes
    the task descriptors the scheduler builds onto `n_cu` compute units (section "The
    task scheduler: mapping tasks to SMs"; section "The task descriptor": 32 int32 per

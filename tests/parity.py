@@ -54,7 +54,7 @@ class GpuStep:
     weights_bits: dict
 
 
-def gpu_step(wl, mode=0, check_weights=False):
+def gpu_step(wl, mode=0, check_weights=False, schedule=None):
     import torch
 
     import decode_megakernel_amd as mkd
@@ -68,6 +68,8 @@ def gpu_step(wl, mode=0, check_weights=False):
     eng = mkd.Engine(wl.geom, 0, max_batch=wl.batch, max_pages_per_seq=wl.max_pages)
     eng.load_weights(W)
     eng.set_mode(mode)
+    if schedule is not None:
+        eng.set_schedule(*schedule)
     logits = torch.full((wl.batch, wl.geom.vocab), float("nan"), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     eng.decode_step(inp["tokens"], inp["seq_lens"], inp["h_seq_lens"], inp["page_table"], pool,

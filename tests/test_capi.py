@@ -107,3 +107,63 @@ def test_plan_structure(geom, max_batch, n_cu):
         assert sorted(o[:, 2].tolist()) == list(range(n_rt))
         nxt = qkv[qkv[:, 1] == layer + 1] if layer + 1 < geom.n_layers else desc[ops == OP_LM_HEAD]
         assert nxt[:, GI].min() > o[:, GI].max()
+
+
+def _task_key(d):
+    # the descriptor without its wave and global indices (which the order renumbers)
+    return tuple(int(v) for v in np.delete(d, [mkd.D_WAVE, GI]))
+
+
+@pytest.mark.parametrize("geom", [synth.TINY, synth.FULL])
+@pytest.mark.parametrize("order", [mkd.ORDER_DEFAULT, mkd.ORDER_ATTN_FIRST, mkd.ORDER_MOE_FIRST,
+                                   mkd.ORDER_INTERLEAVED])
+@pytest.mark.parametrize("placement", [mkd.PLACE_ROUND_ROBIN, mkd.PLACE_XCD])
+def test_schedules_same_tasks_other_order(geom, order, placement):
+    """Every named schedule deals the same tasks (same descriptors but for the global
+    index) in the order and onto the workgroups it names, and passes the static checks."""
+    n_cu = 256
+    ref = mkd.Engine(geom, -1, 4, 64)
+    d0, _ = ref.plan(n_cu)
+    e = mkd.Engine(geom, -1, 4, 64)
+    e.set_schedule(order, placement)
+    desc, offs = e.plan(n_cu)
+    assert sorted(_task_key(d) for d in desc) == sorted(_task_key(d) for d in d0)
+    glob = desc[np.argsort(desc[:, GI])]
+    ops, layers = glob[:, 0], glob[:, 1]
+    for layer in range(geom.n_layers):
+        pos = {op: np.nonzero((ops == op) & (layers == layer))[0] for op in (OP_QKV, OP_ROUTER, OP_ATTN, OP_MOE_UP, OP_OUT)}
+        first = {op: p.min() for op, p in pos.items()}
+        last = {op: p.max() for op, p in pos.items()}
+        # producers ahead of consumers in every schedule
+        assert last[OP_QKV] < first[OP_ATTN] and last[OP_ROUTER] < first[OP_MOE_UP]
+        assert max(last[OP_ATTN], last[OP_MOE_UP]) < first[OP_OUT]
+        if order == mkd.ORDER_DEFAULT:
+            assert last[OP_ROUTER] < first[OP_ATTN] and last[OP_ATTN] < first[OP_MOE_UP]
+        elif order == mkd.ORDER_ATTN_FIRST:
+            assert last[OP_ATTN] < first[OP_ROUTER]
+        elif order == mkd.ORDER_MOE_FIRST:
+            assert last[OP_ROUTER] < first[OP_QKV] and last[OP_MOE_UP] < first[OP_ATTN]
+        else:
+            # claimer i of the attention queue directly followed by claimer i of the MoE queue
+            a, m = pos[OP_ATTN], pos[OP_MOE_UP]
+            assert (glob[a, 2] == np.arange(len(a))).all() and (m - a == 1).all()
+    for li in range(n_cu):
+        g = desc[offs[li]:offs[li + 1], GI]
+        assert (np.diff(g) > 0).all()
+        q = g % n_cu
+        if placement == mkd.PLACE_ROUND_ROBIN:
+            assert (q == li).all()
+        else:
+            # XCD-major slots: workgroup li runs on XCD li mod 8 and takes the slots of its XCD
+            assert ((q // (n_cu // 8)) == li % 8).all() and ((q % (n_cu // 8)) * 8 + q // (n_cu // 8) == li).all()
+
+
+def test_schedule_rejects_bad_arguments():
+    e = mkd.Engine(synth.TINY, -1, 1, 8)
+    for order, placement in ((4, 0), (-1, 0), (0, 2)):
+        assert mkd.lib().mkd_set_schedule(e._h, order, placement) == mkd.MKD_ERR_ARG
+    e.set_schedule(mkd.ORDER_DEFAULT, mkd.PLACE_XCD)
+    with pytest.raises(mkd.MkdError):
+        e.plan(7)   # XCD placement needs a multiple of 8 compute units
+    e.set_schedule(mkd.ORDER_DEFAULT, mkd.PLACE_ROUND_ROBIN)
+    e.plan(7)
