@@ -45,7 +45,10 @@ EXPORTS = ("mkd_create", "mkd_destroy", "mkd_workspace_bytes", "mkd_set_workspac
            "mkd_load_weights", "mkd_set_mode", "mkd_decode_step", "mkd_decode_step_static",
            "mkd_sync_status",
            "mkd_set_watchdog", "mkd_last_error", "mkd_debug_read", "mkd_plan_inspect",
-           "mkd_set_trace", "mkd_set_schedule")
+           "mkd_set_trace", "mkd_set_schedule",
+           "mkd_server_create", "mkd_server_destroy", "mkd_server_buffer_bytes", "mkd_server_set_buffer",
+           "mkd_server_join", "mkd_server_step", "mkd_server_last_step", "mkd_server_stats",
+           "mkd_server_last_error")
 
 
 class MkdError(RuntimeError):
@@ -95,6 +98,15 @@ def lib():
             "mkd_plan_inspect": ([VP, I32, VP, I32, VP, P(I32)], I32),
             "mkd_set_schedule": ([VP, I32, I32], I32),
             "mkd_set_trace": ([VP, VP, ctypes.c_size_t], I32),
+            "mkd_server_create": ([VP, I32, I32, P(VP)], I32),
+            "mkd_server_destroy": ([VP], None),
+            "mkd_server_buffer_bytes": ([VP], ctypes.c_size_t),
+            "mkd_server_set_buffer": ([VP, VP, ctypes.c_size_t], I32),
+            "mkd_server_join": ([VP, ctypes.c_int64, I32, I32, I32, VP, I32], I32),
+            "mkd_server_step": ([VP, VP, VP, P(I32)], I32),
+            "mkd_server_last_step": ([VP, VP, VP, VP, VP, VP, VP, I32, P(I32)], I32),
+            "mkd_server_stats": ([VP, P(I32), P(I32), P(I32)], I32),
+            "mkd_server_last_error": ([VP], ctypes.c_char_p),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -125,6 +137,7 @@ class Engine:
 
     def __init__(self, geom, device: int, max_batch: int, max_pages_per_seq: int, workspace=True):
         self.geom = geom
+        self.device = device
         self.max_batch = max_batch
         self.max_pages = max_pages_per_seq
         self._cfg = config_of(geom)
@@ -237,3 +250,90 @@ class Engine:
         self._check(lib().mkd_plan_inspect(self._h, n_cu, desc.ctypes.data, n.value,
                                            offs.ctypes.data, ctypes.byref(n)))
         return desc, offs
+
+
+class Server:
+    """The continuous-decode loop (mkd_server_*) over an engine: sequences join with a
+    cached length and a first token, each step feeds every scheduled sequence and samples
+    greedily, finished sequences retire.  The device buffer is a torch uint8 tensor."""
+
+    def __init__(self, engine: Engine, n_pages: int, max_live: int):
+        import torch
+
+        self.engine = engine
+        h = ctypes.c_void_p()
+        rc = lib().mkd_server_create(engine._h, int(n_pages), int(max_live), ctypes.byref(h))
+        if rc != MKD_OK:
+            raise MkdError(rc, "mkd_server_create failed")
+        self._h = h.value
+        self.max_batch = engine.max_batch
+        self.max_pages = engine.max_pages
+        self.vocab = engine.geom.vocab
+        self._buf = None
+        if engine.device >= 0:
+            self._buf = torch.empty(lib().mkd_server_buffer_bytes(self._h), dtype=torch.uint8,
+                                    device=f"cuda:{engine.device}")
+            self._check(lib().mkd_server_set_buffer(self._h, _ptr(self._buf), self._buf.numel()))
+
+    def _check(self, rc):
+        if rc != MKD_OK:
+            raise MkdError(rc, lib().mkd_server_last_error(self._h).decode())
+
+    def join(self, seq_id: int, cached_len: int, first_token: int, max_new_tokens: int) -> np.ndarray:
+        """Returns the physical pages given to the cached tokens (to be filled by the caller)."""
+        pages = np.empty(max(1, self.max_pages), dtype=np.int32)
+        self._check(lib().mkd_server_join(self._h, int(seq_id), int(cached_len), int(first_token),
+                                          int(max_new_tokens), pages.ctypes.data, pages.size))
+        return pages[:-(-int(cached_len) // self.engine.geom.page_size)] if cached_len > 0 else pages[:0]
+
+    def try_join(self, *args) -> "np.ndarray | None":
+        try:
+            return self.join(*args)
+        except MkdError as e:
+            if e.code == MKD_ERR_CAPACITY:
+                return None
+            raise
+
+    def step(self, kv_pool, stream=None) -> int:
+        if stream is not None or kv_pool is None:
+            s = stream or 0
+        else:
+            import torch
+
+            s = torch.cuda.current_stream().cuda_stream
+        n = ctypes.c_int32()
+        self._check(lib().mkd_server_step(self._h, ctypes.c_void_p(s), _ptr(kv_pool), ctypes.byref(n)))
+        return n.value
+
+    def last_step(self, logits=False) -> dict:
+        B, P = self.max_batch, self.max_pages
+        ids = np.empty(B, np.int64)
+        fed, smp, lens = (np.empty(B, np.int32) for _ in range(3))
+        table = np.empty((B, P), np.int32)
+        lg = np.empty((B, self.vocab), np.float32) if logits else None
+        n = ctypes.c_int32()
+        self._check(lib().mkd_server_last_step(self._h, ids.ctypes.data, fed.ctypes.data, smp.ctypes.data,
+                                               lens.ctypes.data, table.ctypes.data,
+                                               lg.ctypes.data if logits else None, B, ctypes.byref(n)))
+        b = n.value
+        out = dict(ids=ids[:b], fed=fed[:b], sampled=smp[:b], seq_lens=lens[:b], page_table=table[:b])
+        if logits:
+            out["logits"] = lg[:b]
+        return out
+
+    def stats(self) -> dict:
+        a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        self._check(lib().mkd_server_stats(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+        return dict(live=a.value, parked=b.value, free_pages=c.value)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().mkd_server_destroy(self._h)
+            self._h = None
+        self._buf = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -355,6 +355,12 @@ uint64_t engine_id(const mkd_engine* e) { return e->id; }
 int32_t engine_device(const mkd_engine* e) { return e->device; }
 size_t engine_ws_bytes(const mkd_engine* e) { return e->ws_bytes; }
 int engine_fail(mkd_engine* e, int code, const char* msg) { return fail(e, code, msg); }
+void engine_limits(const mkd_engine* e, int32_t* max_batch, int32_t* max_pages, int32_t* vocab, int32_t* page) {
+  *max_batch = e->max_batch;
+  *max_pages = e->max_pages;
+  *vocab = e->cfg.vocab;
+  *page = e->cfg.page_size;
+}
 
 // One step on the workspace at `ws` whose last step used epoch *epoch (advanced here):
 // validation, the step's attention item size, the counter clear and the launch.  Shared

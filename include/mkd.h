@@ -244,6 +244,62 @@ int mkd_debug_read(mkd_engine* eng, int32_t what, void* dst, size_t bytes);
    not recorded.  dev_buf = NULL disables it.  The caller owns the buffer. */
 int mkd_set_trace(mkd_engine* eng, void* dev_buf, size_t bytes);
 
+/* ---------------------------------------------------------------- continuous decode
+   The loop around the step (section "The serving engine around the kernel": each step
+   updates the KV positions and page tables, clears the step state, selects the schedule
+   by the longest live context, launches, samples and retires finished sequences, while
+   others join; a sequence that cannot get a KV page waits).  A server borrows an engine
+   (which must outlive it and have its weights and workspace set) and manages n_pages
+   physical pages of a caller-owned KV pool laid out as for mkd_decode_step.
+
+   mkd_server_create     up to max_live (<= 4096) live sequences; allocates only pinned
+                         host staging (two copies of the step's upload) at creation.  Over
+                         a host-only engine the server does every step's scheduling and
+                         bookkeeping without launching (kv_pool may be NULL, no buffer;
+                         mkd_server_last_step reports fed = the first token of a new
+                         sequence, else -1, and sampled = -1).
+   mkd_server_buffer_bytes / mkd_server_set_buffer
+                         a caller-owned device buffer (256-byte aligned) for the step's
+                         inputs, the logits [max_batch][vocab] fp32 and the sampled tokens;
+                         settable while no sequence is live.
+   mkd_server_join       a sequence with cached_len tokens already in the cache, fed
+                         first_token at position cached_len, generating max_new_tokens
+                         tokens (greedy); ceil(cached_len / page_size) pages are taken
+                         from the free list now and written to h_pages (the caller fills
+                         them with the cached K/V, ordered after the previous step on
+                         its stream).  MKD_ERR_CAPACITY when max_live sequences are live
+                         or too few pages are free (nothing is taken), MKD_ERR_ARG for a
+                         duplicate id or a sequence longer than max_pages_per_seq pages.
+   mkd_server_step       one step on `stream`: the live sequences in join order, up to
+                         the engine's max_batch; a sequence whose next token opens a page
+                         takes a free page or is parked (keeps its pages, skipped) until
+                         one is free.  Feeds each sequence its first token or its last
+                         sampled token, runs mkd_decode_step, samples every row with an
+                         argmax (ties to the lower id), retires the sequences that have
+                         generated their tokens (their pages return to the free list).
+                         Asynchronous: one upload and one download on the stream, no
+                         allocation.  *n_scheduled = the step's batch (0 when nothing is
+                         live).  MKD_ERR_CAPACITY when every live sequence is parked;
+                         errors of mkd_decode_step are passed on.
+   mkd_server_last_step  waits for the last step and reports its batch: sequence ids,
+                         tokens fed, tokens sampled, seq_lens (the fed token's position),
+                         page-table rows [batch][max_pages_per_seq] and, when logits is
+                         not NULL, the logits [batch][vocab] (a synchronous copy); any
+                         output pointer may be NULL.
+   mkd_server_stats      live and parked sequences, free pages. */
+typedef struct mkd_server mkd_server;
+int mkd_server_create(mkd_engine* eng, int32_t n_pages, int32_t max_live, mkd_server** out);
+void mkd_server_destroy(mkd_server* srv);
+size_t mkd_server_buffer_bytes(const mkd_server* srv);
+int mkd_server_set_buffer(mkd_server* srv, void* dev_ptr, size_t bytes);
+int mkd_server_join(mkd_server* srv, int64_t seq_id, int32_t cached_len, int32_t first_token,
+                    int32_t max_new_tokens, int32_t* h_pages, int32_t max_pages_out);
+int mkd_server_step(mkd_server* srv, void* stream, void* kv_pool, int32_t* n_scheduled);
+int mkd_server_last_step(mkd_server* srv, int64_t* ids, int32_t* fed, int32_t* sampled, int32_t* seq_lens,
+                         int32_t* page_table, float* logits, int32_t max_batch_out, int32_t* batch);
+int mkd_server_stats(const mkd_server* srv, int32_t* n_live, int32_t* n_parked, int32_t* n_free_pages);
+const char* mkd_server_last_error(const mkd_server* srv);
+
 /* Schedule of the engine's task lists (section "The task scheduler: mapping tasks to
    SMs": the wave order and the placement of tasks on SMs; every schedule that keeps each
    producer wave ahead of its consumers computes the same step, bit for bit, because every
