@@ -9,7 +9,7 @@
 // A step schedules the live sequences in join order up to the engine's max_batch.  A
 // sequence whose next token starts a new page takes one from the free list; when the
 // list is empty it is parked (it keeps its pages and is not scheduled) and resumes at the
-// first step where a page is free.  After the step kernel an argmax kernel samples every
+// first step where a page is free.  After the step kernel two argmax kernels sample every
 // row (ties to the lower token id) into the token that sequence is fed next; sequences
 // that have generated their tokens retire and return their pages.  The step's attention
 // item size follows the longest live context (chosen inside the engine's step).
@@ -44,30 +44,36 @@ __global__ void serve_gather(const int32_t* __restrict__ slot_of, const int32_t*
   }
 }
 
-// One workgroup of 256 threads per row: the index of the row's largest logit, the lowest
-// index among equal maxima (NaN never wins; a row without a number gives 0).
-__global__ void __launch_bounds__(256) serve_argmax(const float* __restrict__ logits, int32_t vocab,
-                                                    const int32_t* __restrict__ slot_of, int32_t* __restrict__ slot_tok,
-                                                    int32_t* __restrict__ sampled) {
-  const int b = blockIdx.x;
-  const float* row = logits + (int64_t)b * vocab;
-  float best = -INFINITY;
-  int32_t bi = 0x7FFFFFFF;
-  for (int i = threadIdx.x; i < vocab; i += 256) {
-    const float v = row[i];
-    if (v > best || (v == best && i < bi)) {
-      best = v;
-      bi = i;
-    }
+// Greedy sampling in two passes: workgroup (c, b) finds the largest logit of chunk c of
+// row b (kArgmaxChunks chunks per row, 256 threads) and its lowest index among equal
+// maxima; one wave per row then combines the chunks in the same way.  NaN never wins; a
+// row without a number gives token 0.
+constexpr int kArgmaxChunks = 64;
+
+__device__ __forceinline__ void argmax_take(float& best, int32_t& bi, float v, int32_t i) {
+  if (v > best || (v == best && i < bi)) {
+    best = v;
+    bi = i;
   }
+}
+__device__ __forceinline__ void argmax_wave(float& best, int32_t& bi) {
   for (int off = 32; off > 0; off >>= 1) {
     const float ov = __shfl_xor(best, off);
     const int32_t oi = __shfl_xor(bi, off);
-    if (ov > best || (ov == best && oi < bi)) {
-      best = ov;
-      bi = oi;
-    }
+    argmax_take(best, bi, ov, oi);
   }
+}
+
+__global__ void __launch_bounds__(256) serve_argmax_chunks(const float* __restrict__ logits, int32_t vocab,
+                                                           float* __restrict__ part_v, int32_t* __restrict__ part_i) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int per = (vocab + kArgmaxChunks - 1) / kArgmaxChunks;
+  const int lo = c * per, hi = min(vocab, lo + per);
+  const float* row = logits + (int64_t)b * vocab;
+  float best = -INFINITY;
+  int32_t bi = 0x7FFFFFFF;
+  for (int i = lo + (int)threadIdx.x; i < hi; i += 256) argmax_take(best, bi, row[i], i);
+  argmax_wave(best, bi);
   __shared__ float sv[4];
   __shared__ int32_t si[4];
   if ((threadIdx.x & 63) == 0) {
@@ -76,16 +82,26 @@ __global__ void __launch_bounds__(256) serve_argmax(const float* __restrict__ lo
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
-      if (sv[w] > best || (sv[w] == best && si[w] < bi)) {
-        best = sv[w];
-        bi = si[w];
-      }
+    for (int w = 1; w < 4; ++w) argmax_take(best, bi, sv[w], si[w]);
+    part_v[b * kArgmaxChunks + c] = best;
+    part_i[b * kArgmaxChunks + c] = bi;
+  }
+}
+
+__global__ void __launch_bounds__(64) serve_argmax_final(const float* __restrict__ part_v, const int32_t* __restrict__ part_i,
+                                                         const int32_t* __restrict__ slot_of, int32_t* __restrict__ slot_tok,
+                                                         int32_t* __restrict__ sampled) {
+  const int b = blockIdx.x;
+  float best = part_v[b * kArgmaxChunks + threadIdx.x];
+  int32_t bi = part_i[b * kArgmaxChunks + threadIdx.x];
+  argmax_wave(best, bi);
+  if (threadIdx.x == 0) {
     if (bi == 0x7FFFFFFF) bi = 0;
     sampled[b] = bi;
     slot_tok[slot_of[b]] = bi;
   }
 }
+static_assert(kArgmaxChunks == 64, "the final pass is one wave");
 
 struct Seq {
   int64_t id;
@@ -108,9 +124,10 @@ struct mkd_server {
   std::vector<int32_t> free_pages;  // a stack; the lowest page on top at creation
   std::vector<Seq> live;            // join order
   std::vector<char> slot_used;
-  // device buffer (caller-owned): upload area | tokens | per-slot tokens | sampled | logits
+  // device buffer (caller-owned): upload area | tokens | per-slot tokens | sampled |
+  // argmax partials | logits
   char* dev = nullptr;
-  size_t off_up = 0, off_tok = 0, off_slot = 0, off_smp = 0, off_logits = 0, bytes = 0;
+  size_t off_up = 0, off_tok = 0, off_slot = 0, off_smp = 0, off_part = 0, off_logits = 0, bytes = 0;
   int32_t up_ints = 0;  // 3 * max_batch + max_batch * max_pages
   // pinned host memory: two staging copies of the upload area, fed and sampled tokens
   int32_t* stage[2] = {nullptr, nullptr};
@@ -168,6 +185,8 @@ int mkd_server_create(mkd_engine* eng, int32_t n_pages, int32_t max_live, mkd_se
   at = align256(at + sizeof(int32_t) * (size_t)max_live);
   s->off_smp = at;
   at = align256(at + sizeof(int32_t) * (size_t)s->max_batch);
+  s->off_part = at;
+  at = align256(at + (sizeof(float) + sizeof(int32_t)) * (size_t)s->max_batch * kArgmaxChunks);
   s->off_logits = at;
   at = align256(at + sizeof(float) * (size_t)s->max_batch * s->vocab);
   s->bytes = at;
@@ -325,8 +344,14 @@ int mkd_server_step(mkd_server* s, void* stream, void* kv_pool, int32_t* n_sched
   if (rc != hipSuccess) return shfail(s, rc, "token gather launch");
   const int r = mkd_decode_step(s->eng, stream, B, d_tok, d_up, lens, d_up + 3 * MB, table, kv_pool, s->n_pages, d_logits);
   if (r != MKD_OK) return sfail(s, r, std::string("step: ") + mkd_last_error(s->eng));
-  serve_argmax<<<B, 256, 0, st>>>(d_logits, s->vocab, d_up + MB, d_slot, d_smp);
+  float* d_pv = (float*)(s->dev + s->off_part);
+  int32_t* d_pi = (int32_t*)(d_pv + (size_t)MB * kArgmaxChunks);
+  serve_argmax_chunks<<<dim3(kArgmaxChunks, B), 256, 0, st>>>(d_logits, s->vocab, d_pv, d_pi);
   rc = hipGetLastError();
+  if (rc == hipSuccess) {
+    serve_argmax_final<<<B, 64, 0, st>>>(d_pv, d_pi, d_up + MB, d_slot, d_smp);
+    rc = hipGetLastError();
+  }
   if (rc == hipSuccess) rc = hipMemcpyAsync(s->h_fed, d_tok, sizeof(int32_t) * B, hipMemcpyDeviceToHost, st);
   if (rc == hipSuccess) rc = hipMemcpyAsync(s->h_smp, d_smp, sizeof(int32_t) * B, hipMemcpyDeviceToHost, st);
   if (rc != hipSuccess) return shfail(s, rc, "sampling");

@@ -133,6 +133,15 @@ def ragged_workload(geom: Geometry, seq_lens: Sequence[int], spare_pages: int = 
     return make_workload(f"ragged-b{len(seq_lens)}", geom, list(seq_lens), spare_pages=spare_pages)
 
 
+def continuous_sequences(n: int, vocab: int, seed: int = 11, cached=(512, 32768), new=(8, 64)):
+    """A seeded stream of sequences for continuous batching: (id, cached tokens drawn
+    uniform in [cached[0], cached[1]], first token uniform over the vocabulary, tokens to
+    generate uniform in [new[0], new[1]])."""
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(cached[0], cached[1] + 1)), int(rng.integers(0, vocab)),
+             int(rng.integers(new[0], new[1] + 1))) for i in range(n)]
+
+
 def page_tables(wl: Workload) -> np.ndarray:
     """[batch][max_pages] int32 page table: every sequence's logical pages map to
     distinct physical pages of one randomly permuted pool (unused entries -1)."""
