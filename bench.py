@@ -250,6 +250,12 @@ def run(args):
             json.dump(summ, f, indent=1)
         out["trace_summary"] = {k: summ[k] for k in ("span_us", "layer_span_us_median",
                                                       "workgroup_busy_fraction_mean")}
+        if args.tile_report:
+            # the traced step's positions and the experts it selected
+            off = (args.warmup + args.steps) % args.max_positions
+            tids = eng.debug_read(mkd.DEBUG_TOPK_IDS, batch)
+            out["tile_report"] = mtrace.tile_report(rec, g, [s + off for s in wl.seq_lens],
+                                                    [len(np.unique(tids[l])) for l in range(g.n_layers)])
     # Release every device resource before returning: the engine (its handle; the
     # workspace and weight references it holds), the weights, the KV pool and the step
     # buffers, then return the caching allocator's blocks to the driver.  Nothing is left
@@ -434,6 +440,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace", default="", help="write a per-task trace summary (JSON) here")
     ap.add_argument("--chrome", action="store_true", help="with --trace: also write the Chrome trace")
+    ap.add_argument("--tile-report", action="store_true",
+                    help="with --trace: per-operation bandwidth of the traced step (phase GB/s, per-CU GB/s)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the run, multiply 1 GiB into another 1 GiB buffer three times "
                          "(calibration of the HBM byte counters)")

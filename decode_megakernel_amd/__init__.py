@@ -48,7 +48,7 @@ EXPORTS = ("mkd_create", "mkd_destroy", "mkd_workspace_bytes", "mkd_set_workspac
            "mkd_set_trace", "mkd_set_schedule",
            "mkd_server_create", "mkd_server_destroy", "mkd_server_buffer_bytes", "mkd_server_set_buffer",
            "mkd_server_join", "mkd_server_step", "mkd_server_last_step", "mkd_server_stats",
-           "mkd_server_last_error")
+           "mkd_server_last_error", "mkd_protocol_litmus")
 
 
 class MkdError(RuntimeError):
@@ -107,6 +107,7 @@ def lib():
             "mkd_server_last_step": ([VP, VP, VP, VP, VP, VP, VP, I32, P(I32)], I32),
             "mkd_server_stats": ([VP, P(I32), P(I32), P(I32)], I32),
             "mkd_server_last_error": ([VP], ctypes.c_char_p),
+            "mkd_protocol_litmus": ([I32, I32, I32, VP], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -337,3 +338,12 @@ class Server:
             self.close()
         except Exception:
             pass
+
+
+def protocol_litmus(device: int, n_pairs: int = 128, rounds: int = 2000) -> dict:
+    """Message-passing litmus test of the inter-workgroup protocol (mkd_protocol_litmus)."""
+    res = np.zeros(4, dtype=np.uint32)
+    rc = lib().mkd_protocol_litmus(int(device), int(n_pairs), int(rounds), res.ctypes.data)
+    if rc != MKD_OK:
+        raise MkdError(rc, "mkd_protocol_litmus failed")
+    return dict(torn_words=int(res[0]), stale_data=int(res[1]), timeouts=int(res[2]), rounds_done=int(res[3]))

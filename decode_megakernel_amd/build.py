@@ -13,7 +13,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["mkd_kernels.hip", "mkd_plan.cpp", "mkd_engine.cpp", "mkd_static.hip", "mkd_serve.hip"]
+SOURCES = ["mkd_kernels.hip", "mkd_plan.cpp", "mkd_engine.cpp", "mkd_static.hip", "mkd_serve.hip", "mkd_litmus.hip"]
 
 
 def build(verbose=False, extra=(), out=SO):

@@ -18,7 +18,7 @@ TICK_US = 0.01  # 100 MHz
 
 
 def decode(desc: np.ndarray, trace: np.ndarray) -> dict:
-    """desc: [n][32] descriptors (any order, field 10 = global index); trace: [>=n][4] uint64."""
+    """desc: [n][32] descriptors (any order, field 7 = global index); trace: [>=n][4] uint64."""
     gidx = desc[:, 7]  # descriptor word D_GIDX
     order = np.argsort(gidx)
     d = desc[order]
@@ -115,3 +115,48 @@ def chrome_trace(rec: dict, path: str) -> None:
                             "staged": round(float(rec["staged"][i]), 3), "done": round(float(rec["done"][i]), 3)}})
     with open(path, "w") as f:
         json.dump({"traceEvents": ev, "displayTimeUnit": "ns"}, f)
+
+
+def op_bytes(geom, seq_lens, n_distinct) -> dict:
+    """Algorithmic bytes each operation of one layer streams (bf16 weights, cached K/V):
+    QKV rows, router rows, every cached K and V of the batch, gate/up rows of the distinct
+    selected experts, O-proj plus their down rows."""
+    H, I, hd, nq, nkv, bf = geom.hidden, geom.moe_inter, geom.head_dim, geom.n_q_heads, geom.n_kv_heads, 2
+    return {
+        "qkv": geom.qkv_rows * H * bf,
+        "router": geom.n_experts * H * bf,
+        "attn": sum(s + 1 for s in seq_lens) * nkv * hd * 2 * bf,
+        "moe_up": n_distinct * 2 * I * H * bf,
+        "out": (H * nq * hd + n_distinct * H * I) * bf,
+    }
+
+
+def tile_report(rec: dict, geom, seq_lens, distinct) -> dict:
+    """Per operation, the median over layers 1 .. L-1 of: the phase bandwidth (its bytes
+    over the span from its first input-ready time to its last end) and the per-CU rate (its
+    bytes over the summed work time of its tasks, i.e. the rate of one CU while it works on
+    that operation); distinct[l] = distinct experts selected in layer l."""
+    v = rec["valid"]
+    names = {2: "qkv", 3: "router", 4: "attn", 5: "moe_up", 6: "out"}
+    rows = {n: {"phase": [], "per_cu": [], "span_us": [], "bytes": []} for n in names.values()}
+    for layer in range(1, geom.n_layers):
+        ob = op_bytes(geom, seq_lens, distinct[layer])
+        for op, name in names.items():
+            m = v & (rec["layer"] == layer) & (rec["op"] == op)
+            if not m.any():
+                continue
+            span = float(rec["end"][m].max() - rec["ready"][m].min())
+            work = float((rec["end"][m] - rec["ready"][m]).sum())
+            b = ob[name]
+            rows[name]["phase"].append(b / (span * 1e-6) / 1e9 if span > 0 else 0.0)
+            rows[name]["per_cu"].append(b / (work * 1e-6) / 1e9 if work > 0 else 0.0)
+            rows[name]["span_us"].append(span)
+            rows[name]["bytes"].append(b)
+    out = {}
+    for name, r in rows.items():
+        if r["phase"]:
+            out[name] = {"bytes_per_layer": int(np.median(r["bytes"])),
+                         "phase_span_us": round(float(np.median(r["span_us"])), 2),
+                         "phase_GBps": round(float(np.median(r["phase"])), 1),
+                         "per_cu_GBps": round(float(np.median(r["per_cu"])), 2)}
+    return out

@@ -244,6 +244,21 @@ int mkd_debug_read(mkd_engine* eng, int32_t what, void* dst, size_t bytes);
    not recorded.  dev_buf = NULL disables it.  The caller owns the buffer. */
 int mkd_set_trace(mkd_engine* eng, void* dev_buf, size_t bytes);
 
+/* Message-passing litmus test of the step's inter-workgroup protocol on device
+   hip_device (section "Barriers": producers publish, consumers spin until the dependency
+   is met, and the fences must leave no data race across SMs; here across XCDs).
+   n_pairs producer / consumer pairs of workgroups (2p, 2p + 1: on different XCDs) run
+   `rounds` rounds over the same buffers, with the step's own primitives: 256 tagged
+   words (agent-scope 64-bit stores and loads; the consumer checks the value of every word
+   whose tag is the round) and 512 bf16 words published by agent-scope 16-bit stores, the
+   producer's wait for them and a tagged flag, read after the flag and an agent-scope
+   acquire with the non-temporal 16-byte loads that read K/V pages.  h_result[4]: words
+   whose tag was new and value old, data words read stale after flag and acquire, waits
+   that timed out, rounds the consumers completed.  Allocates and frees its buffers (a
+   test call, not for a decode loop).  MKD_ERR_ARG unless 1 <= n_pairs <= 4096 and
+   1 <= rounds <= 100000; MKD_ERR_HIP on a runtime error. */
+int mkd_protocol_litmus(int32_t hip_device, int32_t n_pairs, int32_t rounds, uint32_t* h_result);
+
 /* ---------------------------------------------------------------- continuous decode
    The loop around the step (section "The serving engine around the kernel": each step
    updates the KV positions and page tables, clears the step state, selects the schedule
