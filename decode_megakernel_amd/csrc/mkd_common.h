@@ -46,7 +46,7 @@ enum Opcode : int32_t {
 // 32 int32 per task, 128 bytes, read with scalar loads.  The pages' descriptor also
 // carries the barrier to wait on, its target and the barrier to signal; here every data
 // edge is a tagged word that the consumer polls, so those fields do not exist and words
-// 7..31 are zero (reserved).
+// 8..31 are zero (reserved).
 enum DescField : int32_t {
   D_OPCODE = 0,
   D_LAYER = 1,

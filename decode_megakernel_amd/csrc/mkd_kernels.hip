@@ -938,7 +938,8 @@ __device__ __forceinline__ int attn_item_count(const DParams& p) {
 // and the matching up rows; epilogue silu(gate) * up for every token routed to the expert,
 // stored as tagged words that the output tasks poll.
 //
-// Static streaming (when at least kMinFreeClaimers claimers have no attention item): the
+// Static streaming (when at least kMinFreeClaimers claimers have no attention item and
+// each of them has at most kStaticItemsPerClaimer items, i.e. at small batch): the
 // free claimers take the items round robin (free claimer f: items f, f + n_free, ...) and
 // stream all of them through one ring of weight loads that runs on from one item into the
 // next, so no item waits for its first loads; after each item the workers meet the
