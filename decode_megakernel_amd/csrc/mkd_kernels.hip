@@ -1184,7 +1184,7 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
     if (!route_layer(c, l)) return false;
   }
   // (1) O-proj: NSO * R rows of length KH; token groups that fit in LDS
-  {
+  auto oproj = [&]() -> bool {
     RowSrc so;
     so.base = p.w_o + ((int64_t)l * H + r0) * QD;
     so.seg0 = 0u; so.seg1 = (uint32_t)KH; so.seg2 = 2u * KH; so.seg3 = 3u * KH;
@@ -1219,11 +1219,12 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
         }
       }
     }
-  }
+      return true;
+  };
   // (2) expert down rows: one GEMV per group of consecutive active experts whose (expert,
   // token) entries fit the LDS (one group for the whole layer up to batch 4), segment s =
   // expert a0 + s with its own token count, rows addressed through the routing table
-  {
+  auto down = [&]() -> bool {
     const LAS int32_t* rtab = c.s.route;
     const LAS float* rw = reinterpret_cast<const LAS float*>(rtab + RT_W);
     const int n_act = __builtin_amdgcn_readfirstlane(rtab[RT_NACT]);
@@ -1287,6 +1288,23 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
         }
       }
       a0 += na;
+    }
+      return true;
+  };
+  // The two GEMVs in the order their inputs usually arrive: at batch 1 the experts'
+  // activations (MoE-up streams beside attention on the CUs free of it) come before the
+  // combined attention, so the expert rows go first; above, the claimers run attention
+  // first and the O-proj goes first.
+#ifndef MKD_DOWN_FIRST
+#define MKD_DOWN_FIRST 1
+#endif
+  // (one call site each: the GEMV loops are inlined once)
+  const bool down_first = MKD_DOWN_FIRST && B == 1;
+  for (int part = 0; part < 2; ++part) {
+    if ((part == 0) == down_first) {
+      if (!down()) return false;
+    } else {
+      if (!oproj()) return false;
     }
   }
   // (3) h_{l+1}[rows] = h_l + a + m and the tile's sums of squares, as tagged words (the
