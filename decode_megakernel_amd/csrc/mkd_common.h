@@ -24,11 +24,16 @@ namespace mkd {
 //                          the chunks of the query heads (b, h) with (b*nq + h) mod
 //                          n_claimers == i, from the items' tagged partials
 //   MOE_UPGATE_ACT_DRAIN -> OP_MOE_UP
-//   O_PROJ, MOE_DOWN_DRAIN, MOE_COMBINE and the fused residual add + RMSNorm
+//   MOE_DOWN_DRAIN      -> at batch >= kDownSplitBatch, OP_MOE_DOWN: claimed (active expert,
+//                          chunk of down rows) items, each leaving the expert's output rows
+//                          for each of its tokens as tagged partials; below, a no-op (the
+//                          output task computes the down rows itself)
+//   O_PROJ, MOE_COMBINE and the fused residual add + RMSNorm
 //                       -> OP_OUT, one task per residual row tile: the tile's O-proj rows
-//                          over every KV group, its expert down rows over every active
-//                          expert weighted by the router scores, and h_{l+1} with the
-//                          tile's sum of squares (consumers apply the norm on the fly)
+//                          over every KV group, the experts' rows weighted by the router
+//                          scores (its own down GEMV over every active expert at small
+//                          batch, else the sum of the OP_MOE_DOWN partials), and h_{l+1}
+//                          with the tile's sum of squares (consumers apply the norm)
 //   LM_HEAD             -> OP_LM_HEAD; OP_EMBED seeds the residual stream.
 enum Opcode : int32_t {
   OP_NOP = 0,
@@ -39,7 +44,8 @@ enum Opcode : int32_t {
   OP_MOE_UP = 5,
   OP_OUT = 6,
   OP_LM_HEAD = 7,
-  OP_COUNT = 8,
+  OP_MOE_DOWN = 8,
+  OP_COUNT = 9,
 };
 
 // ---------------------------------------------------------------- descriptor
@@ -66,6 +72,7 @@ struct CounterLayout {
   int32_t per_layer;   // counters per layer block
   int32_t attn_claim;  // attention queue head
   int32_t up_claim;    // MoE up queue head
+  int32_t down_claim;  // MoE down queue head
   int32_t global_base; // start of the step-global block (after n_layers+1 layer blocks)
   int32_t total;       // total counters
 };
@@ -97,6 +104,8 @@ struct PlanShape {
   int32_t qkv_tph;         // QKV tiles per head
   int32_t router_rows;     // rows per router tile
   int32_t lm_rows;         // rows per LM-head tile
+  int32_t down_rows;       // expert down rows per OP_MOE_DOWN item
+  int32_t n_down_chunks;   // hidden / down_rows
 };
 
 // ---------------------------------------------------------------- kernel parameters
@@ -133,6 +142,7 @@ struct Params {
   int32_t* topk_ids;  // [L][maxB][k]
   float* topk_w;      // [L][maxB][k]
   uint64_t* moe_act;  // [L][maxB*k][I] tagged
+  uint64_t* moe_part; // [maxB*k][H] tagged: an expert's output rows per (token, choice)
   const double* inv_freq;  // [hd/2] RoPE frequencies base^(-2i/hd), fp64
   uint64_t* rope;          // [maxB][hd/2][2] tagged cos, sin of this step's positions
   const void* dummy;       // 1 KB of zeros: target of the GEMV ring's idle slots

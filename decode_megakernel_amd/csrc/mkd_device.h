@@ -251,6 +251,7 @@ struct DParams {
   GAS int32_t* topk_ids;
   GAS float* topk_w;
   GAS uint64_t* moe_act;
+  GAS uint64_t* moe_part;
   const CAS double* inv_freq;
   GAS uint64_t* rope;
   GAS uint32_t* counters;
@@ -285,7 +286,9 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.shape.up_rows = p.shape.up_rows; d.shape.n_up_tiles = p.shape.n_up_tiles;
   d.shape.pages_per_item = p.shape.pages_per_item; d.shape.qkv_rows = p.shape.qkv_rows; d.shape.qkv_tph = p.shape.qkv_tph;
   d.shape.router_rows = p.shape.router_rows; d.shape.lm_rows = p.shape.lm_rows;
+  d.shape.down_rows = p.shape.down_rows; d.shape.n_down_chunks = p.shape.n_down_chunks;
   d.ctr.per_layer = p.ctr.per_layer; d.ctr.attn_claim = p.ctr.attn_claim; d.ctr.up_claim = p.ctr.up_claim;
+  d.ctr.down_claim = p.ctr.down_claim;
   d.ctr.global_base = p.ctr.global_base;
   d.ctr.total = p.ctr.total;
   d.embed = gas(p.embed); d.norm = gas(p.norm); d.w_qkv = gas(p.w_qkv); d.w_o = gas(p.w_o);
@@ -294,7 +297,7 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.kv_pool = gas(p.kv_pool); d.logits = gas(p.logits);
   d.h = gas(p.h); d.ss = gas(p.ss); d.q = gas(p.q); d.kvflag = gas(p.kvflag); d.attn_part = gas(p.attn_part); d.attn_o = gas(p.attn_o);
   d.router = gas(p.router); d.route_tbl = gas(p.route_tbl); d.topk_ids = gas(p.topk_ids); d.topk_w = gas(p.topk_w);
-  d.moe_act = gas(p.moe_act); d.inv_freq = cas(p.inv_freq);
+  d.moe_act = gas(p.moe_act); d.moe_part = gas(p.moe_part); d.inv_freq = cas(p.inv_freq);
   d.rope = gas(p.rope);
   d.counters = gas(p.counters); d.tasks = cas(p.tasks); d.cu_offsets = cas(p.cu_offsets);
   d.max_attn_items = p.max_attn_items; d.spin_limit = p.spin_limit; d.epoch = p.epoch;

@@ -57,8 +57,8 @@ struct mkd_engine {
   bool have_weights = false;
   int32_t mode = MKD_MODE_MEGAKERNEL;
   // workspace layout (offsets) and the caller's buffer
-  Region r_h, r_ss, r_q, r_kvflag, r_part, r_attn_o, r_router, r_tbl, r_topk_ids, r_topk_w, r_act, r_inv_freq,
-      r_rope, r_dummy, r_counters, r_tasks_cu, r_tasks_global, r_offsets;
+  Region r_h, r_ss, r_q, r_kvflag, r_part, r_attn_o, r_router, r_tbl, r_topk_ids, r_topk_w, r_act, r_moe_part,
+      r_inv_freq, r_rope, r_dummy, r_counters, r_tasks_cu, r_tasks_global, r_offsets;
   size_t ws_bytes = 0;
   char* ws = nullptr;
   Params base{};
@@ -74,7 +74,7 @@ struct mkd_engine {
   std::vector<double> inv_freq;  // RoPE frequencies base^(-2i/hd), copied into every workspace
   std::vector<const Region*> regions() const {
     return {&r_h, &r_ss, &r_q, &r_kvflag, &r_part, &r_attn_o, &r_router, &r_tbl, &r_topk_ids,
-            &r_topk_w, &r_act, &r_inv_freq, &r_rope, &r_dummy, &r_counters, &r_tasks_cu,
+            &r_topk_w, &r_act, &r_moe_part, &r_inv_freq, &r_rope, &r_dummy, &r_counters, &r_tasks_cu,
             &r_tasks_global, &r_offsets};
   }
 };
@@ -138,6 +138,9 @@ void layout(mkd_engine* e) {
   put(e->r_topk_ids, sizeof(int32_t) * L * B * K, false);
   put(e->r_topk_w, sizeof(float) * L * B * K, false);
   put(e->r_act, w8 * L * B * K * c.moe_inter, true);
+  // one layer's expert output rows per (token, choice); every layer reuses it (its tags
+  // carry the layer)
+  put(e->r_moe_part, w8 * B * K * H, true);
   put(e->r_inv_freq, sizeof(double) * c.head_dim / 2, false);
   put(e->r_rope, w8 * B * c.head_dim, true);
   put(e->r_dummy, 1024, false);
@@ -161,6 +164,7 @@ void point_params(const mkd_engine* e, char* ws, Params& p) {
   p.topk_ids = (int32_t*)(ws + e->r_topk_ids.off);
   p.topk_w = (float*)(ws + e->r_topk_w.off);
   p.moe_act = (uint64_t*)(ws + e->r_act.off);
+  p.moe_part = (uint64_t*)(ws + e->r_moe_part.off);
   p.inv_freq = (const double*)(ws + e->r_inv_freq.off);
   p.rope = (uint64_t*)(ws + e->r_rope.off);
   p.dummy = ws + e->r_dummy.off;

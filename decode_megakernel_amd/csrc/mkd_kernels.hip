@@ -1145,6 +1145,72 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   return true;
 }
 
+// ------------------------------------------------------------------ OP_MOE_DOWN (claimer)
+// The page's MOE_DOWN_DRAIN, at batch >= kDownSplitBatch: items are (active expert a, chunk
+// of down_rows output rows), claimed like the attention items (claimer i takes item i
+// first, later items come from the queue).  An item waits for its expert's activation rows
+// of its tokens (tagged, left by the MoE-up items), computes W_down[e][chunk rows] . act
+// for each token and leaves the rows as tagged words y[slot][row], slot = b * k + j (the
+// token and its choice), which the output tasks weight and sum.  Each item stages only its
+// own expert's activations, where an output task that computed the down rows itself
+// would stage every active expert's.  Below the threshold the output tasks compute the
+// down rows themselves (one hop less) and this task does nothing.
+#ifndef MKD_DOWN_SPLIT_BATCH
+#define MKD_DOWN_SPLIT_BATCH 2
+#endif
+constexpr int kDownSplitBatch = MKD_DOWN_SPLIT_BATCH;
+
+template <int KI>
+__device__ __forceinline__ bool op_moe_down(Ctx& c) {
+  const DParams p = device_view(*c.kp);
+  if (p.batch < kDownSplitBatch) return true;
+  const int l = c.d[D_LAYER];
+  const int DR = p.shape.down_rows, NC = p.shape.n_down_chunks, H = p.hidden, k = p.top_k, E = p.n_experts;
+  GAS uint32_t* head = layer_ctr(p, l, p.ctr.down_claim);
+  const int ci = c.d[D_ARG0], n_cl = c.d[D_ARG1];
+  if (c.ctl) ctl_claim_put(c, 0, (uint32_t)ci);
+  bar(c);
+  if (!route_layer(c, l)) return false;
+  const LAS int32_t* rt = c.s.route;
+  const int n_items = __builtin_amdgcn_readfirstlane(rt[RT_NACT]) * NC;
+  const uint32_t ep = layer_tag(p.epoch, l);
+  const GAS uint64_t* abase = p.moe_act + (int64_t)l * p.max_batch * k * KI;
+  for (int j = 0;; ++j) {
+    const int idx = read_claim(c, j & 1);
+    if (idx >= n_items) break;
+    const int a = idx / NC, chunk = idx % NC;
+    const int e = __builtin_amdgcn_readfirstlane(rt[RT_ACT + a]);
+    const int o0 = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a]);
+    const int n_e = __builtin_amdgcn_readfirstlane(rt[RT_OFF + a + 1]) - o0;
+    const GAS uint16_t* base = p.w_down + (((int64_t)l * E + e) * H + (int64_t)chunk * DR) * KI;
+    const RowSrc src = row_src(base, base, KI, DR);
+    LAS float* xs = c.s.xs;
+    // the expert's activation rows of its tokens (entry o0 + r at xs row r)
+    auto stage = [&]() {
+      return team_poll<8>(
+          c, ep, n_e * KI, [&](int i) { return abase + (int64_t)rt[RT_FLAT + o0 + i / KI] * KI + i % KI; },
+          [&](int i) -> LAS float& { return xs[xsplit<KI>(i)]; });
+    };
+    if (!c.ctl) {
+      if (!worker_gemv<KI>(c, src, DR, c.s.xs, c.s.mi + MI_TOK, n_e, c.s.rowsum, stage)) return false;
+    } else {
+      const bool ok = stage();
+      if (ok) {
+        if (c.lane < 16) c.s.mi[MI_TOK + c.lane] = c.lane;
+        if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
+      }
+      const uint32_t nxt = ctl_claim_issue(c, head, n_cl);
+      if (!ctl_gemv_barriers(c, ok, (j + 1) & 1, nxt)) return false;
+      for (int i = c.lane; i < DR * n_e; i += 64) {
+        const int r = i / n_e, jj = i % n_e;
+        const int slot = rt[RT_FLAT + o0 + jj];  // b * k + j
+        st_tag(p.moe_part + (int64_t)slot * H + (int64_t)chunk * DR + r, c.s.rowsum[r * n_e + jj], ep);
+      }
+    }
+  }
+  return true;
+}
+
 // ------------------------------------------------------------------ OP_OUT
 // Residual row tile rt, rows [r0, r0 + R) with R = rt_rows:
 //   a = W_o[rows] . attn_o        (all KV groups; the nq*hd columns are split into blocks of
@@ -1226,6 +1292,31 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
   // expert a0 + s with its own token count, rows addressed through the routing table
   auto down = [&]() -> bool {
     const LAS int32_t* rtab = c.s.route;
+    if (B >= kDownSplitBatch) {
+      // the experts' rows of this tile per (token, choice), left by the MoE-down items:
+      // word (b * k + j) * R + r, weighted by the router and summed in selection order
+      const LAS float* rwt = reinterpret_cast<const LAS float*>(rtab + RT_W);
+      LAS float* stg = c.s.xs;
+      const bool ok = team_poll<8>(
+          c, layer_tag(p.epoch, l), B * k * R,
+          [&](int i) { return p.moe_part + (int64_t)(i / R) * H + r0 + i % R; },
+          [&](int i) -> LAS float& { return stg[i]; });
+      if (c.ctl) ctl_set_ok(c, ok);
+      bar(c);
+      if (!read_ok(c)) return false;
+      if (c.ctl) {
+        if (c.lane == 0) c.s.mi[MI_T_STAGED] = (int32_t)(uint32_t)wall_clock64();
+        for (int i = c.lane; i < R * B; i += 64) {
+          const int r = i / B, b = i % B;
+          float a = acc_m[r * kMaxBatch + b];
+          for (int j = 0; j < k; ++j) a += rwt[b * 16 + j] * stg[(b * k + j) * R + r];
+          acc_m[r * kMaxBatch + b] = a;
+        }
+        if (c.lane == 0) c.s.mi[MI_XS_LAYER] = -1;
+      }
+      bar(c);
+      return true;
+    }
     const LAS float* rw = reinterpret_cast<const LAS float*>(rtab + RT_W);
     const int n_act = __builtin_amdgcn_readfirstlane(rtab[RT_NACT]);
     // entries per group: staged rows (three spare rows for the reads of a partial group of
@@ -1794,6 +1885,7 @@ MKD_EXEC(exec_router, return op_rows_on_x<G::kHidden>(c, false);)
 MKD_EXEC(exec_lm_head, return op_rows_on_x<G::kHidden>(c, true);)
 MKD_EXEC(exec_moe_up, return op_moe_up<G::kHidden>(c);)
 MKD_EXEC(exec_out, return (op_out<G::kHidden, G::kInter>(c));)
+MKD_EXEC(exec_moe_down, return op_moe_down<G::kInter>(c);)
 MKD_EXEC(exec_attn, return op_attn<G::kHd>(c);)
 
 template <class G>
@@ -1805,6 +1897,7 @@ __device__ __forceinline__ bool run_task(KParams* kp, LAS char* lds, const CAS i
     case OP_LM_HEAD: return exec_lm_head<G>(kp, lds, d, task);
     case OP_MOE_UP: return exec_moe_up<G>(kp, lds, d, task);
     case OP_OUT: return exec_out<G>(kp, lds, d, task);
+    case OP_MOE_DOWN: return exec_moe_down<G>(kp, lds, d, task);
     case OP_ATTN: return exec_attn<G>(kp, lds, d, task);
     default: return true;
   }

@@ -23,6 +23,8 @@ PlanShape make_shape(const Geometry& g, const PlanOptions& o) {
   s.qkv_rows = 2 * o.qkv_max_pairs;
   s.router_rows = o.router_rows;
   s.lm_rows = o.lm_rows;
+  s.down_rows = o.down_rows;
+  s.n_down_chunks = g.hidden / o.down_rows;
   return s;
 }
 
@@ -31,6 +33,7 @@ CounterLayout make_counters(const Geometry& g) {
   int32_t at = 0;
   c.attn_claim = at++;
   c.up_claim = at++;
+  c.down_claim = at++;
   c.per_layer = (at + 15) / 16 * 16;
   c.global_base = c.per_layer * (g.n_layers + 1);
   c.total = c.global_base + G_COUNT;
@@ -62,10 +65,10 @@ struct Emitter {
 
 std::string set_schedule(PlanOptions* o, int32_t order, int32_t placement) {
   static const int32_t orders[ORDER_COUNT][W_KINDS] = {
-      {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT},
-      {W_QKV, W_ATTN, W_ROUTER, W_MOE_UP, W_OUT},
-      {W_ROUTER, W_QKV, W_MOE_UP, W_ATTN, W_OUT},
-      {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT},
+      {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_OUT},
+      {W_QKV, W_ATTN, W_ROUTER, W_MOE_UP, W_MOE_DOWN, W_OUT},
+      {W_ROUTER, W_QKV, W_MOE_UP, W_MOE_DOWN, W_ATTN, W_OUT},
+      {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_OUT},
   };
   if (order < 0 || order >= ORDER_COUNT) return "unknown schedule order";
   if (placement < 0 || placement >= PLACE_COUNT) return "unknown placement";
@@ -97,6 +100,14 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   // a GEMV tile holds at most 5 row steps per worker wave (7 workers, >= 1 row per step)
   if (o.rt_rows > 35 || 2 * o.up_rows > 35 || 2 * o.qkv_max_pairs > 35 || o.router_rows > 35 || o.lm_rows > 35)
     return "GEMV tiles are limited to 35 rows";
+  {
+    // a MoE-down item is one GEMV tile over rows of length inter: at most 5 row steps of
+    // 7 workers, each step covering 64 / (lanes per row) rows
+    const int ch = g.inter / 8;
+    const int lpr = (ch % 64 == 0) ? 64 : (ch % 32 == 0) ? 32 : (ch % 16 == 0) ? 16 : 8;
+    if (o.down_rows < 1 || g.hidden % o.down_rows || o.down_rows > 35 * (64 / lpr))
+      return "down_rows must divide hidden and fit one GEMV tile";
+  }
   Plan& P = *out;
   P = Plan();
   P.n_cu = n_cu;
@@ -125,6 +136,7 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   const int n_router_tiles = (g.n_experts + o.router_rows - 1) / o.router_rows;
   const int n_attn = o.n_attn_claimers > 0 ? o.n_attn_claimers : n_cu;
   const int n_up = o.n_up_claimers > 0 ? o.n_up_claimers : n_cu;
+  const int n_down = o.n_down_claimers > 0 ? o.n_down_claimers : n_cu;
 
   begin_wave(-1, 0);
   // residual rows, their sums of squares and the RoPE table leave as tagged words
@@ -167,6 +179,10 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
         case W_MOE_UP:
           for (int i = 0; i < n_up; ++i)
             em.emit(OP_MOE_UP, l, i, n_up, 0, 0);
+          break;
+        case W_MOE_DOWN:
+          for (int i = 0; i < n_down; ++i)
+            em.emit(OP_MOE_DOWN, l, i, n_down, 0, 0);
           break;
         case W_OUT:
           // waits inside the task: the combined attention of every KV group, then the up
@@ -226,6 +242,7 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
   // consumers' waves in the global order.
   for (int l = 0; l < g.n_layers; ++l) {
     int router_end = -1, up_first = -1, attn_end = -1, up_end = -1, out_first = -1, qkv_end = -1, attn_first = -1;
+    int down_first = -1, down_end = -1;
     for (const Wave& w : P.waves)
       if (w.layer == l) {
         if (w.kind == W_ROUTER) router_end = w.first + w.count;
@@ -239,6 +256,10 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
         if (w.kind == W_ATTN_MOE) {
           attn_first = up_first = w.first;
           attn_end = up_end = w.first + w.count;
+        }
+        if (w.kind == W_MOE_DOWN) {
+          down_first = w.first;
+          down_end = w.first + w.count;
         }
         if (w.kind == W_OUT) out_first = w.first;
       }
@@ -255,8 +276,11 @@ std::string validate_plan(const Geometry& g, const Plan& P) {
     }
     if (prev_end < 0 || first < prev_end)
       return "layer " + std::to_string(l) + ": its tasks must follow the previous layer's output wave";
-    if (attn_end < 0 || up_end < 0 || out_first < 0 || out_first < attn_end || out_first < up_end)
-      return "layer " + std::to_string(l) + ": the output wave must follow the attention and MoE-up waves";
+    if (down_first < 0 || down_first < up_end)
+      return "layer " + std::to_string(l) + ": the MoE-down wave must follow the MoE-up wave";
+    if (attn_end < 0 || up_end < 0 || out_first < 0 || out_first < attn_end || out_first < up_end ||
+        out_first < down_end)
+      return "layer " + std::to_string(l) + ": the output wave must follow the attention and MoE waves";
   }
   {
     int last_out_end = -1, lm_first = -1;

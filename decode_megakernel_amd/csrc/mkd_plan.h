@@ -41,17 +41,18 @@ struct Geometry {
 
 // Wave kinds of one layer, in the order they can be arranged.  W_ATTN_MOE is the merged
 // wave of the interleaved order (attention and MoE-up claimers alternating).
-enum WaveKind : int32_t { W_QKV = 0, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT, W_KINDS, W_ATTN_MOE = W_KINDS };
+enum WaveKind : int32_t { W_QKV = 0, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_OUT, W_KINDS, W_ATTN_MOE = W_KINDS };
 
 // Named wave orders ("The task scheduler: mapping tasks to SMs": the default order and
 // its two ablations, mapped onto this design's waves, in which the attention combine
 // belongs to the attention claimers and the O-proj to the output tasks):
-//   ORDER_DEFAULT      qkv -> router -> attention -> MoE-up -> output
-//   ORDER_ATTN_FIRST   qkv -> attention -> router -> MoE-up -> output (attention is dealt
-//                      before any routing or expert work)
-//   ORDER_MOE_FIRST    router -> qkv -> MoE-up -> attention -> output
-//   ORDER_INTERLEAVED  qkv -> router -> (attention, MoE-up claimers alternating) -> output:
-//                      dealt round robin, the two branches run side by side on disjoint CUs
+//   ORDER_DEFAULT      qkv -> router -> attention -> MoE-up -> MoE-down -> output
+//   ORDER_ATTN_FIRST   qkv -> attention -> router -> MoE-up -> MoE-down -> output (attention
+//                      is dealt before any routing or expert work)
+//   ORDER_MOE_FIRST    router -> qkv -> MoE-up -> MoE-down -> attention -> output
+//   ORDER_INTERLEAVED  qkv -> router -> (attention, MoE-up claimers alternating) -> MoE-down
+//                      -> output: dealt round robin, the two branches run side by side on
+//                      disjoint CUs
 enum ScheduleOrder : int32_t { ORDER_DEFAULT = 0, ORDER_ATTN_FIRST, ORDER_MOE_FIRST, ORDER_INTERLEAVED, ORDER_COUNT };
 // Placement of the global order onto workgroups (workgroup w runs on XCD w mod 8):
 //   PLACE_ROUND_ROBIN  task k -> workgroup k mod n_cu (consecutive tasks on different XCDs)
@@ -83,7 +84,9 @@ struct PlanOptions {
   // Order of the waves inside a layer: the pages' default order (qkv -> router ->
   // attention -> MoE -> output), which measured fastest of the orders tried (MoE-up
   // before attention: 25% slower; router before QKV: no change).
-  int32_t order[W_KINDS] = {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_OUT};
+  int32_t order[W_KINDS] = {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_OUT};
+  int32_t down_rows = 64;  // expert down rows per MoE-down item (a divisor of hidden)
+  int32_t n_down_claimers = 0;  // 0: one per CU
   int32_t interleave = 0;  // merge the attention and MoE-up waves (ORDER_INTERLEAVED)
   int32_t placement = PLACE_ROUND_ROBIN;
 };

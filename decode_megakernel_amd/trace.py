@@ -13,7 +13,7 @@ import json
 
 import numpy as np
 
-OPNAMES = {0: "nop", 1: "embed", 2: "qkv", 3: "router", 4: "attn", 5: "moe_up", 6: "out", 7: "lm_head"}
+OPNAMES = {0: "nop", 1: "embed", 2: "qkv", 3: "router", 4: "attn", 5: "moe_up", 6: "out", 7: "lm_head", 8: "moe_down"}
 TICK_US = 0.01  # 100 MHz
 
 

@@ -12,7 +12,7 @@ import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OP_EMBED, OP_QKV, OP_ROUTER, OP_ATTN, OP_MOE_UP, OP_OUT, OP_LM_HEAD = range(1, 8)
+OP_EMBED, OP_QKV, OP_ROUTER, OP_ATTN, OP_MOE_UP, OP_OUT, OP_LM_HEAD, OP_MOE_DOWN = range(1, 9)
 
 
 def test_exports_every_declared_symbol():
@@ -99,6 +99,12 @@ def test_plan_structure(geom, max_batch, n_cu):
         assert a[:, GI].min() > t[:, GI].max()
         for h in range(gq):
             assert sorted(t[t[:, 2] == h][:, 5].tolist()) == list(range((t[:, 2] == h).sum()))
+    # one MoE-down claimer per CU per layer (a no-op below the batch that splits the down
+    # rows out of the output tasks), after the layer's MoE-up claimers
+    assert (ops == OP_MOE_DOWN).sum() == geom.n_layers * n_cu
+    up, dn = desc[ops == OP_MOE_UP], desc[ops == OP_MOE_DOWN]
+    for layer in range(geom.n_layers):
+        assert dn[dn[:, 1] == layer][:, GI].min() > up[up[:, 1] == layer][:, GI].max()
     # one output task per residual row tile and layer; the residual rows travel as tagged
     # words and the next layer's tasks come after the output wave in the global order
     out = desc[ops == OP_OUT]
@@ -131,18 +137,20 @@ def test_schedules_same_tasks_other_order(geom, order, placement):
     glob = desc[np.argsort(desc[:, GI])]
     ops, layers = glob[:, 0], glob[:, 1]
     for layer in range(geom.n_layers):
-        pos = {op: np.nonzero((ops == op) & (layers == layer))[0] for op in (OP_QKV, OP_ROUTER, OP_ATTN, OP_MOE_UP, OP_OUT)}
+        pos = {op: np.nonzero((ops == op) & (layers == layer))[0]
+               for op in (OP_QKV, OP_ROUTER, OP_ATTN, OP_MOE_UP, OP_MOE_DOWN, OP_OUT)}
         first = {op: p.min() for op, p in pos.items()}
         last = {op: p.max() for op, p in pos.items()}
         # producers ahead of consumers in every schedule
         assert last[OP_QKV] < first[OP_ATTN] and last[OP_ROUTER] < first[OP_MOE_UP]
-        assert max(last[OP_ATTN], last[OP_MOE_UP]) < first[OP_OUT]
+        assert last[OP_MOE_UP] < first[OP_MOE_DOWN]
+        assert max(last[OP_ATTN], last[OP_MOE_DOWN]) < first[OP_OUT]
         if order == mkd.ORDER_DEFAULT:
             assert last[OP_ROUTER] < first[OP_ATTN] and last[OP_ATTN] < first[OP_MOE_UP]
         elif order == mkd.ORDER_ATTN_FIRST:
             assert last[OP_ATTN] < first[OP_ROUTER]
         elif order == mkd.ORDER_MOE_FIRST:
-            assert last[OP_ROUTER] < first[OP_QKV] and last[OP_MOE_UP] < first[OP_ATTN]
+            assert last[OP_ROUTER] < first[OP_QKV] and last[OP_MOE_DOWN] < first[OP_ATTN]
         else:
             # claimer i of the attention queue directly followed by claimer i of the MoE queue
             a, m = pos[OP_ATTN], pos[OP_MOE_UP]
