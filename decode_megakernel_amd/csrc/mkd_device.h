@@ -71,6 +71,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
+// The same for finite values, by CDNA4's packed conversion (one instruction).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
 
 // sum_k w[k] * x[k] over 8 bf16 weights and 8 fp32 activations.
 __device__ __forceinline__ float dot8(const u32x4 w, const f32x4 a, const f32x4 b) {
@@ -118,6 +124,22 @@ __device__ __forceinline__ int row16_min(int v) {
   v = min(v, dpp_i<0x122>(v));
   v = min(v, dpp_i<0x121>(v));
   return v;
+}
+// Maximum / sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48),
+// returned to every lane, by CDNA4's lane swaps between register halves and row pairs (two
+// VALU instructions each, no LDS round trip).  Every lane adds the same two partial sums,
+// so the four lanes of a column get the same value.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ __forceinline__ float lane_f(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));

@@ -795,6 +795,30 @@ __device__ __forceinline__ void route_csr(const Ctx& c, const DParams& p) {
   const int B = p.batch, E = p.n_experts, k = p.top_k, n = B * k;  // n <= 256
   LAS int32_t* rt = c.s.route;
   const int lane = c.lane;
+  if (B == 1) {
+    // One token: its k choices are normally k distinct experts, so the active experts are
+    // the choices in ascending order, each with one entry (its choice index j); the rank
+    // of choice j is the number of choices with a lower expert id.  Repeated ids (only
+    // possible with non-finite logits) take the general path below.
+    const int id = lane < k ? rt[RT_IDS + lane] : 0x7FFFFFFF;
+    int rank = 0;
+    bool dup = false;
+    for (int j = 0; j < k; ++j) {
+      const int x = __builtin_amdgcn_readlane(id, j);
+      rank += x < id ? 1 : 0;
+      dup = dup || (x == id && j != lane);
+    }
+    if (__ballot(lane < k && dup) == 0) {
+      if (lane < k) {
+        rt[RT_ACT + rank] = id;
+        rt[RT_FLAT + rank] = lane;  // entry b * k + j of token 0
+        rt[RT_EPOS + lane] = rank << 16;
+      }
+      if (lane <= k) rt[RT_OFF + lane] = lane;
+      if (lane == 0) rt[RT_NACT] = k;
+      return;
+    }
+  }
   int ev[4];  // expert of entry lane + 64 q (entry t = b * k + j)
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1703,20 +1727,18 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
           for (int r = 0; r < 4; ++r)
             if (lpg * p.page + (c.lane >> 4) * 4 + r > pos) s[r] = -INFINITY;
         }
-        float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-        pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+        // scores are <= 0 after the shift: the hardware base-2 exponential (no range
+        // reduction needed; results below 2^-126 of the maximum flush to zero)
+        const float pm = rows4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
         const float mn = fmaxf(m, pm);
-        const float alpha = exp2f(m - mn);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
         float pr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = exp2f(s[r] - mn);
-        float ps = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
+        for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r] - mn);
+        const float ps = rows4_sum((pr[0] + pr[1]) + (pr[2] + pr[3]));
         lsum = lsum * alpha + ps;
         m = mn;
-        const u32x2 pb2 = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+        const u32x2 pb2 = u32x2{cvt_bf16x2(pr[0], pr[1]), cvt_bf16x2(pr[2], pr[3])};
         const s16x4 pb = __builtin_bit_cast(s16x4, pb2);
 #pragma unroll
         for (int dt = 0; dt < NV; ++dt) {
