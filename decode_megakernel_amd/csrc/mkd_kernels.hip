@@ -798,17 +798,18 @@ __device__ __forceinline__ void route_csr(const Ctx& c, const DParams& p) {
   if (B == 1) {
     // One token: its k choices are normally k distinct experts, so the active experts are
     // the choices in ascending order, each with one entry (its choice index j); the rank
-    // of choice j is the number of choices with a lower expert id.  Repeated ids (only
-    // possible with non-finite logits) take the general path below.
+    // of choice j is the number of choices with a lower expert id.  Repeated or invalid
+    // ids (only possible with NaN logits) take the general path below, which leaves such
+    // entries out.
     const int id = lane < k ? rt[RT_IDS + lane] : 0x7FFFFFFF;
     int rank = 0;
-    bool dup = false;
+    bool odd = id < 0 || id >= E;
     for (int j = 0; j < k; ++j) {
       const int x = __builtin_amdgcn_readlane(id, j);
       rank += x < id ? 1 : 0;
-      dup = dup || (x == id && j != lane);
+      odd = odd || (x == id && j != lane);
     }
-    if (__ballot(lane < k && dup) == 0) {
+    if (__ballot(lane < k && odd) == 0) {
       if (lane < k) {
         rt[RT_ACT + rank] = id;
         rt[RT_FLAT + rank] = lane;  // entry b * k + j of token 0
