@@ -180,6 +180,18 @@ __device__ __forceinline__ bool read_ok(Ctx& c) { return read_mi(c, MI_OK) != 0 
 // until it is; the watchdog and the abort flag bound the wait.  No barrier inside: every
 // wave may call it with its share, and the caller synchronises the team.  On failure a
 // worker marks MI_WFAIL, so that the team leaves the task after its next barrier.
+// Words per thread per round of the team-wide waits that stage a whole layer input: the
+// normed input (batch x hidden plus the row-tile sums of squares) and the combined
+// attention of the O-proj.  Measured at batch 1, 4 and 16 (8K): rounds of 12 or 16 words
+// for both were 1-5% slower than these widths.
+#ifndef MKD_W_X
+#define MKD_W_X 5
+#endif
+#ifndef MKD_W_A
+#define MKD_W_A 8
+#endif
+constexpr int kStageXWords = MKD_W_X;
+constexpr int kStageAWords = MKD_W_A;
 #ifndef MKD_POLL_SLEEP
 #define MKD_POLL_SLEEP 1
 #endif
@@ -516,7 +528,7 @@ __device__ __forceinline__ bool team_stage_x(const Ctx& c, int l, bool& fresh) {
   const GAS uint64_t* sb = p.ss + (int64_t)l * p.max_batch * NRT;
   const GAS uint16_t* gamma = p.norm + (int64_t)l * H;
   LAS float* xs = c.s.xs;
-  return team_poll<5>(
+  return team_poll<kStageXWords>(
       c, layer_tag(p.epoch, l), nh + B * NRT, [&](int i) { return i < nh ? hb + i : sb + (i - nh); },
       [&](int i) -> LAS float& { return xs[i < nh ? xsplit<K>(i) : i]; },
       [&](int i) { return i < nh ? bf16_to_f32(gamma[i % H]) : 1.0f; });
@@ -1290,7 +1302,7 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
       const GAS uint64_t* asrc = p.attn_o + ((int64_t)l * p.max_batch + t0) * QD;
       LAS float* xs = c.s.xs;
       auto stage = [&]() {
-        return team_poll<8>(c, layer_tag(p.epoch, l), nb * QD, [&](int i) { return asrc + i; },
+        return team_poll<kStageAWords>(c, layer_tag(p.epoch, l), nb * QD, [&](int i) { return asrc + i; },
                             [&](int i) -> LAS float& { return xs[xsplit<KH>(i)]; });
       };
       if (!c.ctl) {
