@@ -92,6 +92,13 @@ enum GlobalCounter : int32_t {
 
 // Words of one layer's published routing table (the LDS routing area's layout).
 constexpr int32_t kRouteTableWords = 1548;
+// Batch from which the expert down rows are computed by the MoE-down items (OP_MOE_DOWN)
+// instead of inside the output tasks; a schedule built for smaller batches has no MoE-down
+// tasks.
+#ifndef MKD_DOWN_SPLIT_BATCH
+#define MKD_DOWN_SPLIT_BATCH 2
+#endif
+constexpr int32_t kDownSplitBatch = MKD_DOWN_SPLIT_BATCH;
 
 // ---------------------------------------------------------------- plan constants
 struct PlanShape {

@@ -1192,10 +1192,6 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
 // own expert's activations, where an output task that computed the down rows itself
 // would stage every active expert's.  Below the threshold the output tasks compute the
 // down rows themselves (one hop less) and this task does nothing.
-#ifndef MKD_DOWN_SPLIT_BATCH
-#define MKD_DOWN_SPLIT_BATCH 2
-#endif
-constexpr int kDownSplitBatch = MKD_DOWN_SPLIT_BATCH;
 
 template <int KI>
 __device__ __forceinline__ bool op_moe_down(Ctx& c) {

@@ -136,7 +136,9 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   const int n_router_tiles = (g.n_experts + o.router_rows - 1) / o.router_rows;
   const int n_attn = o.n_attn_claimers > 0 ? o.n_attn_claimers : n_cu;
   const int n_up = o.n_up_claimers > 0 ? o.n_up_claimers : n_cu;
-  const int n_down = o.n_down_claimers > 0 ? o.n_down_claimers : n_cu;
+  // no MoE-down claimers when no batch of this schedule reaches the split (their tasks
+  // would only cost a dispatch on every CU per layer)
+  const int n_down = max_batch < kDownSplitBatch ? 0 : o.n_down_claimers > 0 ? o.n_down_claimers : n_cu;
 
   begin_wave(-1, 0);
   // residual rows, their sums of squares and the RoPE table leave as tagged words
