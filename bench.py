@@ -46,9 +46,12 @@ def algorithmic_bytes(geom, seq_lens, n_distinct_experts):
     bf = 2
     dense = (geom.qkv_rows * H + H * nq * hd + geom.n_experts * H + H) * bf
     expert = (2 * geom.moe_inter * H + H * geom.moe_inter) * bf
-    kv_per_layer = sum((s + 1) for s in seq_lens) * nkv * hd * 2 * bf
+    window, every = getattr(geom, "attn_window", 0), getattr(geom, "full_every", 1)
     total = 0
     for layer in range(geom.n_layers):
+        # a local-attention layer reads the last `window` positions of each sequence
+        local = window > 0 and (layer + 1) % every != 0
+        kv_per_layer = sum(min(s + 1, window) if local else s + 1 for s in seq_lens) * nkv * hd * 2 * bf
         total += dense + n_distinct_experts[layer] * expert + kv_per_layer
     total += geom.vocab * H * bf + H * bf + len(seq_lens) * H * bf
     return total
@@ -126,6 +129,10 @@ def run(args):
     if args.layers:
         import dataclasses
         wl = dataclasses.replace(wl, geom=dataclasses.replace(wl.geom, n_layers=args.layers))
+    if args.window:
+        import dataclasses
+        wl = dataclasses.replace(wl, geom=dataclasses.replace(wl.geom, attn_window=args.window,
+                                                              full_every=args.full_every))
     g = wl.geom
     t_setup = time.perf_counter()
     W = sdev.device_weights(wl)
@@ -137,6 +144,8 @@ def run(args):
     eng.load_weights(W)
     eng.set_mode(mkd.MODE_OP_PER_KERNEL if args.mode == "ablation" else mkd.MODE_MEGAKERNEL)
     eng.set_schedule(ORDERS[args.order], PLACEMENTS[args.placement])
+    if args.window:
+        eng.set_attention_window(args.window, args.full_every)
     stream = torch.cuda.current_stream()
     logits = torch.empty((batch, g.vocab), dtype=torch.float32, device="cuda")
     tokens = inp["tokens"].clone()
@@ -205,6 +214,7 @@ def run(args):
             "batch": batch, "context": ctx, "layers": g.n_layers, "experts": g.n_experts, "top_k": g.top_k,
             "mode": "megakernel" if args.mode != "ablation" else "op-per-kernel",
             "order": args.order, "placement": args.placement,
+            **({"attn_window": args.window, "full_every": args.full_every} if args.window else {}),
         },
         "achieved_TBps": round(mean_bytes / (ms_per_step * 1e-3) / 1e12, 4),
         "sol_fraction": round(sol_ms / ms_per_step, 4),
@@ -226,7 +236,8 @@ def run(args):
         "kernel_source": kernel_source_hash(),
     }
     pmc = os.path.join(ROOT, "profiles", "mk_persistent_full_b1_ctx8k_traffic.json")
-    if os.path.exists(pmc) and args.mode != "ablation" and batch == 1 and ctx == 8192 and not args.layers:
+    if (os.path.exists(pmc) and args.mode != "ablation" and batch == 1 and ctx == 8192 and not args.layers
+            and not args.window):
         with open(pmc) as f:
             rec = json.load(f)
         if rec.get("kernel_source") == out["kernel_source"]:
@@ -428,6 +439,10 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--ctx", type=int, default=8192)
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (diagnostics)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="local-attention layers: attend to the last WINDOW positions (0: all layers full)")
+    ap.add_argument("--full-every", type=int, default=1,
+                    help="with --window: layer l is full attention when (l + 1) %% FULL_EVERY == 0")
     ap.add_argument("--mode", choices=["megakernel", "ablation"], default="megakernel")
     ap.add_argument("--max-positions", type=int, default=128)
     ap.add_argument("--workload", choices=["step", "continuous"], default="step",

@@ -44,7 +44,7 @@ D_GIDX = 7  # descriptor word holding the task's position in the global order
 EXPORTS = ("mkd_create", "mkd_destroy", "mkd_workspace_bytes", "mkd_set_workspace",
            "mkd_load_weights", "mkd_set_mode", "mkd_decode_step", "mkd_decode_step_static",
            "mkd_sync_status",
-           "mkd_set_watchdog", "mkd_last_error", "mkd_debug_read", "mkd_plan_inspect",
+           "mkd_set_watchdog", "mkd_set_attention_window", "mkd_last_error", "mkd_debug_read", "mkd_plan_inspect",
            "mkd_set_trace", "mkd_set_schedule",
            "mkd_server_create", "mkd_server_destroy", "mkd_server_buffer_bytes", "mkd_server_set_buffer",
            "mkd_server_join", "mkd_server_step", "mkd_server_last_step", "mkd_server_stats",
@@ -88,6 +88,7 @@ def lib():
             "mkd_workspace_bytes": ([VP], ctypes.c_size_t),
             "mkd_set_workspace": ([VP, VP, ctypes.c_size_t], I32),
             "mkd_set_watchdog": ([VP, I32], I32),
+            "mkd_set_attention_window": ([VP, I32, I32], I32),
             "mkd_load_weights": ([VP, P(Weights)], I32),
             "mkd_set_mode": ([VP, I32], I32),
             "mkd_decode_step": ([VP, VP, I32, VP, VP, VP, VP, VP, VP, I32, VP], I32),
@@ -166,6 +167,11 @@ class Engine:
 
     def set_watchdog(self, polls: int):
         self._check(lib().mkd_set_watchdog(self._h, int(polls)))
+
+    def set_attention_window(self, window: int, full_every: int = 1):
+        """Local-attention layers: layer l attends to its last `window` positions unless
+        (l + 1) % full_every == 0; window 0 makes every layer full attention."""
+        self._check(lib().mkd_set_attention_window(self._h, int(window), int(full_every)))
 
     def close(self):
         if getattr(self, "_h", None):

@@ -165,6 +165,10 @@ struct Params {
   //  (inputs staged - start) << 32 | (workers done - start) << 48, both in clock ticks)
   uint64_t* trace;
   int32_t trace_cap;         // tasks the trace buffer holds
+  // local-attention layers: layer l attends to its last attn_window positions when
+  // attn_window > 0 and (l + 1) % full_every != 0, to every position otherwise
+  int32_t attn_window;
+  int32_t full_every;
 };
 
 }  // namespace mkd

@@ -284,6 +284,7 @@ struct DParams {
   uint32_t epoch;
   GAS uint64_t* trace;
   int32_t trace_cap;
+  int32_t attn_window, full_every;
 };
 
 template <typename T>
@@ -324,6 +325,7 @@ __device__ __forceinline__ DParams device_view(KParams& p) {
   d.counters = gas(p.counters); d.tasks = cas(p.tasks); d.cu_offsets = cas(p.cu_offsets);
   d.max_attn_items = p.max_attn_items; d.spin_limit = p.spin_limit; d.epoch = p.epoch;
   d.trace = gas(p.trace); d.trace_cap = p.trace_cap;
+  d.attn_window = p.attn_window; d.full_every = p.full_every;
   return d;
 }
 

@@ -70,6 +70,7 @@ struct mkd_engine {
   uint64_t* trace = nullptr;
   int32_t trace_cap = 0;
   int32_t spin_limit = 4000000;
+  int32_t attn_window = 0, full_every = 1;  // local-attention layers (mkd_set_attention_window)
   uint32_t epoch = 0;  // number of the last step, in [1, 2^24) (0: none since the workspace was cleared)
   std::vector<double> inv_freq;  // RoPE frequencies base^(-2i/hd), copied into every workspace
   std::vector<const Region*> regions() const {
@@ -344,6 +345,14 @@ int mkd_set_mode(mkd_engine* e, int32_t mode) {
   return MKD_OK;
 }
 
+int mkd_set_attention_window(mkd_engine* e, int32_t window, int32_t full_every) {
+  if (!e) return MKD_ERR_ARG;
+  if (window < 0 || full_every < 1) return fail(e, MKD_ERR_ARG, "window must be >= 0 and full_every >= 1");
+  e->attn_window = window;
+  e->full_every = full_every;
+  return MKD_OK;
+}
+
 int mkd_set_watchdog(mkd_engine* e, int32_t polls) {
   if (!e) return MKD_ERR_ARG;
   if (polls < 1) return fail(e, MKD_ERR_ARG, "the watchdog bound must be at least one poll");
@@ -422,6 +431,8 @@ int enqueue_step(mkd_engine* e, char* ws, uint32_t* epoch, void* stream, int32_t
   p.trace = e->trace;
   p.trace_cap = e->trace_cap;
   p.spin_limit = e->spin_limit;
+  p.attn_window = e->attn_window;
+  p.full_every = e->full_every;
   // A fresh epoch per step (tagged words carry (epoch << 8) | layer).  Epoch 0 is never
   // used, so zeroed words never read as ready; when the 24-bit epoch wraps, the tagged
   // buffers are cleared first, so no word from 2^24 steps ago can pass for a new one.

@@ -963,10 +963,24 @@ __device__ __forceinline__ void ctl_route_ahead(Ctx& c, int l) {
 }
 
 // Attention items of this step: (sequence, KV group, chunk of pages_per_item pages).
-__device__ __forceinline__ int attn_item_count(const DParams& p) {
+// First position that layer l attends to for a sequence whose new token is at pos: the
+// last attn_window positions on a local-attention layer, all positions otherwise.
+__device__ __forceinline__ int attn_first_pos(const DParams& p, int l, int pos) {
+  const bool local = p.attn_window > 0 && (l + 1) % p.full_every != 0;
+  return local ? max(0, pos - p.attn_window + 1) : 0;
+}
+// Pages of sequence b that layer l reads: first .. last (the new token's page).
+__device__ __forceinline__ int attn_first_page(const DParams& p, int l, int b) {
+  return attn_first_pos(p, l, seq_len_of(p, b)) / p.page;
+}
+__device__ __forceinline__ int attn_chunks(const DParams& p, int l, int b) {
   const int ppi = p.shape.pages_per_item;
+  const int npg = seq_len_of(p, b) / p.page + 1 - attn_first_page(p, l, b);
+  return (npg + ppi - 1) / ppi;
+}
+__device__ __forceinline__ int attn_item_count(const DParams& p, int l) {
   int n = 0;
-  for (int b = 0; b < p.batch; ++b) n += ((seq_len_of(p, b) / p.page + 1 + ppi - 1) / ppi) * p.n_kv;
+  for (int b = 0; b < p.batch; ++b) n += attn_chunks(p, l, b) * p.n_kv;
   return min(n, p.max_attn_items);
 }
 
@@ -1119,7 +1133,7 @@ __device__ __forceinline__ bool op_moe_up(Ctx& c) {
   const int l = c.d[D_LAYER];
   const int UR = p.shape.up_rows, NT = p.shape.n_up_tiles, H = p.hidden, I = p.inter, k = p.top_k;
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.up_claim);
-  const int n_attn = attn_item_count(p), ci = c.d[D_ARG0], n_cl = c.d[D_ARG1];
+  const int n_attn = attn_item_count(p, l), ci = c.d[D_ARG0], n_cl = c.d[D_ARG1];
   // static streaming when enough claimers are free of attention and each of them has a
   // few items at most (bounded by the batch's k choices per token): otherwise the
   // attention claimers, idle after their item, share the items through the queue
@@ -1485,14 +1499,12 @@ __device__ __forceinline__ bool op_out(Ctx& c) {
 // tiles; only the page holding the new token is read after it.  Each item leaves its
 // partial (o, m, l per head) as tagged words; after its claim loop, every claimer merges
 // the chunks of the query heads assigned to it (log-sum-exp, below).
-__device__ __forceinline__ void attn_map(const DParams& p, int idx, int& b, int& g, int& chunk, int& nchunks,
-                                         int& base_bg) {
-  const int ppi = p.shape.pages_per_item;
+__device__ __forceinline__ void attn_map(const DParams& p, int l, int idx, int& b, int& g, int& chunk,
+                                         int& nchunks, int& base_bg) {
   b = -1;
   int acc = 0;
   for (int bb = 0; bb < p.batch; ++bb) {
-    const int npg = seq_len_of(p, bb) / p.page + 1;
-    const int nit = (npg + ppi - 1) / ppi;
+    const int nit = attn_chunks(p, l, bb);
     if (idx < acc + nit * p.n_kv) {
       const int local = idx - acc;
       b = bb;
@@ -1512,7 +1524,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
   const int l = c.d[D_LAYER];
   const int nkv = p.n_kv, ppi = p.shape.pages_per_item, hpg = p.n_q / nkv;
   constexpr int NK = HD / 32, NV = HD / 16, MAXP = kMaxPagesPerWave;
-  const int n_items = attn_item_count(p);
+  const int n_items = attn_item_count(p, l);
   GAS uint32_t* head = layer_ctr(p, l, p.ctr.attn_claim);
   const int nw = c.nw;
   // The attention buffers go after this layer's staged normed input when both fit, so
@@ -1542,10 +1554,13 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
     if (idx >= n_items) break;
     uint32_t nxt = 0;  // controller: claim reply for the next item
     int b, g = 0, chunk = 0, nchunks = 0, base_bg = 0;
-    attn_map(p, idx, b, g, chunk, nchunks, base_bg);
+    attn_map(p, l, idx, b, g, chunk, nchunks, base_bg);
     const int pos = seq_len_of(p, b);
     const int npg = pos / p.page + 1, last = npg - 1;
-    const int c0 = chunk * ppi, c1 = min(npg, c0 + ppi);
+    // a local-attention layer reads from the page of its first position on, and masks
+    // the positions before it on that page
+    const int first = attn_first_pos(p, l, pos), fpg = first / p.page;
+    const int c0 = fpg + chunk * ppi, c1 = min(npg, c0 + ppi);
     u32x4 kr[MAXP][NK];
     u32x2 vr[MAXP][NV];
     int lp[MAXP];
@@ -1736,6 +1751,11 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
           for (int r = 0; r < 4; ++r)
             if (lpg * p.page + (c.lane >> 4) * 4 + r > pos) s[r] = -INFINITY;
         }
+        if (lpg == fpg && first > 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (lpg * p.page + (c.lane >> 4) * 4 + r < first) s[r] = -INFINITY;
+        }
         // scores are <= 0 after the shift: the hardware base-2 exponential (no range
         // reduction needed; results below 2^-126 of the maximum flush to zero)
         const float pm = rows4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
@@ -1838,7 +1858,7 @@ __device__ __forceinline__ bool op_attn(Ctx& c) {
       const int b = dj / p.n_q, qh = dj % p.n_q, g = qh / hpg, h = qh % hpg;
       int base_bg = 0, nch = 0;
       for (int bb = 0; bb <= b; ++bb) {
-        const int nit = (seq_len_of(p, bb) / p.page + 1 + ppi - 1) / ppi;
+        const int nit = attn_chunks(p, l, bb);
         if (bb == b) {
           base_bg += g * nit;
           nch = nit;

@@ -193,6 +193,15 @@ int mkd_sync_status(mkd_engine* eng);
    MKD_ERR_ARG unless 1 <= polls. */
 int mkd_set_watchdog(mkd_engine* eng, int32_t polls);
 
+/* Local-attention layers, the model variant of layers that are not full attention (the
+   page's section "Tasks": the attention drain runs "only for full-attention layers").
+   With window > 0, layer l attends to the last `window` positions of each sequence
+   (positions pos - window + 1 .. pos, the new token's position pos included) unless
+   (l + 1) % full_every == 0, in which case it attends to every position; window = 0
+   (the default) makes every layer full attention.  The KV cache keeps every position.
+   Applies to the following steps.  MKD_ERR_ARG unless window >= 0 and full_every >= 1. */
+int mkd_set_attention_window(mkd_engine* eng, int32_t window, int32_t full_every);
+
 /* Text of the engine's last error ("" if none).  The pointer stays valid until the
    next call on the engine.  With eng == NULL returns the last creation error. */
 const char* mkd_last_error(const mkd_engine* eng);

@@ -24,12 +24,23 @@ class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "top_k",
         "moe_inter", "vocab", "page_size")] + [("rms_eps", ctypes.c_float),
-                                               ("rope_base", ctypes.c_float)]
+                                               ("rope_base", ctypes.c_float),
+                                               ("attn_window", ctypes.c_int32),
+                                               ("full_every", ctypes.c_int32)]
 
 
-def dims_of(g) -> Dims:
+def layer_window(g, layer):
+    """Attention window of layer `layer` in a decode step (0: every position)."""
+    w, every = getattr(g, "attn_window", 0), getattr(g, "full_every", 1)
+    return w if w > 0 and (every < 1 or (layer + 1) % every != 0) else 0
+
+
+def dims_of(g, window=None) -> Dims:
+    """Dims of geometry g; `window` overrides the attention window (per-layer calls)."""
+    w = getattr(g, "attn_window", 0) if window is None else window
     return Dims(g.n_layers, g.hidden, g.n_q_heads, g.n_kv_heads, g.head_dim, g.n_experts,
-                g.top_k, g.moe_inter, g.vocab, g.page_size, g.rms_eps, g.rope_base)
+                g.top_k, g.moe_inter, g.vocab, g.page_size, g.rms_eps, g.rope_base,
+                w, getattr(g, "full_every", 1))
 
 
 def load(path):
@@ -137,8 +148,10 @@ def qkv_rope_append(g, pos, page_row, x, w_qkv, kv_layer, n_pages):
     return q
 
 
-def attention(g, pos, page_row, kv_layer, n_pages, q):
-    d = dims_of(g)
+def attention(g, pos, page_row, kv_layer, n_pages, q, window=0):
+    """Attention of every q head over positions 0..pos (the last `window` of them when
+    window > 0)."""
+    d = dims_of(g, window)
     page_row, q, kv_layer = _i32(page_row), _f32(q), _u16(kv_layer)
     o = np.empty(g.n_q_heads * g.head_dim, dtype=np.float32)
     lib().orc_attention(ctypes.byref(d), pos, _p(page_row), _p(kv_layer), n_pages, _p(q), _p(o))
@@ -185,10 +198,11 @@ def moe(g, x, ids, w, gate_up, down):
 
 
 def layer(g, seq_lens, page_table, kv_layer, n_pages, gamma, w_qkv, w_o, w_router, w_gate_up,
-          w_down, h, debug=False):
+          w_down, h, debug=False, layer_index=0):
     """One layer for a batch.  h [B][H] float32 is updated in place; kv_layer in
-    place.  With debug=True returns a dict of intermediate values."""
-    d = dims_of(g)
+    place.  With debug=True returns a dict of intermediate values.  layer_index selects
+    the attention window of a local-attention geometry."""
+    d = dims_of(g, layer_window(g, layer_index))
     seq_lens, page_table = _i32(seq_lens), _i32(page_table)
     B = seq_lens.size
     assert h.dtype == np.float32 and h.flags.c_contiguous and h.shape == (B, g.hidden)

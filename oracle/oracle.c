@@ -98,24 +98,27 @@ void orc_qkv_rope_append(const orc_dims* d, int64_t pos, const int32_t* page_row
 /* Decode attention ("Tasks": ATTN_DECODE over KV slices + ATTN_COMBINE is, by
    definition, plain softmax attention over the whole sequence; Figure 7: q head j
    reads KV group j / (nq / nkv)).  s_t = q . k_t / sqrt(hd), P = softmax(s),
-   o = sum_t P_t v_t, positions 0..pos (the new token included). */
+   o = sum_t P_t v_t, positions 0..pos (the new token included); on a local-attention
+   layer, positions pos - W + 1 .. pos only (W = d->attn_window > 0). */
 void orc_attention(const orc_dims* d, int64_t pos, const int32_t* page_row,
                    const uint16_t* kv_layer, int32_t n_pages, const float* q, float* o) {
   const int32_t nq = d->n_q_heads, hd = d->head_dim, P = d->page_size;
   const int32_t group = nq / d->n_kv_heads;
-  const int64_t n = pos + 1;
+  const int64_t t0 = (d->attn_window > 0 && pos + 1 > d->attn_window) ? pos + 1 - d->attn_window : 0;
+  const int64_t n = pos + 1 - t0;  /* positions t0 .. pos; s[i] belongs to position t0 + i */
   const float scale = 1.0f / sqrtf((float)hd);
 #pragma omp parallel for schedule(static)
   for (int32_t j = 0; j < nq; ++j) {
     const int32_t g = j / group;
     const float* qj = q + (int64_t)j * hd;
     float* s = (float*)malloc(sizeof(float) * (size_t)n);
-    for (int64_t t = 0; t < n; ++t) {
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t t = t0 + i;
       const int32_t page = page_row[t / P], tt = (int32_t)(t % P);
       float dot = 0.0f;
       for (int32_t e = 0; e < hd; ++e)
         dot += qj[e] * orc_bf16_to_f32(kv_layer[orc_kv_index(d, n_pages, 0, page, g, tt, e)]);
-      s[t] = dot * scale;
+      s[i] = dot * scale;
     }
     float mx = s[0];
     for (int64_t t = 1; t < n; ++t) mx = s[t] > mx ? s[t] : mx;
@@ -127,10 +130,11 @@ void orc_attention(const orc_dims* d, int64_t pos, const int32_t* page_row,
     for (int64_t t = 0; t < n; ++t) s[t] /= sum;
     float* oj = o + (int64_t)j * hd;
     for (int32_t e = 0; e < hd; ++e) oj[e] = 0.0f;
-    for (int64_t t = 0; t < n; ++t) {
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t t = t0 + i;
       const int32_t page = page_row[t / P], tt = (int32_t)(t % P);
       for (int32_t e = 0; e < hd; ++e)
-        oj[e] += s[t] * orc_bf16_to_f32(kv_layer[orc_kv_index(d, n_pages, 1, page, g, tt, e)]);
+        oj[e] += s[i] * orc_bf16_to_f32(kv_layer[orc_kv_index(d, n_pages, 1, page, g, tt, e)]);
     }
     free(s);
   }
@@ -270,7 +274,10 @@ void orc_decode_step(const orc_dims* d, int32_t batch, const int32_t* tokens,
       h[b * H + i] = orc_bf16_to_f32(embed[(int64_t)tokens[b] * H + i]);
   for (int32_t l = 0; l < d->n_layers; ++l) {
     if (h_layers) memcpy(h_layers + (int64_t)l * batch * H, h, sizeof(float) * (size_t)(batch * H));
-    orc_layer(d, batch, seq_lens, page_table, max_pages, kv_pool + l * kv_layer, n_pages,
+    /* this layer's attention window: local unless every full_every-th layer */
+    orc_dims dl = *d;
+    if (!(d->attn_window > 0 && (d->full_every < 1 || (l + 1) % d->full_every != 0))) dl.attn_window = 0;
+    orc_layer(&dl, batch, seq_lens, page_table, max_pages, kv_pool + l * kv_layer, n_pages,
               norm + l * H, w_qkv + l * qkv_rows * H, w_o + l * H * nq * hd,
               w_router + l * E * H, w_gate_up + l * E * 2 * I * H, w_down + l * E * H * I, h,
               NULL, NULL, NULL, NULL, ids_layers ? ids_layers + (int64_t)l * batch * K : NULL,

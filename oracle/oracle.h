@@ -38,10 +38,16 @@
 extern "C" {
 #endif
 
+/* attn_window / full_every: local-attention layers (the page's section "Tasks": the
+   attention drain serves "only full-attention layers", so some layers are not).  In a
+   decode step, layer l attends to the last attn_window positions when attn_window > 0
+   and (full_every < 1 or (l + 1) % full_every != 0), to every position otherwise.
+   orc_attention and orc_layer apply attn_window as given (0: every position). */
 typedef struct orc_dims {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim;
   int32_t n_experts, top_k, moe_inter, vocab, page_size;
   float rms_eps, rope_base;
+  int32_t attn_window, full_every;
 } orc_dims;
 
 float orc_bf16_to_f32(uint16_t b);
@@ -67,7 +73,7 @@ void orc_qkv_rope_append(const orc_dims* d, int64_t pos, const int32_t* page_row
                          const uint16_t* w_qkv, uint16_t* kv_layer, int32_t n_pages, float* q);
 
 /* Decode attention of every q head over positions 0..pos read through the page
-   table.  o is [nq][hd]. */
+   table, or over the last d->attn_window of them when attn_window > 0.  o is [nq][hd]. */
 void orc_attention(const orc_dims* d, int64_t pos, const int32_t* page_row,
                    const uint16_t* kv_layer, int32_t n_pages, const float* q, float* o);
 

@@ -53,6 +53,10 @@ class Geometry:
     page_size: int = 16
     rms_eps: float = 1e-6
     rope_base: float = 10000.0
+    # local-attention layers: layer l attends to the last attn_window positions unless
+    # (l + 1) % full_every == 0 (attn_window 0: every layer full attention)
+    attn_window: int = 0
+    full_every: int = 1
 
     @property
     def qkv_rows(self) -> int:

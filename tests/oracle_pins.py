@@ -236,6 +236,69 @@ def check_attention_page_permutation_invariant():
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
+def check_attention_local_window_brute_force():
+    # A local-attention layer attends to positions pos - W + 1 .. pos: scipy softmax over
+    # exactly those positions of the contiguous K/V, for windows that start mid-page, on a
+    # page boundary, cover one position, and exceed the sequence (every position).
+    rng = np.random.default_rng(9)
+    g = G
+    n = 23
+    n_pages = 11
+    page_row = rng.permutation(n_pages)[:6].astype(np.int32)
+    k = _rand_bf16(rng, (g.n_kv_heads, n, g.head_dim))
+    v = _rand_bf16(rng, (g.n_kv_heads, n, g.head_dim))
+    pool = _paged_pool(g, k, v, page_row, n_pages)
+    q = rng.standard_normal(g.n_q_heads * g.head_dim).astype(np.float32)
+    grp = g.n_q_heads // g.n_kv_heads
+    kf, vf = oracle.bf16_to_f32(k).astype(np.float64), oracle.bf16_to_f32(v).astype(np.float64)
+    pos = n - 1
+    for window in (7, 8, 11, 1, 23, 40):
+        o = oracle.attention(g, pos, page_row, pool, n_pages, q, window=window)
+        t0 = max(0, pos - window + 1)
+        for j in range(g.n_q_heads):
+            qj = q[j * g.head_dim:(j + 1) * g.head_dim].astype(np.float64)
+            s = kf[j // grp, t0:pos + 1] @ qj / math.sqrt(g.head_dim)
+            ref = scipy.special.softmax(s) @ vf[j // grp, t0:pos + 1]
+            assert _rel(o[j * g.head_dim:(j + 1) * g.head_dim], ref) < 1e-5, window
+    # window 1: the new token's v exactly; window >= pos + 1: identical to full attention
+    o1 = oracle.attention(g, pos, page_row, pool, n_pages, q, window=1)
+    for j in range(g.n_q_heads):
+        assert np.array_equal(o1[j * g.head_dim:(j + 1) * g.head_dim], oracle.bf16_to_f32(v[j // grp, pos]))
+    assert np.array_equal(oracle.attention(g, pos, page_row, pool, n_pages, q, window=n),
+                          oracle.attention(g, pos, page_row, pool, n_pages, q))
+
+
+def check_local_layers_follow_full_every():
+    # In a step, layer l is local iff (l + 1) % full_every != 0: a 2-layer geometry with
+    # full_every 2 equals a step whose layer 0 runs with the window and layer 1 without
+    # (each layer replayed with the layer function), and differs from the all-full step.
+    rng = np.random.default_rng(10)
+    base = dataclasses.replace(G, n_layers=2)
+    loc = dataclasses.replace(base, attn_window=5, full_every=2)
+    assert [oracle.layer_window(loc, l) for l in range(4)] == [5, 0, 5, 0]
+    assert [oracle.layer_window(base, l) for l in range(2)] == [0, 0]
+    wl = synth.ragged_workload(loc, [13, 6], spare_pages=1)
+    W = synth.host_weights(wl)
+    pt = synth.page_tables(wl)
+    toks = synth.host_tokens(wl)
+    pool = synth.host_kv_pool(wl)
+    pool_full = pool.copy()
+    logits, hl, _, _ = oracle.decode_step(loc, toks, wl.seq_lens, pt, pool, wl.n_pages, W)
+    full, _, _, _ = oracle.decode_step(base, toks, wl.seq_lens, pt, pool_full, wl.n_pages, W)
+    assert not np.allclose(logits, full)
+    H = loc.hidden
+    nl = loc.kv_layer_numel(wl.n_pages)
+    rep = synth.host_kv_pool(wl)
+    h = hl[0].copy()
+    for layer in range(2):
+        g_l = loc if layer == 0 else base
+        oracle.layer(g_l, wl.seq_lens, pt, rep[layer * nl:(layer + 1) * nl], wl.n_pages, W["norm"][layer * H:(layer + 1) * H],
+                     W["w_qkv"].reshape(2, -1)[layer], W["w_o"].reshape(2, -1)[layer], W["w_router"].reshape(2, -1)[layer],
+                     W["w_gate_up"].reshape(2, -1)[layer], W["w_down"].reshape(2, -1)[layer], h,
+                     layer_index=0 if layer == 0 else 1)
+        assert np.array_equal(h, hl[layer + 1]), layer
+
+
 # ------------------------------------------------------------------ routing
 
 def check_topk_library_and_ties():

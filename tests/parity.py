@@ -68,6 +68,8 @@ def gpu_step(wl, mode=0, check_weights=False, schedule=None):
     eng = mkd.Engine(wl.geom, 0, max_batch=wl.batch, max_pages_per_seq=wl.max_pages)
     eng.load_weights(W)
     eng.set_mode(mode)
+    if getattr(wl.geom, "attn_window", 0) > 0:
+        eng.set_attention_window(wl.geom.attn_window, wl.geom.full_every)
     if schedule is not None:
         eng.set_schedule(*schedule)
     logits = torch.full((wl.batch, wl.geom.vocab), float("nan"), dtype=torch.float32, device="cuda")
@@ -281,7 +283,7 @@ def reference_layers(wl, r):
                          W["w_qkv"].reshape(geo.n_layers, -1)[layer], W["w_o"].reshape(geo.n_layers, -1)[layer],
                          W["w_router"].reshape(geo.n_layers, -1)[layer],
                          W["w_gate_up"].reshape(geo.n_layers, -1)[layer],
-                         W["w_down"].reshape(geo.n_layers, -1)[layer], h, debug=True)
+                         W["w_down"].reshape(geo.n_layers, -1)[layer], h, debug=True, layer_index=layer)
         for key in out:
             out[key][layer] = o[key]
     assert np.array_equal(h, r["hidden"][geo.n_layers]), "layer replay differs from the reference step"

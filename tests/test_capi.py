@@ -179,3 +179,13 @@ def test_schedule_rejects_bad_arguments():
         e.plan(7)   # XCD placement needs a multiple of 8 compute units
     e.set_schedule(mkd.ORDER_DEFAULT, mkd.PLACE_ROUND_ROBIN)
     e.plan(7)
+
+
+def test_attention_window_rejects_bad_arguments():
+    e = mkd.Engine(synth.TINY, -1, 1, 8)
+    for window, every in ((-1, 1), (4, 0), (4, -2)):
+        with pytest.raises(RuntimeError):
+            e.set_attention_window(window, every)
+    e.set_attention_window(0, 1)
+    e.set_attention_window(32, 4)
+    e.close()

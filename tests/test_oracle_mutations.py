@@ -29,9 +29,12 @@ MUTATIONS = {
                         "const double ang = (double)((float)pos * (float)theta);"),
     "rope_position_off_by_one": ("orc_rope(hd, d->rope_base, pos, k + g * hd)",
                                  "orc_rope(hd, d->rope_base, pos + 1, k + g * hd)"),
-    "attn_no_scale": ("s[t] = dot * scale;", "s[t] = dot;"),
+    "attn_no_scale": ("s[i] = dot * scale;", "s[i] = dot;"),
     "attn_gqa_modulo": ("const int32_t g = j / group;", "const int32_t g = j % d->n_kv_heads;"),
-    "attn_excludes_new_token": ("const int64_t n = pos + 1;", "const int64_t n = pos > 0 ? pos : 1;"),
+    "attn_excludes_new_token": ("const int64_t n = pos + 1 - t0;", "const int64_t n = pos - t0 > 0 ? pos - t0 : 1;"),
+    "attn_window_one_longer": ("? pos + 1 - d->attn_window : 0;", "? pos - d->attn_window : 0;"),
+    "attn_window_ignored": ("const int64_t t0 = (d->attn_window > 0", "const int64_t t0 = 0 * (d->attn_window > 0"),
+    "step_window_on_every_layer": ("(d->full_every < 1 || (l + 1) % d->full_every != 0)", "(1)"),
     "attn_no_normalise": ("for (int64_t t = 0; t < n; ++t) s[t] /= sum;", ""),
     "attn_page_index": ("const int32_t page = page_row[t / P], tt = (int32_t)(t % P);\n      for (int32_t e = 0; e < hd; ++e)\n        oj[e]",
                         "const int32_t page = page_row[(t / P) % 2], tt = (int32_t)(t % P);\n      for (int32_t e = 0; e < hd; ++e)\n        oj[e]"),
