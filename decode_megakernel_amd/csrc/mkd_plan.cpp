@@ -6,18 +6,20 @@
 
 namespace mkd {
 
-// MoE-up item rows: the largest divisor of the expert inter size not above the option.
-static int32_t up_rows_for(const Geometry& g, const PlanOptions& o) {
-  int32_t r = std::max(1, std::min(o.up_rows, g.inter));
+// MoE-up item rows: the largest divisor of the expert inter size not above the option
+// for the schedule's batch size.
+static int32_t up_rows_for(const Geometry& g, const PlanOptions& o, int32_t max_batch) {
+  const int32_t want = max_batch >= o.up_rows_large_from ? o.up_rows_large : o.up_rows;
+  int32_t r = std::max(1, std::min(want, g.inter));
   while (g.inter % r) --r;
   return r;
 }
 
-PlanShape make_shape(const Geometry& g, const PlanOptions& o) {
+PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t max_batch) {
   PlanShape s{};
   s.rt_rows = o.rt_rows;
   s.n_rt = g.hidden / o.rt_rows;
-  s.up_rows = up_rows_for(g, o);
+  s.up_rows = up_rows_for(g, o, max_batch);
   s.n_up_tiles = g.inter / s.up_rows;
   s.pages_per_item = o.pages_per_item;
   s.qkv_rows = 2 * o.qkv_max_pairs;
@@ -98,7 +100,7 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
       o.pages_per_item_max > 64)
     return "pages_per_item <= pages_per_item_long <= pages_per_item_max <= 64 is required";
   // a GEMV tile holds at most 5 row steps per worker wave (7 workers, >= 1 row per step)
-  if (o.rt_rows > 35 || 2 * o.up_rows > 35 || 2 * o.qkv_max_pairs > 35 || o.router_rows > 35 || o.lm_rows > 35)
+  if (o.rt_rows > 35 || 2 * std::max(o.up_rows, o.up_rows_large) > 35 || 2 * o.qkv_max_pairs > 35 || o.router_rows > 35 || o.lm_rows > 35)
     return "GEMV tiles are limited to 35 rows";
   {
     // a MoE-down item is one GEMV tile over rows of length inter: at most 5 row steps of
@@ -111,7 +113,7 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   Plan& P = *out;
   P = Plan();
   P.n_cu = n_cu;
-  P.shape = make_shape(g, o);
+  P.shape = make_shape(g, o, max_batch);
   P.ctr = make_counters(g);
   const PlanShape& s = P.shape;
   const CounterLayout& c = P.ctr;

@@ -17,6 +17,12 @@
 #ifndef MKD_MAXP
 #define MKD_MAXP 1  // attention pages per worker wave (kernel register budget)
 #endif
+#ifndef MKD_UP_ROWS_LARGE
+#define MKD_UP_ROWS_LARGE 16
+#endif
+#ifndef MKD_UP_ROWS_LARGE_FROM
+#define MKD_UP_ROWS_LARGE_FROM 2
+#endif
 #ifndef MKD_UP_ROWS
 #define MKD_UP_ROWS 12  // batch 1, 8K context: 4 -> 268, 8 -> 289, 12 -> 293, 16 -> 291 tok/s
 #endif
@@ -65,6 +71,12 @@ struct PlanOptions {
   int32_t rt_rows = 8;         // residual rows per output task (O-proj + expert down rows)
   int32_t up_rows = MKD_UP_ROWS;  // activation rows per MoE-up item at most (weights: 2x rows); the
                                   // largest divisor of the expert inter size not above it is used
+  // ... for schedules whose batches reach up_rows_large_from: larger items, whose fixed
+  // cost (claim, ring start, barriers) weighs less when the items are claimed from the
+  // queue (8K context: batch 2 515 -> 522-527 tok/s, 4: 667 -> 689, 8: 748 -> 775, 16:
+  // 809 -> 828-833 with 16 rows; batch 1, which streams its items, keeps 12: 430 vs 419)
+  int32_t up_rows_large = MKD_UP_ROWS_LARGE;
+  int32_t up_rows_large_from = MKD_UP_ROWS_LARGE_FROM;
   int32_t pages_per_item = MKD_PPI;  // attention pages per claimed item (7 worker waves)
   // when the step's attention items at pages_per_item outnumber the CUs (long contexts):
   // larger items, since every item pays a claim, a merge and a partial result; when they
@@ -113,7 +125,7 @@ struct Plan {
 };
 
 // Shape constants and counter layout (independent of the batch size).
-PlanShape make_shape(const Geometry& g, const PlanOptions& o);
+PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t max_batch);
 CounterLayout make_counters(const Geometry& g);
 
 // Build the schedule for batches of up to `max_batch` sequences on `n_cu` compute units.
