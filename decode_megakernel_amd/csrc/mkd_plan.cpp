@@ -15,6 +15,10 @@ static int32_t up_rows_for(const Geometry& g, const PlanOptions& o, int32_t max_
   return r;
 }
 
+static int32_t down_rows_for(const PlanOptions& o, int32_t max_batch) {
+  return max_batch >= o.down_rows_large_from ? o.down_rows_large : o.down_rows;
+}
+
 PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t max_batch) {
   PlanShape s{};
   s.rt_rows = o.rt_rows;
@@ -25,8 +29,8 @@ PlanShape make_shape(const Geometry& g, const PlanOptions& o, int32_t max_batch)
   s.qkv_rows = 2 * o.qkv_max_pairs;
   s.router_rows = o.router_rows;
   s.lm_rows = o.lm_rows;
-  s.down_rows = o.down_rows;
-  s.n_down_chunks = g.hidden / o.down_rows;
+  s.down_rows = down_rows_for(o, max_batch);
+  s.n_down_chunks = g.hidden / s.down_rows;
   return s;
 }
 
@@ -103,12 +107,11 @@ std::string build_plan(const Geometry& g, const PlanOptions& o, int32_t max_batc
   if (o.rt_rows > 35 || 2 * std::max(o.up_rows, o.up_rows_large) > 35 || 2 * o.qkv_max_pairs > 35 || o.router_rows > 35 || o.lm_rows > 35)
     return "GEMV tiles are limited to 35 rows";
   {
-    // a MoE-down item is one GEMV tile over rows of length inter: at most 5 row steps of
-    // 7 workers, each step covering 64 / (lanes per row) rows
-    const int ch = g.inter / 8;
-    const int lpr = (ch % 64 == 0) ? 64 : (ch % 32 == 0) ? 32 : (ch % 16 == 0) ? 16 : 8;
-    if (o.down_rows < 1 || g.hidden % o.down_rows || o.down_rows > 35 * (64 / lpr))
-      return "down_rows must divide hidden and fit one GEMV tile";
+    // a MoE-down item is one GEMV tile over rows of length inter whose row sums (one per
+    // row and token of its expert) fit the 2048-float row-sum area
+    const int dr = down_rows_for(o, max_batch);
+    if (dr < 1 || g.hidden % dr || dr * max_batch > 2048)
+      return "MoE-down rows must divide hidden, with rows * max_batch <= 2048";
   }
   Plan& P = *out;
   P = Plan();

@@ -98,6 +98,10 @@ struct PlanOptions {
   // before attention: 25% slower; router before QKV: no change).
   int32_t order[W_KINDS] = {W_QKV, W_ROUTER, W_ATTN, W_MOE_UP, W_MOE_DOWN, W_OUT};
   int32_t down_rows = 64;  // expert down rows per MoE-down item (a divisor of hidden)
+  // ... for schedules whose batches reach down_rows_large_from (8K context: batch 8 772 -> 780
+  // tok/s, 16: 832 -> 841 with 128 rows; batch 2 and 4 were 1% slower with them)
+  int32_t down_rows_large = 128;
+  int32_t down_rows_large_from = 8;
   int32_t n_down_claimers = 0;  // 0: one per CU
   int32_t interleave = 0;  // merge the attention and MoE-up waves (ORDER_INTERLEAVED)
   int32_t placement = PLACE_ROUND_ROBIN;

@@ -35,7 +35,8 @@ def test_tiny_step_op_per_kernel_matches_megakernel():
     assert np.array_equal(a.hidden, b.hidden)
 
 
-@pytest.mark.parametrize("seq_lens", [[0], [15], [16], [5, 64, 17, 0], [33, 1, 100]])
+@pytest.mark.parametrize("seq_lens", [[0], [15], [16], [5, 64, 17, 0], [33, 1, 100],
+                                      [5, 64, 17, 0, 33, 1, 100, 16], [3] * 16])
 def test_tiny_ragged_batches(seq_lens):
     wl = synth.ragged_workload(synth.TINY, seq_lens, spare_pages=3)
     print(f"[case] tiny ragged {seq_lens}", flush=True)
